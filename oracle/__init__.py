@@ -1,0 +1,10 @@
+"""CPU oracle (test infrastructure only; never used by the product path)."""
+from .flce_oracle import (  # noqa: F401
+    IGNORE_INDEX,
+    flce_forward,
+    flce_forward_backward,
+    flce_rows,
+    log_sum_exp,
+    reduction_scale,
+    valid_rows,
+)

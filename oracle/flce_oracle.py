@@ -1,0 +1,169 @@
+"""Oracle for fused linear cross-entropy, forward and backward (fp64, CPU).
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check in
+``__graft_entry__`` and the CPU-baseline leg of ``bench.py`` may import or
+call this module.  It shares no code with the HIP library and imports nothing
+from it.
+
+It is the plain, materialising definition of what the fused kernels compute,
+written from the pages:
+
+* logits ``Z = H . W^T`` over the whole vocabulary -- the un-fused path of the
+  blog page "Liger Kernel: Fused Triton Kernels for LLM Training", section
+  "The Problem: The Logits Memory Wall" (unembedding projection, logits
+  tensor materialised);
+* per-row log-sum-exp ``LSE(z) = m + log(sum_j exp(z_j - m))`` with
+  ``m = max_j z_j`` -- same page, section "1. Fused Linear Cross-Entropy with
+  Online LogSumExp", step 3;
+* the target logit ``z_y`` -- same section, step 4; the token NLL is
+  ``LSE - z_y``;
+* ``dL/dz_j = P(z_j) - 1[j = y]`` with ``P(z_j) = exp(z_j - LSE)``,
+  ``dL/dH = (dL/dZ) . W`` and ``dL/dW = (dL/dZ)^T . H`` -- same page, section
+  "2. In-Kernel Gradient Computation During the Backward Pass" (the softmax
+  there carries a denominator that is identically 1 and is dropped here);
+* ``reduction="mean"`` as in the loss module call on the lecture page
+  ("GPU MODE lecture 028 - Liger Kernel", the LigerCrossEntropyLoss example);
+  the mean is taken over the rows whose label is not ``ignore_index``, and a
+  mean over zero valid rows is defined as 0 (loss and gradients), a reading of
+  the pages, which are silent on it.
+
+Everything is computed in float64 from the exact float64 images of the inputs
+(bf16 and fp32 values convert exactly).  The row blocking below only bounds
+host memory; every block sees the full vocabulary, so no online merging
+happens here.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+IGNORE_INDEX = -100
+
+
+def _as_f64(x) -> np.ndarray:
+    """Exact float64 image of a float32/bf16/float64 array or CPU torch tensor."""
+    if hasattr(x, "detach"):  # torch tensor; bf16 has no numpy dtype, go through float32 (exact)
+        import torch
+        x = x.detach().to("cpu")
+        if x.dtype == torch.bfloat16:
+            x = x.to(torch.float32)
+        x = x.numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def _as_labels(y) -> np.ndarray:
+    if hasattr(y, "detach"):
+        y = y.detach().to("cpu").numpy()
+    return np.asarray(y, dtype=np.int64)
+
+
+def valid_rows(labels, v: int, ignore_index: int = IGNORE_INDEX) -> np.ndarray:
+    """Boolean mask of rows that count toward the loss.
+
+    A label must be ``ignore_index`` or lie in ``[0, v)``; anything else is a
+    caller error and raises ``ValueError``.
+    """
+    y = _as_labels(labels)
+    valid = y != ignore_index
+    bad = valid & ((y < 0) | (y >= v))
+    if bad.any():
+        i = int(np.flatnonzero(bad)[0])
+        raise ValueError(f"label {int(y[i])} at row {i} is outside [0, {v}) and is not ignore_index")
+    return valid
+
+
+def reduction_scale(n_valid: int, reduction: str) -> float:
+    """Factor applied to every valid row's NLL and gradient: 1/n_valid for mean, 1 for sum."""
+    if reduction == "mean":
+        return 1.0 / n_valid if n_valid > 0 else 0.0
+    if reduction == "sum":
+        return 1.0
+    raise ValueError(f"unknown reduction {reduction!r}")
+
+
+def log_sum_exp(z: np.ndarray) -> np.ndarray:
+    """Row-wise LSE(z) = m + log(sum_j exp(z_j - m)), m = max_j z_j."""
+    m = z.max(axis=1)
+    return m + np.log(np.exp(z - m[:, None]).sum(axis=1))
+
+
+def flce_forward(h, w, labels, ignore_index: int = IGNORE_INDEX, reduction: str = "mean",
+                 block_rows: int = 1024):
+    """Loss (float) and per-row LSE [N] (float64) of softmax(H W^T) against the labels."""
+    hd, wd, y = _as_f64(h), _as_f64(w), _as_labels(labels)
+    n, v = hd.shape[0], wd.shape[0]
+    valid = valid_rows(y, v, ignore_index)
+    scale = reduction_scale(int(valid.sum()), reduction)
+    lse = np.empty(n, dtype=np.float64)
+    nll = np.zeros(n, dtype=np.float64)
+    for r0 in range(0, n, block_rows):
+        r1 = min(n, r0 + block_rows)
+        z = hd[r0:r1] @ wd.T
+        lse[r0:r1] = log_sum_exp(z)
+        vb = valid[r0:r1]
+        rows = np.flatnonzero(vb)
+        nll[r0 + rows] = lse[r0 + rows] - z[rows, y[r0 + rows]]
+    return float(scale * nll.sum()), lse
+
+
+def flce_forward_backward(h, w, labels, ignore_index: int = IGNORE_INDEX, reduction: str = "mean",
+                          block_rows: int = 1024):
+    """Return (loss, lse[N], dH[N, D], dW[V, D]), all float64.
+
+    The gradients are those of the returned loss with an upstream gradient of 1.
+    Ignored rows contribute nothing to the loss, have a zero dH row and add
+    nothing to dW; their LSE is still reported.
+    """
+    hd, wd, y = _as_f64(h), _as_f64(w), _as_labels(labels)
+    n, d = hd.shape
+    v = wd.shape[0]
+    if wd.shape[1] != d:
+        raise ValueError("H and W disagree on the hidden size")
+    valid = valid_rows(y, v, ignore_index)
+    scale = reduction_scale(int(valid.sum()), reduction)
+    lse = np.empty(n, dtype=np.float64)
+    nll = np.zeros(n, dtype=np.float64)
+    dh = np.zeros((n, d), dtype=np.float64)
+    dw = np.zeros((v, d), dtype=np.float64)
+    for r0 in range(0, n, block_rows):
+        r1 = min(n, r0 + block_rows)
+        z = hd[r0:r1] @ wd.T                       # logits block, all V columns
+        lse_b = log_sum_exp(z)
+        lse[r0:r1] = lse_b
+        rows = np.flatnonzero(valid[r0:r1])
+        tgt = y[r0 + rows]
+        nll[r0 + rows] = lse_b[rows] - z[rows, tgt]
+        g = np.exp(z - lse_b[:, None])             # softmax P(z)
+        g[rows, tgt] -= 1.0                        # P - onehot
+        g[~valid[r0:r1]] = 0.0                     # ignored rows carry no gradient
+        g *= scale
+        dh[r0:r1] = g @ wd                         # dL/dH = (dL/dZ) W
+        dw += g.T @ hd[r0:r1]                      # dL/dW = (dL/dZ)^T H
+    return float(scale * nll.sum()), lse, dh, dw
+
+
+def flce_rows(h, w, labels, rows, ignore_index: int = IGNORE_INDEX, reduction: str = "mean"):
+    """LSE and dH for selected rows only, at any problem size.
+
+    Each row's LSE and gradient depend only on that row's logits and on the
+    global valid count (for the mean), so they can be computed one by one.
+    Returns (lse[len(rows)], dH[len(rows), D]).
+    """
+    wd, y = _as_f64(w), _as_labels(labels)
+    v = wd.shape[0]
+    valid = valid_rows(y, v, ignore_index)
+    scale = reduction_scale(int(valid.sum()), reduction)
+    rows = np.asarray(rows, dtype=np.int64)
+    if hasattr(h, "detach"):
+        import torch
+        hr = _as_f64(h[torch.as_tensor(rows)])
+    else:
+        hr = _as_f64(np.asarray(h)[rows])
+    z = hr @ wd.T
+    lse = log_sum_exp(z)
+    g = np.exp(z - lse[:, None])
+    vr = valid[rows]
+    idx = np.flatnonzero(vr)
+    g[idx, y[rows[idx]]] -= 1.0
+    g[~vr] = 0.0
+    g *= scale
+    return lse, g @ wd

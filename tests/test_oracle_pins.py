@@ -1,0 +1,340 @@
+"""Pins of the fp64 oracle against facts that do not come from the oracle itself.
+
+Each test targets a different plausible mistake (dropped term, wrong sign,
+wrong index, transposed operand, wrong normaliser, overflow) so that such a
+mistake fails at least one of them:
+
+* closed forms at W = 0 and H = 0, and for a two-word vocabulary;
+* invariants: gradient rows of softmax - onehot sum to zero; ignored rows;
+  logit shift by a constant; mean vs sum; token and vocabulary permutations;
+* central finite differences of the loss;
+* torch's own cross-entropy with autograd in float64 (a library routine);
+* brute force with scalar Python loops on tiny inputs.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import flce_forward, flce_forward_backward, flce_rows, log_sum_exp
+
+RTOL = 1e-12
+
+
+def _rand(seed, n, d, v, sigma_w=0.5, ignore=(), labels=None):
+    g = np.random.default_rng(seed)
+    h = g.standard_normal((n, d))
+    w = sigma_w * g.standard_normal((v, d))
+    y = g.integers(0, v, n) if labels is None else np.array(labels, dtype=np.int64)
+    y = y.astype(np.int64)
+    for i in ignore:
+        y[i] = -100
+    return h, w, y
+
+
+def _close(a, b, tol=RTOL):
+    a, b = np.asarray(a, dtype=np.float64), np.asarray(b, dtype=np.float64)
+    scale = max(np.max(np.abs(b)), 1e-300)
+    err = np.max(np.abs(a - b)) if a.size else 0.0
+    assert err <= tol * scale, f"max|diff| {err:.3e} > {tol:.1e} * {scale:.3e}"
+
+
+# --- closed forms -----------------------------------------------------------------
+
+@pytest.mark.parametrize("reduction", ["mean", "sum"])
+def test_w_zero_closed_form(reduction):
+    """W = 0: every logit is 0, LSE = ln V, loss = ln V (mean) or n_valid ln V (sum),
+    dH = 0 and dW_j = scale * (sum_valid H_i / V - sum_{valid, y_i = j} H_i)."""
+    n, d, v = 9, 4, 7
+    h, w, y = _rand(1, n, d, v, ignore=(2, 5))
+    w[:] = 0.0
+    loss, lse, dh, dw = flce_forward_backward(h, w, y, reduction=reduction)
+    valid = y != -100
+    nv = int(valid.sum())
+    scale = 1.0 / nv if reduction == "mean" else 1.0
+    assert np.allclose(lse, math.log(v), rtol=0, atol=1e-15)
+    assert loss == pytest.approx(math.log(v) * (1.0 if reduction == "mean" else nv), rel=1e-14)
+    assert np.all(dh == 0.0)
+    expect = np.zeros((v, d))
+    for i in range(n):
+        if valid[i]:
+            expect += h[i] / v
+            expect[y[i]] -= h[i]
+    _close(dw, scale * expect)
+
+
+def test_h_zero_closed_form():
+    """H = 0: loss = ln V, dW = 0, dH_i = scale * (mean_j W_j - W_{y_i}) for valid rows."""
+    n, d, v = 6, 5, 8
+    h, w, y = _rand(2, n, d, v, ignore=(1,))
+    h[:] = 0.0
+    loss, lse, dh, dw = flce_forward_backward(h, w, y, reduction="mean")
+    nv = int((y != -100).sum())
+    assert loss == pytest.approx(math.log(v), rel=1e-14)
+    assert np.all(dw == 0.0)
+    for i in range(n):
+        if y[i] == -100:
+            assert np.all(dh[i] == 0.0)
+        else:
+            _close(dh[i], (w.mean(axis=0) - w[y[i]]) / nv)
+
+
+@pytest.mark.parametrize("reduction", ["mean", "sum"])
+def test_two_word_vocabulary(reduction):
+    """V = 2: the NLL is softplus(z_other - z_y) and the gradient row is
+    (+sigma, -sigma) * scale, with sigma = logistic(z_other - z_y)."""
+    n, d = 7, 3
+    h, w, y = _rand(3, n, d, 2, sigma_w=1.5, ignore=(4,))
+    loss, lse, dh, dw = flce_forward_backward(h, w, y, reduction=reduction)
+    valid = y != -100
+    scale = 1.0 / valid.sum() if reduction == "mean" else 1.0
+    total = 0.0
+    dh_e = np.zeros_like(h)
+    dw_e = np.zeros_like(w)
+    for i in range(n):
+        if not valid[i]:
+            continue
+        o = 1 - y[i]
+        delta = float(h[i] @ w[o] - h[i] @ w[y[i]])
+        total += math.log1p(math.exp(delta))
+        sig = 1.0 / (1.0 + math.exp(-delta))
+        dh_e[i] = scale * sig * (w[o] - w[y[i]])
+        dw_e[o] += scale * sig * h[i]
+        dw_e[y[i]] -= scale * sig * h[i]
+    assert loss == pytest.approx(scale * total, rel=1e-13)
+    _close(dh, dh_e)
+    _close(dw, dw_e)
+
+
+def test_lse_of_constant_row_and_large_logits():
+    """LSE of a row of equal values c is c + ln V, also where exp(c) overflows."""
+    for c in (0.0, 30.0, 100.0, 1000.0, -1000.0):
+        z = np.full((3, 11), c)
+        assert np.allclose(log_sum_exp(z), c + math.log(11), rtol=1e-15, atol=1e-12)
+
+
+# --- invariants ------------------------------------------------------------------
+
+def test_gradient_rows_sum_to_zero():
+    """sum_j (softmax - onehot)_ij = 0, hence sum_j dW[j, :] = 0 and the vocabulary-mean
+    direction of W does not move dH: dH(W + 1 u^T) = dH(W)."""
+    h, w, y = _rand(4, 12, 6, 9, ignore=(0, 7))
+    _, _, dh, dw = flce_forward_backward(h, w, y)
+    assert np.max(np.abs(dw.sum(axis=0))) <= 1e-14 * np.max(np.abs(dw)) * 9
+    u = np.random.default_rng(5).standard_normal(6)
+    _, _, dh2, _ = flce_forward_backward(h, w + u[None, :], y)
+    _close(dh2, dh, 1e-11)
+
+
+def test_ignored_rows():
+    """Ignored rows: zero dH row; changing their H leaves loss, LSE of other rows and dW unchanged."""
+    ign = (1, 4, 6)
+    h, w, y = _rand(6, 8, 5, 10, ignore=ign)
+    loss, lse, dh, dw = flce_forward_backward(h, w, y)
+    for i in ign:
+        assert np.all(dh[i] == 0.0)
+    h2 = h.copy()
+    h2[list(ign)] = 37.0 * np.random.default_rng(7).standard_normal((len(ign), 5))
+    loss2, lse2, dh2, dw2 = flce_forward_backward(h2, w, y)
+    keep = [i for i in range(8) if i not in ign]
+    assert loss2 == pytest.approx(loss, rel=1e-14)
+    _close(lse2[keep], lse[keep])
+    _close(dw2, dw)
+    _close(dh2, dh)
+
+
+def test_all_rows_ignored():
+    """Mean over zero valid rows is defined as 0 with zero gradients; the LSE is still reported."""
+    h, w, y = _rand(8, 5, 4, 6, labels=[-100] * 5)
+    for red in ("mean", "sum"):
+        loss, lse, dh, dw = flce_forward_backward(h, w, y, reduction=red)
+        assert loss == 0.0
+        assert np.all(dh == 0.0) and np.all(dw == 0.0)
+        _close(lse, log_sum_exp(h @ w.T))
+
+
+@pytest.mark.parametrize("c", [0.0, 30.0, 100.0, 1000.0])
+def test_logit_shift(c):
+    """Append a ones column to H and a constant-c column to W: every logit moves by c.
+    Loss, dH[:, :D] and dW[:, :D] are unchanged, LSE moves by c, dH[:, D] = c * sum_j G_ij = 0
+    and the new dW column sums to zero over the vocabulary."""
+    n, d, v = 10, 4, 12
+    h, w, y = _rand(9, n, d, v, ignore=(3,))
+    loss, lse, dh, dw = flce_forward_backward(h, w, y)
+    h1 = np.concatenate([h, np.ones((n, 1))], axis=1)
+    w1 = np.concatenate([w, np.full((v, 1), c)], axis=1)
+    loss1, lse1, dh1, dw1 = flce_forward_backward(h1, w1, y)
+    assert loss1 == pytest.approx(loss, rel=1e-12, abs=1e-12)
+    assert np.allclose(lse1 - c, lse, rtol=0, atol=1e-12 * max(1.0, c))
+    _close(dh1[:, :d], dh, 1e-10)
+    _close(dw1[:, :d], dw, 1e-10)
+    assert np.max(np.abs(dh1[:, d])) <= 1e-12 * max(1.0, c)
+    assert abs(dw1[:, d].sum()) <= 1e-12
+
+
+def test_mean_vs_sum():
+    h, w, y = _rand(10, 11, 5, 7, ignore=(0, 9))
+    nv = int((y != -100).sum())
+    lm, lsem, dhm, dwm = flce_forward_backward(h, w, y, reduction="mean")
+    ls, lses, dhs, dws = flce_forward_backward(h, w, y, reduction="sum")
+    assert lm * nv == pytest.approx(ls, rel=1e-14)
+    _close(dhm * nv, dhs)
+    _close(dwm * nv, dws)
+    _close(lsem, lses)
+
+
+def test_permutations():
+    """Permuting tokens permutes dH rows and LSE and leaves loss and dW unchanged;
+    permuting the vocabulary with matching relabelling permutes dW rows."""
+    n, d, v = 9, 4, 11
+    h, w, y = _rand(11, n, d, v, ignore=(2,))
+    loss, lse, dh, dw = flce_forward_backward(h, w, y)
+    g = np.random.default_rng(12)
+    p = g.permutation(n)
+    loss_p, lse_p, dh_p, dw_p = flce_forward_backward(h[p], w, y[p])
+    assert loss_p == pytest.approx(loss, rel=1e-13)
+    _close(lse_p, lse[p])
+    _close(dh_p, dh[p])
+    _close(dw_p, dw)
+    q = g.permutation(v)           # new row k holds old row q[k]
+    inv = np.argsort(q)
+    y_q = np.where(y == -100, -100, inv[np.where(y == -100, 0, y)])
+    loss_q, lse_q, dh_q, dw_q = flce_forward_backward(h, w[q], y_q)
+    assert loss_q == pytest.approx(loss, rel=1e-13)
+    _close(dh_q, dh)
+    _close(dw_q, dw[q])
+
+
+def test_row_blocking_is_invisible():
+    h, w, y = _rand(13, 37, 6, 15, ignore=(0, 36))
+    a = flce_forward_backward(h, w, y, block_rows=1024)
+    b = flce_forward_backward(h, w, y, block_rows=5)
+    assert a[0] == pytest.approx(b[0], rel=1e-14)
+    for x, z in zip(a[1:], b[1:]):
+        _close(x, z)
+
+
+def test_rows_match_full():
+    h, w, y = _rand(14, 20, 6, 13, ignore=(3, 19))
+    loss, lse, dh, dw = flce_forward_backward(h, w, y)
+    rows = [0, 3, 7, 19]
+    lse_r, dh_r = flce_rows(h, w, y, rows)
+    _close(lse_r, lse[rows])
+    _close(dh_r, dh[rows])
+    assert flce_forward(h, w, y)[0] == pytest.approx(loss, rel=1e-14)
+
+
+def test_bad_label_raises():
+    h, w, y = _rand(15, 4, 3, 5, labels=[0, 1, 5, 2])
+    with pytest.raises(ValueError):
+        flce_forward_backward(h, w, y)
+    with pytest.raises(ValueError):
+        flce_forward(h, w, np.array([0, -1, 2, 3]))
+
+
+# --- finite differences ------------------------------------------------------------
+
+@pytest.mark.parametrize("reduction", ["mean", "sum"])
+def test_finite_differences(reduction):
+    """Central differences (step 1e-6) of the fp64 loss against dH and dW, every entry."""
+    n, d, v = 4, 3, 5
+    h, w, y = _rand(16, n, d, v, sigma_w=0.8, ignore=(2,))
+    _, _, dh, dw = flce_forward_backward(h, w, y, reduction=reduction)
+    eps = 1e-6
+
+    def f(hh, ww):
+        return flce_forward(hh, ww, y, reduction=reduction)[0]
+
+    num_h = np.zeros_like(h)
+    for i in range(n):
+        for k in range(d):
+            hp, hm = h.copy(), h.copy()
+            hp[i, k] += eps
+            hm[i, k] -= eps
+            num_h[i, k] = (f(hp, w) - f(hm, w)) / (2 * eps)
+    num_w = np.zeros_like(w)
+    for j in range(v):
+        for k in range(d):
+            wp, wm = w.copy(), w.copy()
+            wp[j, k] += eps
+            wm[j, k] -= eps
+            num_w[j, k] = (f(h, wp) - f(h, wm)) / (2 * eps)
+    _close(dh, num_h, 1e-7)
+    _close(dw, num_w, 1e-7)
+    assert np.all(num_h[2] == 0.0)
+
+
+# --- library routine: torch cross-entropy with autograd, float64, CPU ---------------
+
+@pytest.mark.parametrize("reduction", ["mean", "sum"])
+@pytest.mark.parametrize("shape", [(16, 8, 10), (33, 17, 64), (64, 32, 500)])
+def test_torch_cross_entropy(reduction, shape):
+    n, d, v = shape
+    h, w, y = _rand(17 + n, n, d, v, sigma_w=0.7, ignore=(0, n // 2))
+    loss, lse, dh, dw = flce_forward_backward(h, w, y, reduction=reduction, block_rows=7)
+    ht = torch.tensor(h, requires_grad=True)
+    wt = torch.tensor(w, requires_grad=True)
+    z = ht @ wt.T
+    lt = torch.nn.functional.cross_entropy(z, torch.tensor(y), ignore_index=-100, reduction=reduction)
+    lt.backward()
+    assert loss == pytest.approx(lt.item(), rel=1e-12)
+    _close(lse, torch.logsumexp(z.detach(), dim=1).numpy())
+    _close(dh, ht.grad.numpy())
+    _close(dw, wt.grad.numpy())
+
+
+# --- brute force: scalar loops ----------------------------------------------------
+
+def _brute(h, w, y, reduction):
+    n, d, v = len(h), len(h[0]), len(w)
+    z = [[sum(h[i][k] * w[j][k] for k in range(d)) for j in range(v)] for i in range(n)]
+    lse = []
+    for i in range(n):
+        m = max(z[i])
+        lse.append(m + math.log(sum(math.exp(z[i][j] - m) for j in range(v))))
+    valid = [y[i] != -100 for i in range(n)]
+    nv = sum(valid)
+    scale = (1.0 / nv if nv else 0.0) if reduction == "mean" else 1.0
+    loss = scale * sum(lse[i] - z[i][y[i]] for i in range(n) if valid[i])
+    g = [[0.0] * v for _ in range(n)]
+    for i in range(n):
+        if not valid[i]:
+            continue
+        for j in range(v):
+            g[i][j] = scale * (math.exp(z[i][j] - lse[i]) - (1.0 if j == y[i] else 0.0))
+    dh = [[sum(g[i][j] * w[j][k] for j in range(v)) for k in range(d)] for i in range(n)]
+    dw = [[sum(g[i][j] * h[i][k] for i in range(n)) for k in range(d)] for j in range(v)]
+    return loss, lse, dh, dw
+
+
+@pytest.mark.parametrize("seed", range(4))
+@pytest.mark.parametrize("reduction", ["mean", "sum"])
+def test_brute_force(seed, reduction):
+    g = np.random.default_rng(100 + seed)
+    n, d, v = int(g.integers(1, 5)), int(g.integers(1, 4)), int(g.integers(2, 7))
+    h = g.standard_normal((n, d)) * 2
+    w = g.standard_normal((v, d))
+    y = g.integers(0, v, n).astype(np.int64)
+    if n > 1:
+        y[int(g.integers(0, n))] = -100
+    loss, lse, dh, dw = flce_forward_backward(h, w, y, reduction=reduction)
+    bl, blse, bdh, bdw = _brute(h.tolist(), w.tolist(), y.tolist(), reduction)
+    assert loss == pytest.approx(bl, rel=1e-12, abs=1e-15)
+    _close(lse, blse)
+    _close(dh, bdh)
+    _close(dw, bdw)
+
+
+# --- statistical sanity (not a pin): Gaussian logits -------------------------------
+
+def test_gaussian_logit_loss_level():
+    """With z ~ N(0, s^2) small, E[NLL] ~ ln V + s^2 / 2 (second-order expansion)."""
+    n, d, v = 512, 512, 4096
+    g = np.random.default_rng(18)
+    h = g.standard_normal((n, d))
+    w = 0.02 * g.standard_normal((v, d))
+    y = g.integers(0, v, n)
+    loss, _ = flce_forward(h, w, y)
+    s2 = 0.02 ** 2 * d
+    assert abs(loss - (math.log(v) + s2 / 2)) < 0.05
