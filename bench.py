@@ -1,0 +1,154 @@
+"""Benchmark: fused linear cross-entropy forward + backward on one MI355X.
+
+One step = one flce_fwd_bwd call (label scan, logits GEMM with the online
+LSE / target epilogue, merge, in-place gradient, dH and dW GEMMs, loss
+reduction) over the Llama-3-8B LM-head workload: N=8192 tokens, D=4096,
+V=128256, bf16, 5% ignored labels, mean reduction.  Inputs are synthetic,
+seeded and resident in HBM before timing starts.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused linear-CE fwd+bwd tokens/s (N=8192,D=4096,V=128256 bf16); MFMA %"
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}      # MI355X dense matrix peaks
+GEMM_KINDS = ("logits_lse", "dh_gemm", "dw_gemm")
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(wl, h, w, y, rows: int):
+    """The fp64 oracle, as it stands, on the first `rows` tokens of the same workload."""
+    import numpy as np
+
+    from oracle import flce_forward_backward
+    cores = len(os.sched_getaffinity(0))
+    hs, ys = h[:rows], y[:rows]
+    t0 = time.perf_counter()
+    flce_forward_backward(hs, w, ys, reduction=wl.reduction)
+    dt = time.perf_counter() - t0
+    del np
+    return {"value": rows / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {rows} of {wl.n} tokens of {wl.name} (full D={wl.d}, V={wl.v}), fp64 numpy, "
+                      f"{dt:.1f} s incl. fp64 conversion"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="llama3_8b_head")
+    ap.add_argument("--cpu-rows", type=int, default=768, help="tokens in the oracle's CPU-baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the fused linear cross-entropy path here has no multi-GPU "
+              "mode (see DESIGN.md for how it would shard); run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import linear_cross_entropy_bwd_amd as flce
+    from workloads import CONFIGS, logits_bytes_avoided, make_inputs
+
+    wl = CONFIGS[args.config]
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    log(f"[bench] generating {wl.name}: n={wl.n} d={wl.d} v={wl.v} {wl.dtype}")
+    h, w, y = make_inputs(wl)
+    hd, wd, yd = h.to(dev), w.to(dev), y.to(dev)
+    out = (torch.empty(1, dtype=torch.float32, device=dev), torch.empty(wl.n, dtype=torch.float32, device=dev),
+           torch.empty_like(hd), torch.empty_like(wd))
+    plan = flce.flce_plan_info(wl.n, wl.d, wl.v, flce.FLCE_BF16 if wl.dtype == "bf16" else flce.FLCE_F32, 1)
+    log(f"[bench] plan {plan}")
+
+    for i in range(args.warmup):
+        flce.linear_cross_entropy(hd, wd, yd, reduction=wl.reduction, out=out)
+    torch.cuda.synchronize()
+    log(f"[bench] {args.warmup} warm-up steps done")
+
+    # peak extra device memory of one call
+    flce.flce_memory_high_water(reset=True)
+    flce.linear_cross_entropy(hd, wd, yd, reduction=wl.reduction, out=out)
+    torch.cuda.synchronize()
+    extra = flce.flce_memory_high_water()
+
+    stream = torch.cuda.current_stream(dev)
+    flce.flce_profile_read()                 # clear
+    flce.flce_profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for _ in range(args.steps):
+        flce.linear_cross_entropy(hd, wd, yd, reduction=wl.reduction, out=out)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    flce.flce_profile_enable(False)
+    kern = flce.flce_profile_read()
+    ms_total = t0.elapsed_time(t1)
+    ms_step = ms_total / args.steps
+    log(f"[bench] {args.steps} steps: {ms_step:.3f} ms/step (wall {wall:.2f} s); kernels {kern}")
+
+    flops_step = 6.0 * wl.n * wl.d * wl.v
+    peak = PEAK_TFLOPS[wl.dtype]
+    # dominant kernel: the contraction kind with the largest total time
+    dom = max(GEMM_KINDS, key=lambda k: kern.get(k, (0, 0.0))[1])
+    launches, dom_ms = kern[dom]
+    flops_launch = 2.0 * wl.n * wl.d * wl.v / plan["num_chunks"]      # 2*C*D*V per chunk launch (avg)
+    dom_avg_ms = dom_ms / max(launches, 1)
+    achieved = flops_launch / (dom_avg_ms * 1e-3) / 1e12
+
+    result = {
+        "metric": METRIC,
+        "value": wl.n * args.steps / (ms_total * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded: H~N(0,1), W~N(0,0.02^2), uniform labels, 5% ignore_index)",
+        "config": {"workload": wl.name, "n": wl.n, "d": wl.d, "v": wl.v, "reduction": wl.reduction,
+                   "ignored_frac": wl.ignore_frac, "parallelism": "none (1 GPU)"},
+        "mfma_pct": 100.0 * flops_step / (ms_step * 1e-3) / (peak * 1e12),
+        "tflops": flops_step / (ms_step * 1e-3) / 1e12,
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                     "frac": achieved / peak, "traffic": None,
+                     "avg_launch_ms": dom_avg_ms, "flop_per_launch": flops_launch},
+        "kernels_ms_per_step": {k: v[1] / args.steps for k, v in kern.items() if v[0]},
+        "memory": {"extra_device_bytes": extra, "logits_bytes_avoided": logits_bytes_avoided(wl.n, wl.v),
+                   "ratio": extra / logits_bytes_avoided(wl.n, wl.v)},
+        "plan": plan,
+    }
+    if not args.no_cpu_baseline:
+        log(f"[bench] CPU baseline: oracle on {args.cpu_rows} rows")
+        result["cpu_baseline"] = cpu_baseline(wl, h, w, y, args.cpu_rows)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

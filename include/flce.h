@@ -1,0 +1,169 @@
+/*
+ * flce.h -- fused linear cross-entropy (forward + backward) for AMD Instinct
+ * MI355X (gfx950), C ABI.
+ *
+ * The operation (blog page "Liger Kernel: Fused Triton Kernels for LLM
+ * Training"; section "1. Fused Linear Cross-Entropy with Online LogSumExp",
+ * steps 1-5, and section "2. In-Kernel Gradient Computation During the
+ * Backward Pass"; the call shape is the LigerFusedLinearCrossEntropyLoss
+ * example of the lecture page "GPU MODE lecture 028 - Liger Kernel"):
+ *
+ *   z_i   = W . h_i                      logits of token i, never stored whole
+ *   lse_i = m_i + log sum_j exp(z_ij - m_i),   m_i = max_j z_ij
+ *   loss  = scale * sum_{i valid} (lse_i - z_{i,y_i})
+ *   G_ij  = scale_i * (exp(z_ij - lse_i) - [j == y_i])
+ *   dH    = G . W                        [n, d]
+ *   dW    = G^T . H                      [v, d]
+ *
+ * A row is valid when its label differs from ignore_index.  scale = 1/n_valid
+ * for FLCE_MEAN (0 when n_valid == 0: loss and gradients are then 0) and 1
+ * for FLCE_SUM; scale_i = scale for valid rows and 0 for ignored rows.
+ * The gradients are those of the returned loss for an upstream gradient of 1.
+ *
+ * Layout: every tensor pointer is a DEVICE pointer to a dense row-major array:
+ *   h [n, d], w [v, d], dh_out [n, d], dw_out [v, d] in `dtype`;
+ *   labels int64 [n]; lse_out fp32 [n]; loss_out fp32 [1].
+ * h, w, dh_out and dw_out must be 16-byte aligned and d * sizeof(dtype) must
+ * be a multiple of 16 (every row starts on a 16-byte boundary); otherwise
+ * FLCE_ERR_ALIGNMENT.  labels must be 8-byte aligned, lse_out and loss_out
+ * 4-byte aligned.
+ *
+ * Arithmetic: products accumulate in fp32 (bf16 inputs feed bf16 matrix
+ * instructions with fp32 accumulation); loss and lse are fp32; dh_out and
+ * dw_out are rounded to `dtype` with round-to-nearest-even.  The full [n, v]
+ * logits tensor is never allocated: token rows are processed in chunks of
+ * fewer than n rows (for n >= 32), see flce_plan_info().
+ *
+ * Ownership: the caller owns every argument buffer; inputs are only read,
+ * outputs are overwritten (never accumulated into) and must not alias the
+ * inputs or each other.  The library allocates its transient workspace
+ * stream-ordered on `stream` from a library-owned memory pool and releases it
+ * stream-ordered before returning; its size is flce_workspace_bytes().  The
+ * pool keeps released memory cached for reuse by later calls.
+ *
+ * Synchronisation: calls enqueue kernels on `stream` (0 = the null stream) and
+ * return without waiting; results are ready when the stream reaches that
+ * point.  Calls on different streams may run concurrently.
+ *
+ * Errors: 0 on success or a negative FLCE_ERR_* code.  Arguments are checked
+ * before anything is enqueued, so a failed call writes nothing.  No exception
+ * crosses this interface and nothing aborts.
+ *
+ * Labels: each label must be ignore_index or lie in [0, v).  Any other value
+ * is a caller error that is not diagnosed on the device: the kernels never
+ * index memory with a label, such a row counts as valid with a target logit
+ * of 0 and no one-hot term.
+ */
+#ifndef FLCE_H_
+#define FLCE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of h, w, dh_out and dw_out. */
+typedef enum { FLCE_BF16 = 0, FLCE_F32 = 1 } flce_dtype;
+
+/* Loss reduction over the valid rows. */
+typedef enum { FLCE_MEAN = 0, FLCE_SUM = 1 } flce_reduction;
+
+enum {
+  FLCE_OK = 0,
+  FLCE_ERR_INVALID_ARG = -1, /* null required pointer, n/d/v <= 0, unknown enum, size overflow */
+  FLCE_ERR_ALIGNMENT = -2,   /* pointer or row pitch not aligned as documented above */
+  FLCE_ERR_OOM = -3,         /* workspace allocation failed */
+  FLCE_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed */
+};
+
+/*
+ * Loss, per-row log-sum-exp and both gradients in one call.
+ * Forward: section "1. Fused Linear Cross-Entropy with Online LogSumExp"
+ * (chunked streaming, online LSE, target extraction); backward: section
+ * "2. In-Kernel Gradient Computation During the Backward Pass" (softmax minus
+ * one-hot, dH = G.W, dW = G^T.H), computed in the same pass from the chunk's
+ * logits rather than by recomputing them.
+ *
+ *   h, w           inputs, see Layout above.
+ *   labels         int64 [n]; ignore_index marks rows that do not count.
+ *   n, d, v        tokens, hidden size, vocabulary size (all > 0).
+ *   dtype          element type of h, w, dh_out, dw_out.
+ *   reduction      FLCE_MEAN or FLCE_SUM.
+ *   loss_out       fp32 [1], required.
+ *   lse_out        fp32 [n] or NULL; the LSE of every row, ignored rows included.
+ *   dh_out, dw_out required; overwritten.
+ *   stream         HIP stream the work is enqueued on.
+ */
+int flce_fwd_bwd(const void* h, const void* w, const int64_t* labels,
+                 int64_t n, int64_t d, int64_t v, flce_dtype dtype,
+                 int64_t ignore_index, flce_reduction reduction,
+                 float* loss_out, float* lse_out, void* dh_out, void* dw_out,
+                 hipStream_t stream);
+
+/*
+ * Forward only: loss and (optionally) the per-row LSE, the two quantities the
+ * forward keeps ("only the final scalar loss and running normalizers are
+ * stored", section "1. Fused Linear Cross-Entropy with Online LogSumExp",
+ * step 5).  Arguments as for flce_fwd_bwd.
+ */
+int flce_fwd(const void* h, const void* w, const int64_t* labels,
+             int64_t n, int64_t d, int64_t v, flce_dtype dtype,
+             int64_t ignore_index, flce_reduction reduction,
+             float* loss_out, float* lse_out, hipStream_t stream);
+
+/*
+ * Bytes of device workspace one call allocates (with_bwd = 1 for
+ * flce_fwd_bwd, 0 for flce_fwd); 0 for invalid sizes.  Honours the
+ * FLCE_CHUNK_ROWS and FLCE_WORKSPACE_CAP_BYTES environment overrides exactly
+ * as the calls do.
+ */
+size_t flce_workspace_bytes(int64_t n, int64_t d, int64_t v, flce_dtype dtype, int with_bwd);
+
+/* Execution plan a call with these sizes uses (host-only; no device access). */
+typedef struct {
+  int64_t chunk_rows;      /* token rows per chunk */
+  int64_t num_chunks;
+  int64_t vocab_pitch;     /* padded row length of the chunk's probability buffer */
+  int64_t group_cols;      /* vocabulary columns per partial (max, sum-exp) pair */
+  int64_t dh_splits;       /* split of the vocabulary reduction in dH = G.W */
+  int32_t engine;          /* 0: bf16 matrix-core engine, 1: fp32 FMA engine */
+  int32_t dw_accumulator;  /* 1 if dW accumulates across chunks in an fp32 workspace */
+  size_t workspace_bytes;
+  size_t prob_buffer_bytes;   /* the chunk's [chunk_rows, vocab_pitch] buffer */
+} flce_plan_t;
+
+/* Fill *out with the plan for these sizes; returns 0 or FLCE_ERR_INVALID_ARG. */
+int flce_plan_info(int64_t n, int64_t d, int64_t v, flce_dtype dtype, int with_bwd, flce_plan_t* out);
+
+/* Static text for a status code. */
+const char* flce_strerror(int status);
+
+/*
+ * Kernel timing instrumentation.  While enabled, every kernel launch of later
+ * calls is bracketed by HIP events on the call's stream.  flce_profile_read()
+ * waits for those events and reports, per kernel kind, the number of launches
+ * and their total duration in milliseconds since the last read, then resets
+ * the counters.  Kinds: see flce_profile_kind_name().  Not thread-safe; meant
+ * for benchmarks.
+ */
+int flce_profile_enable(int on);
+int flce_profile_read(int max_kinds, int64_t* launches, double* total_ms);
+const char* flce_profile_kind_name(int kind);
+
+/*
+ * High-water mark, in bytes, of the workspace the library's memory pool on
+ * the current device has handed out since the last reset (reset != 0 resets
+ * it after reading).  Lets a caller compare the extra device memory of a call
+ * with the [n, v] logits it does not allocate.
+ */
+int flce_memory_high_water(int reset, uint64_t* used_high_bytes);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLCE_H_ */

@@ -1,0 +1,248 @@
+"""Fused linear cross-entropy (forward + backward) on MI355X: Python binding.
+
+Thin ctypes layer over ``libflce.so`` (built from ``csrc/`` by
+``linear_cross_entropy_bwd_amd.build``).  The functions named like the C
+entry points take the same arguments as the C ABI; tensor arguments may be
+passed as torch tensors (their ``data_ptr()`` is used) or raw device
+addresses.  Every step of the computation runs in the library's HIP kernels;
+torch only provides device memory and the stream.  There is no fallback: if
+the library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libflce.so")
+
+FLCE_BF16, FLCE_F32 = 0, 1
+FLCE_MEAN, FLCE_SUM = 0, 1
+FLCE_OK, FLCE_ERR_INVALID_ARG, FLCE_ERR_ALIGNMENT, FLCE_ERR_OOM, FLCE_ERR_HIP = 0, -1, -2, -3, -4
+ENGINE_MFMA, ENGINE_FMA = 0, 1
+
+EXPORTED = (
+    "flce_fwd_bwd",
+    "flce_fwd",
+    "flce_workspace_bytes",
+    "flce_plan_info",
+    "flce_strerror",
+    "flce_profile_enable",
+    "flce_profile_read",
+    "flce_profile_kind_name",
+    "flce_memory_high_water",
+)
+
+
+class FlceError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: status {status}: {strerror(status)}")
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [
+        ("chunk_rows", ctypes.c_int64),
+        ("num_chunks", ctypes.c_int64),
+        ("vocab_pitch", ctypes.c_int64),
+        ("group_cols", ctypes.c_int64),
+        ("dh_splits", ctypes.c_int64),
+        ("engine", ctypes.c_int32),
+        ("dw_accumulator", ctypes.c_int32),
+        ("workspace_bytes", ctypes.c_size_t),
+        ("prob_buffer_bytes", ctypes.c_size_t),
+    ]
+
+    def as_dict(self):
+        return {k: getattr(self, k) for k, _ in self._fields_}
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libflce.so once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run `python -m linear_cross_entropy_bwd_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    p, i64, i32, f = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
+    L.flce_fwd_bwd.argtypes = [p, p, p, i64, i64, i64, i32, i64, i32, p, p, p, p, p]
+    L.flce_fwd_bwd.restype = i32
+    L.flce_fwd.argtypes = [p, p, p, i64, i64, i64, i32, i64, i32, p, p, p]
+    L.flce_fwd.restype = i32
+    L.flce_workspace_bytes.argtypes = [i64, i64, i64, i32, i32]
+    L.flce_workspace_bytes.restype = ctypes.c_size_t
+    L.flce_plan_info.argtypes = [i64, i64, i64, i32, i32, ctypes.POINTER(PlanInfo)]
+    L.flce_plan_info.restype = i32
+    L.flce_strerror.argtypes = [i32]
+    L.flce_strerror.restype = ctypes.c_char_p
+    L.flce_profile_enable.argtypes = [i32]
+    L.flce_profile_enable.restype = i32
+    L.flce_profile_read.argtypes = [i32, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double)]
+    L.flce_profile_read.restype = i32
+    L.flce_profile_kind_name.argtypes = [i32]
+    L.flce_profile_kind_name.restype = ctypes.c_char_p
+    L.flce_memory_high_water.argtypes = [i32, ctypes.POINTER(ctypes.c_uint64)]
+    L.flce_memory_high_water.restype = i32
+    del f
+    _lib = L
+    return L
+
+
+def _ptr(x) -> Optional[int]:
+    if x is None:
+        return None
+    if hasattr(x, "data_ptr"):
+        return x.data_ptr()
+    return int(x)
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return None
+    if hasattr(stream, "cuda_stream"):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def strerror(status: int) -> str:
+    try:
+        return lib().flce_strerror(int(status)).decode()
+    except RuntimeError:
+        return "library not loaded"
+
+
+# --- the C entry points ------------------------------------------------------------
+
+def flce_fwd_bwd(h, w, labels, n, d, v, dtype, ignore_index, reduction, loss_out, lse_out, dh_out, dw_out,
+                 stream) -> int:
+    return lib().flce_fwd_bwd(_ptr(h), _ptr(w), _ptr(labels), n, d, v, dtype, ignore_index, reduction,
+                              _ptr(loss_out), _ptr(lse_out), _ptr(dh_out), _ptr(dw_out), _stream(stream))
+
+
+def flce_fwd(h, w, labels, n, d, v, dtype, ignore_index, reduction, loss_out, lse_out, stream) -> int:
+    return lib().flce_fwd(_ptr(h), _ptr(w), _ptr(labels), n, d, v, dtype, ignore_index, reduction,
+                          _ptr(loss_out), _ptr(lse_out), _stream(stream))
+
+
+def flce_workspace_bytes(n, d, v, dtype, with_bwd) -> int:
+    return int(lib().flce_workspace_bytes(n, d, v, dtype, int(with_bwd)))
+
+
+def flce_plan_info(n, d, v, dtype, with_bwd) -> dict:
+    info = PlanInfo()
+    st = lib().flce_plan_info(n, d, v, dtype, int(with_bwd), ctypes.byref(info))
+    if st != FLCE_OK:
+        raise FlceError(st, "flce_plan_info")
+    return info.as_dict()
+
+
+def flce_strerror(status: int) -> str:
+    return strerror(status)
+
+
+def flce_profile_enable(on: bool) -> int:
+    return lib().flce_profile_enable(1 if on else 0)
+
+
+def flce_profile_read() -> dict:
+    """{kind name: (launches, total ms)} since the previous read."""
+    n = 8
+    launches = (ctypes.c_int64 * n)()
+    ms = (ctypes.c_double * n)()
+    st = lib().flce_profile_read(n, launches, ms)
+    if st != FLCE_OK:
+        raise FlceError(st, "flce_profile_read")
+    out = {}
+    for k in range(n):
+        name = lib().flce_profile_kind_name(k)
+        if name is not None:
+            out[name.decode()] = (int(launches[k]), float(ms[k]))
+    return out
+
+
+def flce_memory_high_water(reset: bool = False) -> int:
+    v = ctypes.c_uint64(0)
+    st = lib().flce_memory_high_water(1 if reset else 0, ctypes.byref(v))
+    if st != FLCE_OK:
+        raise FlceError(st, "flce_memory_high_water")
+    return int(v.value)
+
+
+# --- tensor-level convenience ---------------------------------------------------------
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return FLCE_BF16
+    if t.dtype == torch.float32:
+        return FLCE_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; expected bfloat16 or float32")
+
+
+def _red_code(reduction: str) -> int:
+    if reduction == "mean":
+        return FLCE_MEAN
+    if reduction == "sum":
+        return FLCE_SUM
+    raise ValueError(f"unknown reduction {reduction!r}")
+
+
+def _check_inputs(h, w, labels):
+    import torch
+    if not (h.is_cuda and w.is_cuda and labels.is_cuda):
+        raise ValueError("h, w and labels must be device tensors")
+    if h.dim() != 2 or w.dim() != 2 or labels.dim() != 1:
+        raise ValueError("expected h [n, d], w [v, d], labels [n]")
+    if h.shape[1] != w.shape[1] or labels.shape[0] != h.shape[0]:
+        raise ValueError("shape mismatch between h, w and labels")
+    if h.dtype != w.dtype:
+        raise TypeError("h and w must share a dtype")
+    if labels.dtype != torch.int64:
+        raise TypeError("labels must be int64")
+    if not (h.is_contiguous() and w.is_contiguous() and labels.is_contiguous()):
+        raise ValueError("h, w and labels must be contiguous")
+
+
+def linear_cross_entropy(h, w, labels, ignore_index: int = -100, reduction: str = "mean", out=None):
+    """Loss, per-row LSE, dH and dW of softmax(h w^T) against labels (one library call).
+
+    Returns (loss fp32 [1], lse fp32 [n], dh [n, d], dw [v, d]) on h's device,
+    computed on the current torch stream.  ``out`` may supply preallocated
+    (loss, lse, dh, dw) tensors.
+    """
+    import torch
+    _check_inputs(h, w, labels)
+    n, d = h.shape
+    v = w.shape[0]
+    if out is None:
+        loss = torch.empty(1, dtype=torch.float32, device=h.device)
+        lse = torch.empty(n, dtype=torch.float32, device=h.device)
+        dh = torch.empty_like(h)
+        dw = torch.empty_like(w)
+    else:
+        loss, lse, dh, dw = out
+    st = flce_fwd_bwd(h, w, labels, n, d, v, _dtype_code(h), ignore_index, _red_code(reduction), loss, lse, dh, dw,
+                      torch.cuda.current_stream(h.device))
+    if st != FLCE_OK:
+        raise FlceError(st, "flce_fwd_bwd")
+    return loss, lse, dh, dw
+
+
+def linear_cross_entropy_forward(h, w, labels, ignore_index: int = -100, reduction: str = "mean"):
+    """Loss and per-row LSE only (flce_fwd)."""
+    import torch
+    _check_inputs(h, w, labels)
+    n, d = h.shape
+    v = w.shape[0]
+    loss = torch.empty(1, dtype=torch.float32, device=h.device)
+    lse = torch.empty(n, dtype=torch.float32, device=h.device)
+    st = flce_fwd(h, w, labels, n, d, v, _dtype_code(h), ignore_index, _red_code(reduction), loss, lse,
+                  torch.cuda.current_stream(h.device))
+    if st != FLCE_OK:
+        raise FlceError(st, "flce_fwd")
+    return loss, lse

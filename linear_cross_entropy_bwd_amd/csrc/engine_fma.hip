@@ -1,0 +1,234 @@
+// fp32 engine: LDS-tiled FMA contractions for FLCE_F32 inputs.
+//
+// One 64x64 output tile per 256-thread block, 4x4 outputs per thread, K in
+// steps of 16 staged through LDS in k-major order.  Operands are described by
+// (pointer, leading dimension, k-major flag): a k-major operand has its
+// reduction index contiguous in memory.  The three contractions are
+//   logits  Z[t, j]  = sum_k H[t, k] W[j, k]        A = H (k-major), B = W (k-major)
+//   dH      dH[t, k] = sum_j G[t, j] W[j, k]        A = G (k-major), B = W (n-major)
+//   dW      dW[j, k] = sum_t G[t, j] H[t, k]        A = G^T (m-major), B = H (n-major)
+// fp32 inputs keep fp32 products and sums, which the fp32 tolerances need.
+#include "device_util.h"
+#include "flce_internal.h"
+
+namespace flce {
+
+namespace {
+
+constexpr int BM = 64, BN = 64, BK = 16;
+constexpr int kPad = 4;
+
+template <typename TA, typename TB, bool A_KMAJ, bool B_KMAJ>
+struct TileLoop {
+  // Accumulate acc[4][4] for the tile at (m0, n0); rows m < M, cols n < N, k < K.
+  static __device__ __forceinline__ void run(const TA* __restrict__ A, int64_t lda, const TB* __restrict__ B,
+                                             int64_t ldb, int64_t M, int64_t N, int64_t K, int64_t m0, int64_t n0,
+                                             float (&acc)[4][4]) {
+    __shared__ float As[BK][BM + kPad];
+    __shared__ float Bs[BK][BN + kPad];
+    const int tid = threadIdx.x;
+    const int tx = tid & 15, ty = tid >> 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
+
+    for (int64_t k0 = 0; k0 < K; k0 += BK) {
+      // A tile: BM x BK, 4 elements per thread
+      if (A_KMAJ) {
+        const int m = tid >> 2, kq = (tid & 3) * 4;
+        const int64_t gm = m0 + m;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t gk = k0 + kq + q;
+          As[kq + q][m] = (gm < M && gk < K) ? Elem<TA>::ld(A, gm * lda + gk) : 0.0f;
+        }
+      } else {
+        const int k = tid >> 4, mq = (tid & 15) * 4;
+        const int64_t gk = k0 + k;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t gm = m0 + mq + q;
+          As[k][mq + q] = (gm < M && gk < K) ? Elem<TA>::ld(A, gk * lda + gm) : 0.0f;
+        }
+      }
+      if (B_KMAJ) {
+        const int nn = tid >> 2, kq = (tid & 3) * 4;
+        const int64_t gn = n0 + nn;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t gk = k0 + kq + q;
+          Bs[kq + q][nn] = (gn < N && gk < K) ? Elem<TB>::ld(B, gn * ldb + gk) : 0.0f;
+        }
+      } else {
+        const int k = tid >> 4, nq = (tid & 15) * 4;
+        const int64_t gk = k0 + k;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t gn = n0 + nq + q;
+          Bs[k][nq + q] = (gn < N && gk < K) ? Elem<TB>::ld(B, gk * ldb + gn) : 0.0f;
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int kk = 0; kk < BK; ++kk) {
+        float a[4], b[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a[i] = As[kk][ty * 4 + i];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) b[j] = Bs[kk][tx * 4 + j];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+      }
+      __syncthreads();
+    }
+  }
+};
+
+// Logits tile (rows = chunk tokens, cols = vocabulary): per-row max and
+// sum-exp over the tile's 64 columns (one vocabulary group), the target
+// logit, and optionally exp(z - group max) into the chunk's buffer.
+template <typename T>
+__global__ __launch_bounds__(256) void fma_logits_kernel(const T* __restrict__ H, const T* __restrict__ W,
+                                                         int64_t rows, int64_t d, int64_t v, int64_t vp,
+                                                         const int64_t* __restrict__ labels, float* __restrict__ zy,
+                                                         float* __restrict__ pm, float* __restrict__ ps, int64_t C,
+                                                         float* __restrict__ prob) {
+  const int64_t m0 = static_cast<int64_t>(blockIdx.x) * BM;
+  const int64_t n0 = static_cast<int64_t>(blockIdx.y) * BN;
+  float acc[4][4];
+  TileLoop<T, T, true, true>::run(H, d, W, d, rows, v, d, m0, n0, acc);
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  const int64_t g = blockIdx.y;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t t = m0 + ty * 4 + i;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (n0 + tx * 4 + j < v) mx = fmaxf(mx, acc[i][j]);
+    for (int off = 8; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    float e[4], s = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      e[j] = (n0 + tx * 4 + j < v) ? fast_exp(acc[i][j] - mx) : 0.0f;
+      s += e[j];
+    }
+    for (int off = 8; off > 0; off >>= 1) s += __shfl_xor(s, off);
+    if (t < rows) {
+      if (tx == 0) {
+        pm[g * C + t] = mx;
+        ps[g * C + t] = s;
+      }
+      const int64_t y = labels[t];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t n = n0 + tx * 4 + j;
+        if (n == y && n < v) zy[t] = acc[i][j];
+        if (prob != nullptr && n < vp) prob[t * vp + n] = e[j];
+      }
+    }
+  }
+}
+
+// dH[t, :] (or a split partial) = G[t, :] . W
+template <typename T>
+__global__ __launch_bounds__(256) void fma_dh_kernel(const float* __restrict__ G, int64_t vp, const T* __restrict__ W,
+                                                     int64_t rows, int64_t d, int64_t v, T* __restrict__ out) {
+  const int64_t m0 = static_cast<int64_t>(blockIdx.x) * BM;
+  const int64_t n0 = static_cast<int64_t>(blockIdx.y) * BN;
+  float acc[4][4];
+  TileLoop<float, T, true, false>::run(G, vp, W, d, rows, d, v, m0, n0, acc);
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t t = m0 + ty * 4 + i;
+    if (t >= rows) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t n = n0 + tx * 4 + j;
+      if (n < d) Elem<T>::st(out, t * d + n, acc[i][j]);
+    }
+  }
+}
+
+// dW contribution of one chunk: partial[j, :] = sum_t G[t, j] H[t, :], merged
+// into the fp32 accumulator / output according to the chunk's mode.
+template <typename T>
+__global__ __launch_bounds__(256) void fma_dw_kernel(const float* __restrict__ G, int64_t vp, const T* __restrict__ H,
+                                                     int64_t rows, int64_t d, int64_t v, float* __restrict__ acc_buf,
+                                                     T* __restrict__ out, int mode) {
+  const int64_t m0 = static_cast<int64_t>(blockIdx.x) * BM;
+  const int64_t n0 = static_cast<int64_t>(blockIdx.y) * BN;
+  float acc[4][4];
+  TileLoop<float, T, false, false>::run(G, vp, H, d, v, d, rows, m0, n0, acc);
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t j = m0 + ty * 4 + i;
+    if (j >= v) continue;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t n = n0 + tx * 4 + q;
+      if (n >= d) continue;
+      const int64_t o = j * d + n;
+      const float x = acc[i][q];
+      switch (mode) {
+        case DW_SINGLE: Elem<T>::st(out, o, x); break;
+        case DW_FIRST: acc_buf[o] = x; break;
+        case DW_MID: acc_buf[o] += x; break;
+        default: Elem<T>::st(out, o, acc_buf[o] + x); break;
+      }
+    }
+  }
+}
+
+inline dim3 grid2(int64_t m, int64_t n) {
+  return dim3(static_cast<unsigned>((m + BM - 1) / BM), static_cast<unsigned>((n + BN - 1) / BN));
+}
+
+}  // namespace
+
+hipError_t fma_logits(const Plan& p, const Work& w, const ChunkArgs& a, int store_prob, hipStream_t s) {
+  float* prob = store_prob ? static_cast<float*>(w.prob) : nullptr;
+  const dim3 grid = grid2(a.rows, p.v);
+  if (p.dtype == FLCE_F32)
+    fma_logits_kernel<float><<<grid, 256, 0, s>>>(static_cast<const float*>(a.h), static_cast<const float*>(a.w),
+                                                  a.rows, p.d, p.v, p.vp, a.labels, w.zy, w.pm, w.ps, p.chunk, prob);
+  else
+    fma_logits_kernel<bf16_t><<<grid, 256, 0, s>>>(static_cast<const bf16_t*>(a.h), static_cast<const bf16_t*>(a.w),
+                                                   a.rows, p.d, p.v, p.vp, a.labels, w.zy, w.pm, w.ps, p.chunk, prob);
+  return hipGetLastError();
+}
+
+hipError_t fma_dh(const Plan& p, const Work& w, const ChunkArgs& a, hipStream_t s) {
+  const dim3 grid = grid2(a.rows, p.d);
+  const float* G = static_cast<const float*>(w.prob);
+  if (p.dtype == FLCE_F32)
+    fma_dh_kernel<float><<<grid, 256, 0, s>>>(G, p.vp, static_cast<const float*>(a.w), a.rows, p.d, p.v,
+                                              static_cast<float*>(a.dh));
+  else
+    fma_dh_kernel<bf16_t><<<grid, 256, 0, s>>>(G, p.vp, static_cast<const bf16_t*>(a.w), a.rows, p.d, p.v,
+                                               static_cast<bf16_t*>(a.dh));
+  return hipGetLastError();
+}
+
+hipError_t fma_dw(const Plan& p, const Work& w, const ChunkArgs& a, hipStream_t s) {
+  const dim3 grid = grid2(p.v, p.d);
+  const float* G = static_cast<const float*>(w.prob);
+  if (p.dtype == FLCE_F32) {
+    // fp32 output doubles as the accumulator
+    float* out = static_cast<float*>(a.dw);
+    int mode = a.dw_mode == DW_FIRST ? DW_FIRST : (a.dw_mode == DW_SINGLE ? DW_SINGLE : DW_MID);
+    fma_dw_kernel<float><<<grid, 256, 0, s>>>(G, p.vp, static_cast<const float*>(a.h), a.rows, p.d, p.v, out, out,
+                                              mode);
+  } else {
+    fma_dw_kernel<bf16_t><<<grid, 256, 0, s>>>(G, p.vp, static_cast<const bf16_t*>(a.h), a.rows, p.d, p.v, w.dwacc,
+                                               static_cast<bf16_t*>(a.dw), a.dw_mode);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace flce

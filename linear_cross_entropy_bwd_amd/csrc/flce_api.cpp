@@ -1,0 +1,364 @@
+// C ABI of the fused linear cross-entropy library: argument checks, the
+// execution plan, the stream-ordered workspace, the per-chunk kernel sequence
+// and the timing instrumentation.
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <vector>
+
+#include "flce.h"
+#include "flce_internal.h"
+
+namespace flce {
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr size_t kDefaultProbBudget = size_t(1) << 30;  // bytes for the chunk's [C, vp] buffer
+constexpr int64_t kVocabPad = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int64_t env_i64(const char* name, int64_t fallback) {
+  const char* s = getenv(name);
+  if (s == nullptr || *s == '\0') return fallback;
+  char* end = nullptr;
+  long long v = strtoll(s, &end, 10);
+  if (end == s || v <= 0) return fallback;
+  return static_cast<int64_t>(v);
+}
+
+bool mul_ok(int64_t a, int64_t b) { return a > 0 && b > 0 && a <= (int64_t(1) << 62) / b; }
+
+}  // namespace
+
+// Chunk rows C: as many rows as the probability-buffer budget allows (a
+// multiple of 256 rows once that many fit), never more than half of the rows
+// (rounded up to 16) so that the buffer stays well below the [n, v] logits it
+// replaces, and at least 16.
+int make_plan(int64_t n, int64_t d, int64_t v, int32_t dtype, int32_t with_bwd, Plan* p) {
+  if (p == nullptr || n <= 0 || d <= 0 || v <= 0) return FLCE_ERR_INVALID_ARG;
+  if (dtype != FLCE_BF16 && dtype != FLCE_F32) return FLCE_ERR_INVALID_ARG;
+  if (!mul_ok(n, d) || !mul_ok(v, d) || v > (int64_t(1) << 40) || n > (int64_t(1) << 40))
+    return FLCE_ERR_INVALID_ARG;
+  Plan q;
+  memset(&q, 0, sizeof(q));
+  q.n = n;
+  q.d = d;
+  q.v = v;
+  q.dtype = dtype;
+  q.with_bwd = with_bwd ? 1 : 0;
+  q.engine = ENGINE_FMA;
+  q.group = q.engine == ENGINE_MFMA ? 128 : 64;
+  const int64_t prob_elem = q.engine == ENGINE_MFMA ? 2 : 4;
+  q.vp = (v + kVocabPad - 1) / kVocabPad * kVocabPad;
+  q.ngroups = (v + q.group - 1) / q.group;
+
+  const int64_t budget = env_i64("FLCE_WORKSPACE_CAP_BYTES", static_cast<int64_t>(kDefaultProbBudget));
+  int64_t c_budget = budget / (q.vp * prob_elem);
+  c_budget = c_budget >= 256 ? c_budget / 256 * 256 : (c_budget / 16) * 16;
+  if (c_budget < 16) c_budget = 16;
+  const int64_t half = ((n + 1) / 2 + 15) / 16 * 16;
+  int64_t c = c_budget < half ? c_budget : half;
+  c = env_i64("FLCE_CHUNK_ROWS", c);
+  if (c > n) c = n;
+  q.chunk = c;
+  q.nchunks = (n + c - 1) / c;
+  q.dh_splits = 1;
+  q.dw_acc = (with_bwd && dtype == FLCE_BF16 && q.nchunks > 1) ? 1 : 0;
+  if (!mul_ok(q.chunk, q.vp) || !mul_ok(q.ngroups, q.chunk)) return FLCE_ERR_INVALID_ARG;
+
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align_up(bytes);
+    return o;
+  };
+  q.off_nvalid = take(sizeof(int32_t));
+  q.off_zy = take(sizeof(float) * q.chunk);
+  q.off_gy = take(sizeof(float) * q.chunk);
+  q.off_lse = take(sizeof(float) * n);
+  q.off_loss = take(sizeof(float) * n);
+  q.off_pm = take(sizeof(float) * q.ngroups * q.chunk);
+  q.off_ps = take(sizeof(float) * q.ngroups * q.chunk);
+  q.prob_bytes = with_bwd ? static_cast<size_t>(q.chunk * q.vp * prob_elem) : 0;
+  q.off_prob = take(q.prob_bytes);
+  q.off_dwacc = take(q.dw_acc ? sizeof(float) * static_cast<size_t>(v * d) : 0);
+  q.off_dhpart = take(with_bwd && q.dh_splits > 1 ? sizeof(float) * q.dh_splits * q.chunk * d : 0);
+  q.total = off;
+  *p = q;
+  return FLCE_OK;
+}
+
+namespace {
+
+// ---- library-owned stream-ordered memory pool, one per device --------------------
+
+std::mutex g_pool_mu;
+hipMemPool_t g_pools[64];
+bool g_pool_init[64];
+
+hipError_t device_pool(int dev, hipMemPool_t* out) {
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_pool_mu);
+  if (!g_pool_init[dev]) {
+    hipMemPoolProps props;
+    memset(&props, 0, sizeof(props));
+    props.allocType = hipMemAllocationTypePinned;
+    props.handleTypes = hipMemHandleTypeNone;
+    props.location.type = hipMemLocationTypeDevice;
+    props.location.id = dev;
+    hipMemPool_t pool;
+    hipError_t e = hipMemPoolCreate(&pool, &props);
+    if (e != hipSuccess) return e;
+    uint64_t keep = UINT64_MAX;  // keep freed blocks cached for the next call
+    e = hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
+    if (e != hipSuccess) return e;
+    g_pools[dev] = pool;
+    g_pool_init[dev] = true;
+  }
+  *out = g_pools[dev];
+  return hipSuccess;
+}
+
+// ---- timing instrumentation -------------------------------------------------------
+
+struct Prof {
+  std::mutex mu;
+  bool on = false;
+  struct Pending {
+    int kind;
+    hipEvent_t a, b;
+  };
+  std::vector<Pending> pending;
+  int64_t launches[K_NUM_KINDS] = {};
+  double ms[K_NUM_KINDS] = {};
+};
+Prof g_prof;
+
+const char* const kKindNames[K_NUM_KINDS] = {"label_scan", "logits_lse", "lse_merge", "grad_inplace",
+                                             "dh_gemm",    "dh_reduce",  "dw_gemm",   "loss_reduce"};
+
+template <class F>
+hipError_t timed(int kind, hipStream_t s, F&& launch) {
+  if (!g_prof.on) return launch();
+  hipEvent_t a = nullptr, b = nullptr;
+  if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) return hipErrorOutOfMemory;
+  hipEventRecord(a, s);
+  hipError_t e = launch();
+  hipEventRecord(b, s);
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  g_prof.pending.push_back({kind, a, b});
+  return e;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? FLCE_OK : FLCE_ERR_HIP; }
+
+bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
+
+int check_common(const void* h, const void* w, const int64_t* labels, int64_t n, int64_t d, int64_t v,
+                 flce_dtype dtype, flce_reduction reduction, const float* loss_out, const float* lse_out) {
+  if (h == nullptr || w == nullptr || labels == nullptr || loss_out == nullptr) return FLCE_ERR_INVALID_ARG;
+  if (n <= 0 || d <= 0 || v <= 0) return FLCE_ERR_INVALID_ARG;
+  if (dtype != FLCE_BF16 && dtype != FLCE_F32) return FLCE_ERR_INVALID_ARG;
+  if (reduction != FLCE_MEAN && reduction != FLCE_SUM) return FLCE_ERR_INVALID_ARG;
+  const int64_t elem = dtype == FLCE_BF16 ? 2 : 4;
+  if ((d * elem) % 16 != 0 || !aligned(h, 16) || !aligned(w, 16)) return FLCE_ERR_ALIGNMENT;
+  if (!aligned(labels, 8) || !aligned(loss_out, 4) || (lse_out != nullptr && !aligned(lse_out, 4)))
+    return FLCE_ERR_ALIGNMENT;
+  return FLCE_OK;
+}
+
+Work carve(const Plan& p, char* base) {
+  Work w;
+  w.nvalid = reinterpret_cast<int32_t*>(base + p.off_nvalid);
+  w.zy = reinterpret_cast<float*>(base + p.off_zy);
+  w.gy = reinterpret_cast<float*>(base + p.off_gy);
+  w.lse = reinterpret_cast<float*>(base + p.off_lse);
+  w.loss_rows = reinterpret_cast<float*>(base + p.off_loss);
+  w.pm = reinterpret_cast<float*>(base + p.off_pm);
+  w.ps = reinterpret_cast<float*>(base + p.off_ps);
+  w.prob = base + p.off_prob;
+  w.dwacc = reinterpret_cast<float*>(base + p.off_dwacc);
+  w.dhpart = reinterpret_cast<float*>(base + p.off_dhpart);
+  return w;
+}
+
+// The kernel sequence of one call; workspace already allocated.
+hipError_t run(const Plan& p, const Work& wk, const void* h, const void* w, const int64_t* labels,
+               int64_t ignore_index, int32_t reduction, float* loss_out, float* lse_out, void* dh_out, void* dw_out,
+               hipStream_t s) {
+  const int64_t elem = p.dtype == FLCE_BF16 ? 2 : 4;
+  hipError_t e = timed(K_LABEL_SCAN, s, [&] { return launch_label_scan(p, wk, labels, ignore_index, s); });
+  if (e != hipSuccess) return e;
+  float* lse_base = lse_out != nullptr ? lse_out : wk.lse;
+  for (int64_t c = 0; c < p.nchunks; ++c) {
+    ChunkArgs a;
+    a.row0 = c * p.chunk;
+    a.rows = p.n - a.row0 < p.chunk ? p.n - a.row0 : p.chunk;
+    a.h = static_cast<const char*>(h) + a.row0 * p.d * elem;
+    a.w = w;
+    a.labels = labels + a.row0;
+    a.ignore_index = ignore_index;
+    a.reduction = reduction;
+    a.lse_rows = lse_base + a.row0;
+    a.dh = dh_out != nullptr ? static_cast<char*>(dh_out) + a.row0 * p.d * elem : nullptr;
+    a.dw = dw_out;
+    a.dw_mode = p.nchunks == 1 ? DW_SINGLE : (c == 0 ? DW_FIRST : (c == p.nchunks - 1 ? DW_LAST : DW_MID));
+
+    e = timed(K_LOGITS, s, [&] {
+      return p.engine == ENGINE_MFMA ? mfma_logits(p, wk, a, p.with_bwd, s) : fma_logits(p, wk, a, p.with_bwd, s);
+    });
+    if (e != hipSuccess) return e;
+    e = timed(K_LSE_MERGE, s, [&] { return launch_lse_merge(p, wk, a, p.with_bwd, s); });
+    if (e != hipSuccess) return e;
+    if (!p.with_bwd) continue;
+    e = timed(K_GRAD, s, [&] { return launch_grad(p, wk, a, s); });
+    if (e != hipSuccess) return e;
+    e = timed(K_DH, s, [&] { return p.engine == ENGINE_MFMA ? mfma_dh(p, wk, a, s) : fma_dh(p, wk, a, s); });
+    if (e != hipSuccess) return e;
+    if (p.dh_splits > 1) {
+      e = timed(K_DH_REDUCE, s, [&] { return launch_dh_reduce(p, wk, a, s); });
+      if (e != hipSuccess) return e;
+    }
+    e = timed(K_DW, s, [&] { return p.engine == ENGINE_MFMA ? mfma_dw(p, wk, a, s) : fma_dw(p, wk, a, s); });
+    if (e != hipSuccess) return e;
+  }
+  return timed(K_LOSS, s, [&] { return launch_loss_reduce(p, wk, reduction, loss_out, s); });
+}
+
+int call(const void* h, const void* w, const int64_t* labels, int64_t n, int64_t d, int64_t v, flce_dtype dtype,
+         int64_t ignore_index, flce_reduction reduction, float* loss_out, float* lse_out, void* dh_out,
+         void* dw_out, hipStream_t stream, int with_bwd) {
+  int st = check_common(h, w, labels, n, d, v, dtype, reduction, loss_out, lse_out);
+  if (st != FLCE_OK) return st;
+  if (with_bwd) {
+    if (dh_out == nullptr || dw_out == nullptr) return FLCE_ERR_INVALID_ARG;
+    if (!aligned(dh_out, 16) || !aligned(dw_out, 16)) return FLCE_ERR_ALIGNMENT;
+  }
+  Plan p;
+  st = make_plan(n, d, v, dtype, with_bwd, &p);
+  if (st != FLCE_OK) return st;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FLCE_ERR_HIP;
+  hipMemPool_t pool;
+  if (device_pool(dev, &pool) != hipSuccess) return FLCE_ERR_HIP;
+  void* base = nullptr;
+  if (hipMallocFromPoolAsync(&base, p.total, pool, stream) != hipSuccess || base == nullptr) {
+    (void)hipGetLastError();
+    return FLCE_ERR_OOM;
+  }
+  const Work wk = carve(p, static_cast<char*>(base));
+  hipError_t e = run(p, wk, h, w, labels, ignore_index, reduction, loss_out, lse_out, dh_out, dw_out, stream);
+  hipError_t f = hipFreeAsync(base, stream);
+  if (e != hipSuccess) return FLCE_ERR_HIP;
+  return status_of(f);
+}
+
+}  // namespace
+}  // namespace flce
+
+extern "C" {
+
+int flce_fwd_bwd(const void* h, const void* w, const int64_t* labels, int64_t n, int64_t d, int64_t v,
+                 flce_dtype dtype, int64_t ignore_index, flce_reduction reduction, float* loss_out, float* lse_out,
+                 void* dh_out, void* dw_out, hipStream_t stream) {
+  return flce::call(h, w, labels, n, d, v, dtype, ignore_index, reduction, loss_out, lse_out, dh_out, dw_out, stream,
+                    1);
+}
+
+int flce_fwd(const void* h, const void* w, const int64_t* labels, int64_t n, int64_t d, int64_t v, flce_dtype dtype,
+             int64_t ignore_index, flce_reduction reduction, float* loss_out, float* lse_out, hipStream_t stream) {
+  return flce::call(h, w, labels, n, d, v, dtype, ignore_index, reduction, loss_out, lse_out, nullptr, nullptr,
+                    stream, 0);
+}
+
+size_t flce_workspace_bytes(int64_t n, int64_t d, int64_t v, flce_dtype dtype, int with_bwd) {
+  flce::Plan p;
+  if (flce::make_plan(n, d, v, dtype, with_bwd, &p) != FLCE_OK) return 0;
+  return p.total;
+}
+
+int flce_plan_info(int64_t n, int64_t d, int64_t v, flce_dtype dtype, int with_bwd, flce_plan_t* out) {
+  if (out == nullptr) return FLCE_ERR_INVALID_ARG;
+  flce::Plan p;
+  const int st = flce::make_plan(n, d, v, dtype, with_bwd, &p);
+  if (st != FLCE_OK) return st;
+  out->chunk_rows = p.chunk;
+  out->num_chunks = p.nchunks;
+  out->vocab_pitch = p.vp;
+  out->group_cols = p.group;
+  out->dh_splits = p.dh_splits;
+  out->engine = p.engine;
+  out->dw_accumulator = p.dw_acc;
+  out->workspace_bytes = p.total;
+  out->prob_buffer_bytes = p.prob_bytes;
+  return FLCE_OK;
+}
+
+const char* flce_strerror(int status) {
+  switch (status) {
+    case FLCE_OK: return "success";
+    case FLCE_ERR_INVALID_ARG: return "invalid argument (null pointer, non-positive size, unknown enum or size overflow)";
+    case FLCE_ERR_ALIGNMENT: return "misaligned pointer or row pitch (rows must start on 16-byte boundaries)";
+    case FLCE_ERR_OOM: return "workspace allocation failed";
+    case FLCE_ERR_HIP: return "HIP runtime or kernel launch error";
+    default: return "unknown status";
+  }
+}
+
+int flce_profile_enable(int on) {
+  std::lock_guard<std::mutex> lk(flce::g_prof.mu);
+  flce::g_prof.on = on != 0;
+  return FLCE_OK;
+}
+
+int flce_profile_read(int max_kinds, int64_t* launches, double* total_ms) {
+  using flce::g_prof;
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  int status = FLCE_OK;
+  for (auto& q : g_prof.pending) {
+    float ms = 0.0f;
+    if (hipEventSynchronize(q.b) != hipSuccess || hipEventElapsedTime(&ms, q.a, q.b) != hipSuccess)
+      status = FLCE_ERR_HIP;
+    g_prof.launches[q.kind] += 1;
+    g_prof.ms[q.kind] += ms;
+    hipEventDestroy(q.a);
+    hipEventDestroy(q.b);
+  }
+  g_prof.pending.clear();
+  for (int k = 0; k < flce::K_NUM_KINDS && k < max_kinds; ++k) {
+    if (launches) launches[k] = g_prof.launches[k];
+    if (total_ms) total_ms[k] = g_prof.ms[k];
+    g_prof.launches[k] = 0;
+    g_prof.ms[k] = 0.0;
+  }
+  return status;
+}
+
+const char* flce_profile_kind_name(int kind) {
+  if (kind < 0 || kind >= flce::K_NUM_KINDS) return nullptr;
+  return flce::kKindNames[kind];
+}
+
+int flce_memory_high_water(int reset, uint64_t* used_high_bytes) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FLCE_ERR_HIP;
+  hipMemPool_t pool;
+  if (flce::device_pool(dev, &pool) != hipSuccess) return FLCE_ERR_HIP;
+  if (used_high_bytes != nullptr) {
+    uint64_t v = 0;
+    if (hipMemPoolGetAttribute(pool, hipMemPoolAttrUsedMemHigh, &v) != hipSuccess) return FLCE_ERR_HIP;
+    *used_high_bytes = v;
+  }
+  if (reset) {
+    uint64_t zero = 0;
+    if (hipMemPoolSetAttribute(pool, hipMemPoolAttrUsedMemHigh, &zero) != hipSuccess) return FLCE_ERR_HIP;
+  }
+  return FLCE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,107 @@
+// Internal declarations shared by the host orchestration and the kernel
+// translation units of the fused linear cross-entropy library (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "flce.h"
+
+namespace flce {
+
+enum Engine : int32_t { ENGINE_MFMA = 0, ENGINE_FMA = 1 };
+
+// dW epilogue mode for one chunk of the token reduction.
+enum DwMode : int32_t {
+  DW_SINGLE = 0,  // only chunk: out = partial
+  DW_FIRST = 1,   // acc = partial
+  DW_MID = 2,     // acc += partial
+  DW_LAST = 3     // out = acc + partial
+};
+
+// Execution plan: how a call is cut into chunks and where its workspace lives.
+struct Plan {
+  int64_t n, d, v;
+  int32_t dtype;
+  int32_t engine;
+  int32_t with_bwd;
+  int64_t chunk;       // token rows per chunk (C)
+  int64_t nchunks;
+  int64_t vp;          // row pitch (elements) of the chunk's probability/gradient buffer
+  int64_t group;       // vocabulary columns per partial (max, sum-exp) pair
+  int64_t ngroups;
+  int64_t dh_splits;   // split of the K = vocabulary reduction of dH
+  int32_t dw_acc;      // dW accumulates across chunks in an fp32 workspace buffer
+  // byte offsets inside the single workspace allocation
+  size_t off_nvalid, off_zy, off_gy, off_lse, off_loss, off_pm, off_ps, off_prob, off_dwacc, off_dhpart;
+  size_t total;
+  size_t prob_bytes;
+};
+
+int make_plan(int64_t n, int64_t d, int64_t v, int32_t dtype, int32_t with_bwd, Plan* p);
+
+// Pointers into the workspace for one call.
+struct Work {
+  int32_t* nvalid;   // [1]
+  float* zy;         // [C]   target logit of each chunk row (0 until found)
+  float* gy;         // [C]   gradient value at the target column
+  float* lse;        // [n]   used when the caller passes no lse_out
+  float* loss_rows;  // [n]   per-row NLL (unscaled; 0 for ignored rows)
+  float* pm;         // [G][C] partial row max per vocabulary group; becomes the softmax factor
+  float* ps;         // [G][C] partial sum of exp(z - max) per group
+  void* prob;        // [C][vp] exp(z - group max), turned into G in place (dtype of the engine)
+  float* dwacc;      // [v][d] fp32 dW accumulator (when Plan::dw_acc)
+  float* dhpart;     // [S][C][d] fp32 split-vocabulary partials of dH (when dh_splits > 1)
+};
+
+// Kernel kinds for the timing instrumentation.
+enum Kind : int {
+  K_LABEL_SCAN = 0,
+  K_LOGITS = 1,
+  K_LSE_MERGE = 2,
+  K_GRAD = 3,
+  K_DH = 4,
+  K_DH_REDUCE = 5,
+  K_DW = 6,
+  K_LOSS = 7,
+  K_NUM_KINDS = 8
+};
+
+// --- per-chunk launch arguments --------------------------------------------------
+
+struct ChunkArgs {
+  const void* h;            // chunk's first row of H
+  const void* w;
+  const int64_t* labels;    // chunk's first label
+  int64_t rows;             // rows in this chunk (<= plan.chunk)
+  int64_t row0;             // index of the chunk's first row in the whole call
+  int64_t ignore_index;
+  int32_t reduction;
+  float* lse_rows;          // chunk's slice of the LSE output
+  void* dh;                 // chunk's first row of dH output
+  void* dw;                 // dW output
+  int32_t dw_mode;
+};
+
+// --- launchers (each returns the launch status) ---------------------------------
+
+// Small kernels (kernels_common.hip).
+hipError_t launch_label_scan(const Plan& p, const Work& w, const int64_t* labels, int64_t ignore_index,
+                             hipStream_t s);
+hipError_t launch_lse_merge(const Plan& p, const Work& w, const ChunkArgs& a, int with_grad, hipStream_t s);
+hipError_t launch_grad(const Plan& p, const Work& w, const ChunkArgs& a, hipStream_t s);
+hipError_t launch_loss_reduce(const Plan& p, const Work& w, int32_t reduction, float* loss_out, hipStream_t s);
+hipError_t launch_dh_reduce(const Plan& p, const Work& w, const ChunkArgs& a, hipStream_t s);
+
+// fp32 FMA engine (engine_fma.hip): any dtype, used for FLCE_F32.
+hipError_t fma_logits(const Plan& p, const Work& w, const ChunkArgs& a, int store_prob, hipStream_t s);
+hipError_t fma_dh(const Plan& p, const Work& w, const ChunkArgs& a, hipStream_t s);
+hipError_t fma_dw(const Plan& p, const Work& w, const ChunkArgs& a, hipStream_t s);
+
+// bf16 matrix-core engine (engine_mfma.hip): FLCE_BF16.
+hipError_t mfma_logits(const Plan& p, const Work& w, const ChunkArgs& a, int store_prob, hipStream_t s);
+hipError_t mfma_dh(const Plan& p, const Work& w, const ChunkArgs& a, hipStream_t s);
+hipError_t mfma_dw(const Plan& p, const Work& w, const ChunkArgs& a, hipStream_t s);
+
+}  // namespace flce

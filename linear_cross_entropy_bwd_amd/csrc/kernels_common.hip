@@ -1,0 +1,206 @@
+// Bandwidth-light kernels around the three contractions:
+//   label scan (valid-row count), partial-LSE merge and per-row loss,
+//   in-place softmax-minus-one-hot gradient, split-vocabulary dH reduction,
+//   and the fixed-order loss reduction.
+#include "device_util.h"
+#include "flce_internal.h"
+
+#include <math.h>
+
+namespace flce {
+
+namespace {
+
+constexpr int kScanThreads = 1024;
+
+// Number of rows whose label is not ignore_index; also zeroes the per-chunk
+// target-logit slots that the logits epilogue fills.
+__global__ __launch_bounds__(kScanThreads) void label_scan_kernel(const int64_t* __restrict__ labels, int64_t n,
+                                                                  int64_t ignore_index, int32_t* __restrict__ nvalid,
+                                                                  float* __restrict__ zy, int64_t chunk) {
+  __shared__ int32_t part[kScanThreads / 64];
+  int32_t cnt = 0;
+  for (int64_t i = threadIdx.x; i < n; i += kScanThreads) cnt += labels[i] != ignore_index ? 1 : 0;
+  for (int64_t i = threadIdx.x; i < chunk; i += kScanThreads) zy[i] = 0.0f;
+  for (int off = 32; off > 0; off >>= 1) cnt += __shfl_xor(cnt, off);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) part[wave] = cnt;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int32_t t = 0;
+    for (int k = 0; k < kScanThreads / 64; ++k) t += part[k];
+    *nvalid = t;
+  }
+}
+
+__device__ __forceinline__ float row_scale(int32_t nvalid, int32_t reduction) {
+  if (reduction == FLCE_SUM) return 1.0f;
+  return nvalid > 0 ? 1.0f / static_cast<float>(nvalid) : 0.0f;
+}
+
+// Merge the per-group (max, sum-exp) partials of each chunk row into
+//   lse = m + log(sum_g s_g * exp(m_g - m)),  m = max_g m_g
+// (the online log-sum-exp of the blog's section "1. Fused Linear Cross-Entropy
+// with Online LogSumExp", step 3, done as an exact two-pass merge), and the
+// row's NLL lse - z_y.  With the gradient, each partial max is replaced by
+// the factor scale_i * exp(m_g - lse) that turns the stored exp(z - m_g) into
+// the scaled softmax, and the value the target column takes is precomputed.
+constexpr int kMergeRows = 32;
+constexpr int kMergeSlices = 8;
+
+__global__ __launch_bounds__(kMergeRows* kMergeSlices) void lse_merge_kernel(
+    float* __restrict__ pm, const float* __restrict__ ps, int64_t C, int64_t G, int64_t rows,
+    const int64_t* __restrict__ labels, int64_t ignore_index, int64_t v, const int32_t* __restrict__ nvalid,
+    int32_t reduction, float* __restrict__ zy, float* __restrict__ gy, float* __restrict__ lse_rows,
+    float* __restrict__ loss_rows, int with_grad) {
+  __shared__ float red[kMergeSlices][kMergeRows];
+  __shared__ float row_lse[kMergeRows];
+  const int r = threadIdx.x % kMergeRows;
+  const int sl = threadIdx.x / kMergeRows;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kMergeRows + r;
+  const bool live = t < rows;
+
+  float m = -INFINITY;
+  if (live)
+    for (int64_t g = sl; g < G; g += kMergeSlices) m = fmaxf(m, pm[g * C + t]);
+  red[sl][r] = m;
+  __syncthreads();
+  m = red[0][r];
+  for (int k = 1; k < kMergeSlices; ++k) m = fmaxf(m, red[k][r]);
+  __syncthreads();
+
+  float s = 0.0f;
+  if (live)
+    for (int64_t g = sl; g < G; g += kMergeSlices) {
+      const float mg = pm[g * C + t];
+      s += ps[g * C + t] * fast_exp(mg - m);
+    }
+  red[sl][r] = s;
+  __syncthreads();
+  if (sl == 0) {
+    float tot = 0.0f;
+    for (int k = 0; k < kMergeSlices; ++k) tot += red[k][r];
+    const float l = m + logf(tot);
+    row_lse[r] = l;
+    if (live) {
+      const int64_t y = labels[t];
+      const bool valid = y != ignore_index;
+      const float z = zy[t];
+      zy[t] = 0.0f;  // ready for the next chunk
+      lse_rows[t] = l;
+      loss_rows[t] = valid ? l - z : 0.0f;
+      if (with_grad) {
+        const float sc = valid ? row_scale(*nvalid, reduction) : 0.0f;
+        const bool hit = valid && y >= 0 && y < v;
+        gy[t] = hit ? (fast_exp(z - l) - 1.0f) * sc : 0.0f;
+      }
+    }
+  }
+  if (!with_grad) return;
+  __syncthreads();
+  if (!live) return;
+  const float l = row_lse[r];
+  const int64_t y = labels[t];
+  const float sc = y != ignore_index ? row_scale(*nvalid, reduction) : 0.0f;
+  for (int64_t g = sl; g < G; g += kMergeSlices) pm[g * C + t] = sc * fast_exp(pm[g * C + t] - l);
+}
+
+// G = P * factor(group, row), the target column takes the precomputed value;
+// columns in [v, vp) stay 0.  8 consecutive columns per thread.
+template <typename TP>
+__global__ __launch_bounds__(256) void grad_kernel(TP* __restrict__ prob, int64_t vp, int64_t v, int64_t group,
+                                                   const float* __restrict__ factor, int64_t C,
+                                                   const float* __restrict__ gy, const int64_t* __restrict__ labels) {
+  const int64_t t = blockIdx.x;
+  const int64_t c0 = (static_cast<int64_t>(blockIdx.y) * 256 + threadIdx.x) * 8;
+  if (c0 >= vp) return;
+  const float f = c0 < v ? factor[(c0 / group) * C + t] : 0.0f;
+  const int64_t y = labels[t];
+  const float gt = gy[t];
+  TP* row = prob + t * vp;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int64_t c = c0 + k;
+    float g = Elem<TP>::ld(row, c) * f;
+    if (c == y) g = gt;
+    if (c >= v) g = 0.0f;
+    Elem<TP>::st(row, c, g);
+  }
+}
+
+// dH rows = sum of the split partials, rounded to the output type.
+template <typename TO>
+__global__ __launch_bounds__(256) void dh_reduce_kernel(const float* __restrict__ part, int64_t splits,
+                                                        int64_t stride, int64_t count, TO* __restrict__ out) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= count) return;
+  float acc = 0.0f;
+  for (int64_t s = 0; s < splits; ++s) acc += part[s * stride + i];
+  Elem<TO>::st(out, i, acc);
+}
+
+// loss = scale * sum_i loss_rows[i], summed in fp64 in a fixed order.
+__global__ __launch_bounds__(1024) void loss_reduce_kernel(const float* __restrict__ loss_rows, int64_t n,
+                                                           const int32_t* __restrict__ nvalid, int32_t reduction,
+                                                           float* __restrict__ loss_out) {
+  __shared__ double part[1024];
+  double acc = 0.0;
+  for (int64_t i = threadIdx.x; i < n; i += 1024) acc += static_cast<double>(loss_rows[i]);
+  part[threadIdx.x] = acc;
+  __syncthreads();
+  for (int s = 512; s > 0; s >>= 1) {
+    if (threadIdx.x < s) part[threadIdx.x] += part[threadIdx.x + s];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const int32_t nv = *nvalid;
+    const double sc = reduction == FLCE_SUM ? 1.0 : (nv > 0 ? 1.0 / static_cast<double>(nv) : 0.0);
+    *loss_out = static_cast<float>(part[0] * sc);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_label_scan(const Plan& p, const Work& w, const int64_t* labels, int64_t ignore_index,
+                             hipStream_t s) {
+  label_scan_kernel<<<1, kScanThreads, 0, s>>>(labels, p.n, ignore_index, w.nvalid, w.zy, p.chunk);
+  return hipGetLastError();
+}
+
+hipError_t launch_lse_merge(const Plan& p, const Work& w, const ChunkArgs& a, int with_grad, hipStream_t s) {
+  const int64_t blocks = (a.rows + kMergeRows - 1) / kMergeRows;
+  lse_merge_kernel<<<static_cast<unsigned>(blocks), kMergeRows * kMergeSlices, 0, s>>>(
+      w.pm, w.ps, p.chunk, p.ngroups, a.rows, a.labels, a.ignore_index, p.v, w.nvalid, a.reduction, w.zy, w.gy,
+      a.lse_rows, w.loss_rows + a.row0, with_grad);
+  return hipGetLastError();
+}
+
+hipError_t launch_grad(const Plan& p, const Work& w, const ChunkArgs& a, hipStream_t s) {
+  dim3 grid(static_cast<unsigned>(a.rows), static_cast<unsigned>((p.vp / 8 + 255) / 256));
+  if (p.engine == ENGINE_MFMA)
+    grad_kernel<bf16_t><<<grid, 256, 0, s>>>(static_cast<bf16_t*>(w.prob), p.vp, p.v, p.group, w.pm, p.chunk, w.gy,
+                                             a.labels);
+  else
+    grad_kernel<float><<<grid, 256, 0, s>>>(static_cast<float*>(w.prob), p.vp, p.v, p.group, w.pm, p.chunk, w.gy,
+                                            a.labels);
+  return hipGetLastError();
+}
+
+hipError_t launch_dh_reduce(const Plan& p, const Work& w, const ChunkArgs& a, hipStream_t s) {
+  const int64_t count = a.rows * p.d;
+  const unsigned blocks = static_cast<unsigned>((count + 255) / 256);
+  if (p.dtype == FLCE_BF16)
+    dh_reduce_kernel<bf16_t><<<blocks, 256, 0, s>>>(w.dhpart, p.dh_splits, p.chunk * p.d, count,
+                                                    static_cast<bf16_t*>(a.dh));
+  else
+    dh_reduce_kernel<float><<<blocks, 256, 0, s>>>(w.dhpart, p.dh_splits, p.chunk * p.d, count,
+                                                   static_cast<float*>(a.dh));
+  return hipGetLastError();
+}
+
+hipError_t launch_loss_reduce(const Plan& p, const Work& w, int32_t reduction, float* loss_out, hipStream_t s) {
+  loss_reduce_kernel<<<1, 1024, 0, s>>>(w.loss_rows, p.n, w.nvalid, reduction, loss_out);
+  return hipGetLastError();
+}
+
+}  // namespace flce

@@ -3,6 +3,7 @@ from .flce_oracle import (  # noqa: F401
     IGNORE_INDEX,
     flce_forward,
     flce_forward_backward,
+    flce_dw_rows,
     flce_rows,
     log_sum_exp,
     reduction_scale,

@@ -87,21 +87,34 @@ def log_sum_exp(z: np.ndarray) -> np.ndarray:
 
 
 def flce_forward(h, w, labels, ignore_index: int = IGNORE_INDEX, reduction: str = "mean",
-                 block_rows: int = 1024):
-    """Loss (float) and per-row LSE [N] (float64) of softmax(H W^T) against the labels."""
+                 block_rows: int = 1024, workers: int = 1):
+    """Loss (float) and per-row LSE [N] (float64) of softmax(H W^T) against the labels.
+
+    ``workers`` > 1 evaluates independent row blocks on that many threads; the
+    arithmetic of every block is unchanged.
+    """
     hd, wd, y = _as_f64(h), _as_f64(w), _as_labels(labels)
     n, v = hd.shape[0], wd.shape[0]
     valid = valid_rows(y, v, ignore_index)
     scale = reduction_scale(int(valid.sum()), reduction)
     lse = np.empty(n, dtype=np.float64)
     nll = np.zeros(n, dtype=np.float64)
-    for r0 in range(0, n, block_rows):
+
+    def block(r0):
         r1 = min(n, r0 + block_rows)
         z = hd[r0:r1] @ wd.T
         lse[r0:r1] = log_sum_exp(z)
-        vb = valid[r0:r1]
-        rows = np.flatnonzero(vb)
+        rows = np.flatnonzero(valid[r0:r1])
         nll[r0 + rows] = lse[r0 + rows] - z[rows, y[r0 + rows]]
+
+    starts = range(0, n, block_rows)
+    if workers > 1:
+        import concurrent.futures as cf
+        with cf.ThreadPoolExecutor(workers) as ex:
+            list(ex.map(block, starts))
+    else:
+        for r0 in starts:
+            block(r0)
     return float(scale * nll.sum()), lse
 
 
@@ -167,3 +180,36 @@ def flce_rows(h, w, labels, rows, ignore_index: int = IGNORE_INDEX, reduction: s
     g[~vr] = 0.0
     g *= scale
     return lse, g @ wd
+
+
+def flce_dw_rows(h, w, labels, lse, vocab_rows, ignore_index: int = IGNORE_INDEX, reduction: str = "mean",
+                 block_rows: int = 8192):
+    """dW rows for selected vocabulary ids, at any problem size.
+
+    dW_j = sum_i scale_i * (exp(z_ij - lse_i) - [y_i = j]) * H_i needs every
+    row's LSE, which the caller obtains from ``flce_forward`` (never from the
+    code under test).  Returns [len(vocab_rows), D] float64.
+    """
+    y = _as_labels(labels)
+    cols = np.asarray(vocab_rows, dtype=np.int64)
+    if hasattr(w, "detach"):
+        import torch
+        wj = _as_f64(w[torch.as_tensor(cols)])
+        v = w.shape[0]
+    else:
+        wj = _as_f64(np.asarray(w)[cols])
+        v = np.asarray(w).shape[0]
+    valid = valid_rows(y, v, ignore_index)
+    scale = reduction_scale(int(valid.sum()), reduction)
+    lse = np.asarray(lse, dtype=np.float64)
+    n = y.shape[0]
+    out = np.zeros((cols.size, wj.shape[1]), dtype=np.float64)
+    for r0 in range(0, n, block_rows):
+        r1 = min(n, r0 + block_rows)
+        hb = _as_f64(h[r0:r1])
+        g = np.exp(hb @ wj.T - lse[r0:r1, None])          # softmax columns j, [rows, |J|]
+        g -= (y[r0:r1, None] == cols[None, :])             # one-hot
+        g[~valid[r0:r1]] = 0.0
+        g *= scale
+        out += g.T @ hb
+    return out

@@ -1,0 +1,109 @@
+"""C-ABI checks that need no GPU: the library loads, exports every declared
+symbol, plans chunks as documented and rejects bad arguments before touching
+the device."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+import linear_cross_entropy_bwd_amd as flce
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    names = set()
+    for hdr in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(hdr).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names.update(re.findall(r"\b(flce_[a-z0-9_]+)\s*\(", text))
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    L = flce.lib()
+    names = _declared()
+    assert {"flce_fwd_bwd", "flce_fwd", "flce_workspace_bytes", "flce_strerror"} <= names
+    for name in sorted(names):
+        assert hasattr(L, name), f"{name} declared in include/ but not exported"
+    assert set(flce.EXPORTED) <= names
+
+
+def test_strerror():
+    for code in (0, -1, -2, -3, -4):
+        assert isinstance(flce.flce_strerror(code), str) and flce.flce_strerror(code)
+    assert flce.flce_strerror(-99) == "unknown status"
+
+
+@pytest.mark.parametrize("dtype", [flce.FLCE_BF16, flce.FLCE_F32])
+@pytest.mark.parametrize("shape", [(256, 512, 4096), (8192, 4096, 128256), (4096, 3584, 151936),
+                                   (32768, 4096, 128256), (16384, 4096, 32000), (37, 72, 1001), (1, 8, 3)])
+def test_plan_invariants(dtype, shape):
+    n, d, v = shape
+    p = flce.flce_plan_info(n, d, v, dtype, 1)
+    c = p["chunk_rows"]
+    assert 1 <= c <= n
+    assert p["num_chunks"] == -(-n // c)
+    if n >= 32:
+        assert c < n                                  # never a whole [n, v] buffer
+        assert p["prob_buffer_bytes"] < n * v * 4     # below the fp32 logits it replaces
+    assert p["vocab_pitch"] >= v and p["vocab_pitch"] % 256 == 0
+    assert p["workspace_bytes"] == flce.flce_workspace_bytes(n, d, v, dtype, 1)
+    assert p["workspace_bytes"] >= p["prob_buffer_bytes"]
+    fwd = flce.flce_plan_info(n, d, v, dtype, 0)
+    assert fwd["prob_buffer_bytes"] == 0
+    assert fwd["workspace_bytes"] <= p["workspace_bytes"]
+
+
+def test_plan_env_overrides(monkeypatch):
+    monkeypatch.setenv("FLCE_CHUNK_ROWS", "96")
+    assert flce.flce_plan_info(1000, 64, 500, flce.FLCE_F32, 1)["chunk_rows"] == 96
+    monkeypatch.delenv("FLCE_CHUNK_ROWS")
+    monkeypatch.setenv("FLCE_WORKSPACE_CAP_BYTES", str(64 * 1024 * 1024))
+    p = flce.flce_plan_info(8192, 4096, 128256, flce.FLCE_BF16, 1)
+    assert p["prob_buffer_bytes"] <= 64 * 1024 * 1024
+
+
+def test_invalid_sizes():
+    assert flce.flce_workspace_bytes(0, 8, 8, flce.FLCE_F32, 1) == 0
+    assert flce.flce_workspace_bytes(8, -1, 8, flce.FLCE_F32, 1) == 0
+    assert flce.flce_workspace_bytes(8, 8, 8, 7, 1) == 0
+    with pytest.raises(flce.FlceError):
+        flce.flce_plan_info(8, 8, 0, flce.FLCE_F32, 1)
+
+
+def test_argument_errors_before_any_device_work():
+    # All of these fail validation before the library makes a HIP call.
+    A = 1 << 20  # fake, 16-byte aligned addresses: never dereferenced
+    ok = dict(h=A, w=A, labels=A, n=4, d=8, v=16, dtype=flce.FLCE_F32, ignore_index=-100,
+              reduction=flce.FLCE_MEAN, loss_out=A, lse_out=None, dh_out=A, dw_out=A, stream=None)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return flce.flce_fwd_bwd(**a)
+
+    assert call(h=None) == flce.FLCE_ERR_INVALID_ARG
+    assert call(labels=None) == flce.FLCE_ERR_INVALID_ARG
+    assert call(loss_out=None) == flce.FLCE_ERR_INVALID_ARG
+    assert call(dh_out=None) == flce.FLCE_ERR_INVALID_ARG
+    assert call(n=0) == flce.FLCE_ERR_INVALID_ARG
+    assert call(d=-3) == flce.FLCE_ERR_INVALID_ARG
+    assert call(dtype=5) == flce.FLCE_ERR_INVALID_ARG
+    assert call(reduction=9) == flce.FLCE_ERR_INVALID_ARG
+    assert call(h=A + 4) == flce.FLCE_ERR_ALIGNMENT
+    assert call(dw_out=A + 8) == flce.FLCE_ERR_ALIGNMENT
+    assert call(d=6) == flce.FLCE_ERR_ALIGNMENT           # 24-byte fp32 rows
+    assert call(dtype=flce.FLCE_BF16, d=12) == flce.FLCE_ERR_ALIGNMENT
+    assert call(labels=A + 4) == flce.FLCE_ERR_ALIGNMENT
+    assert flce.flce_fwd(None, A, A, 4, 8, 16, flce.FLCE_F32, -100, 0, A, None, None) == flce.FLCE_ERR_INVALID_ARG
+
+
+def test_no_cpu_fallback(monkeypatch, tmp_path):
+    """Without the built library the binding raises instead of computing anything."""
+    monkeypatch.setattr(flce, "_lib", None)
+    monkeypatch.setattr(flce, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError):
+        flce.lib()

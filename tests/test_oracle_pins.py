@@ -17,7 +17,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import flce_forward, flce_forward_backward, flce_rows, log_sum_exp
+from oracle import flce_dw_rows, flce_forward, flce_forward_backward, flce_rows, log_sum_exp
 
 RTOL = 1e-12
 
@@ -338,3 +338,15 @@ def test_gaussian_logit_loss_level():
     loss, _ = flce_forward(h, w, y)
     s2 = 0.02 ** 2 * d
     assert abs(loss - (math.log(v) + s2 / 2)) < 0.05
+
+
+@pytest.mark.parametrize("reduction", ["mean", "sum"])
+def test_dw_rows_and_threaded_forward_match_full(reduction):
+    """The sampled-row helpers used at full problem sizes agree with the full oracle."""
+    h, w, y = _rand(19, 70, 6, 40, ignore=(0, 13, 69))
+    loss, lse, dh, dw = flce_forward_backward(h, w, y, reduction=reduction)
+    l2, lse2 = flce_forward(h, w, y, reduction=reduction, block_rows=9, workers=4)
+    assert l2 == pytest.approx(loss, rel=1e-14)
+    _close(lse2, lse)
+    cols = [0, 5, 39, 17]
+    _close(flce_dw_rows(h, w, y, lse2, cols, reduction=reduction, block_rows=11), dw[cols])
