@@ -1,10 +1,484 @@
-// bf16 matrix-core engine (placeholder until the MFMA kernels land).
+// bf16 matrix-core engine for gfx950: the three contractions of the fused
+// linear cross-entropy on v_mfma_f32_32x32x16_bf16 with fp32 accumulation.
+//
+//   logits  Z^T[j, t] = sum_k W[j, k] H[t, k]    A = W   (k-major), B = H   (k-major)
+//   dH      dH[t, k]  = sum_j G[t, j] W[j, k]    A = G   (k-major), B = W   (n-major)
+//   dW      dW[j, k]  = sum_t G[t, j] H[t, k]    A = G^T (m-major), B = H   (n-major)
+//
+// One 256x256 output tile per 256-thread block (4 waves, 2x2, 128x128 per
+// wave = 4x4 MFMA tiles of 32x32).  K advances 64 at a time through two LDS
+// stages.  Operand tiles go from global memory straight into LDS with 16-byte
+// direct loads (no register staging); while the MFMAs consume one stage the
+// next stage is in flight.  Tiles whose k index is contiguous in memory sit in
+// LDS as [256 rows][64 k] and feed the fragments with 16-byte reads; tiles
+// whose k index is strided (the n-major W of dH, the m-major G^T and n-major H
+// of dW) sit in LDS as they are in memory, [64 k][256 mn], and are transposed
+// on the way into the fragments by the gfx950 LDS transpose read
+// (ds_read_b64_tr_b16).  Both layouts XOR-swizzle their 16-byte chunks so
+// that the fragment reads hit distinct LDS banks.  Loads that fall outside an
+// operand read a 16-byte block of zeros instead.
+//
+// The logits are computed transposed (vocabulary on the MFMA rows, tokens on
+// the lanes) so that each lane holds 64 vocabulary entries of the same token:
+// the per-token max and sum-exp over a 128-wide vocabulary group need one
+// cross-lane step.  The epilogue stores exp(z - group max) in bf16 into the
+// chunk's buffer; the full logits never leave registers.
+//
+// Consecutive workgroups are dispatched round-robin over the 8 XCDs; block
+// ids are remapped so that each XCD walks a contiguous range of tiles, and
+// tiles are ordered so that neighbours share an operand tile in that XCD's L2.
+#include "device_util.h"
 #include "flce_internal.h"
 
 namespace flce {
 
-hipError_t mfma_logits(const Plan&, const Work&, const ChunkArgs&, int, hipStream_t) { return hipErrorNotSupported; }
-hipError_t mfma_dh(const Plan&, const Work&, const ChunkArgs&, hipStream_t) { return hipErrorNotSupported; }
-hipError_t mfma_dw(const Plan&, const Work&, const ChunkArgs&, hipStream_t) { return hipErrorNotSupported; }
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+constexpr int TM = 256;       // tile rows (MFMA M)
+constexpr int TN = 256;       // tile cols (MFMA N)
+constexpr int TK = 64;        // k per LDS stage
+constexpr int kThreads = 256;
+constexpr int kStageElems = TM * TK;  // one operand, one stage: 32 KB
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+#define FLCE_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+// Source of every out-of-range 16-byte load.
+__device__ __attribute__((aligned(16))) unsigned int g_zero16[4] = {0u, 0u, 0u, 0u};
+
+struct Operand {
+  const bf16_t* ptr;
+  int64_t ld;        // elements between consecutive rows in memory
+  int64_t mn_bound;  // rows (k-major) / columns (mn-major) that exist
+  int64_t k_bound;   // k values that exist (absolute index)
+};
+
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+// Stage layouts in LDS (bf16 elements, one operand, one stage = 256 x 64):
+//  k-major : row R (= mn) of 64 k, 8 chunks of 8 k; position p of row R holds
+//            k-chunk p ^ ((R >> 1) & 7).
+//  mn-major: row k of 256 mn, 32 chunks of 8 mn; position p of row k holds
+//            mn-chunk p ^ (4 (k & 3)).
+// A stage is filled by 8 direct 16-byte loads per wave: load i of wave w
+// fills LDS bytes [1024 (8w + i), +1024), lane L landing at +16 L, i.e.
+//  k-major : rows R = 64 w + 8 i + L / 8, position L % 8;
+//  mn-major: rows k = 16 w + 2 i + L / 32, position L % 32.
+// The swizzle depends on i only through its parity, so a lane needs two
+// byte offsets (even / odd i) relative to a per-load uniform base.
+
+template <bool KMAJ>
+__device__ __forceinline__ void lane_load_offsets(int64_t ld, uint32_t (&off)[2]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int par = 0; par < 2; ++par) {
+    if (KMAJ) {
+      const int kc = (lane & 7) ^ ((4 * par + (lane >> 4)) & 7);
+      off[par] = static_cast<uint32_t>((lane >> 3) * ld * 2 + 16 * kc);
+    } else {
+      const int c = (lane & 31) ^ (4 * ((2 * par + (lane >> 5)) & 3));
+      off[par] = static_cast<uint32_t>((lane >> 5) * ld * 2 + 16 * c);
+    }
+  }
+}
+
+// Interior stage: every load in bounds; uniform base + lane offset.
+template <bool KMAJ>
+__device__ __forceinline__ void load_stage_fast(const Operand& op, int64_t mn0, int64_t k0, bf16_t* lds,
+                                                const uint32_t (&off)[2]) {
+  const int w = wave_id();
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int64_t row0 = KMAJ ? (mn0 + 64 * w + 8 * i) * op.ld + k0 : (k0 + 16 * w + 2 * i) * op.ld + mn0;
+    const char* base = reinterpret_cast<const char*>(op.ptr + row0);
+    __builtin_amdgcn_global_load_lds(base + off[i & 1], FLCE_LDS(lds + (w * 8 + i) * 512), 16, 0, 0);
+  }
+}
+
+// Edge stage: per-lane bounds; out-of-range lanes read 16 zero bytes.
+template <bool KMAJ>
+__device__ __forceinline__ void load_stage_edge(const Operand& op, int64_t mn0, int64_t k0, bf16_t* lds) {
+  const int lane = threadIdx.x & 63;
+  const int w = wave_id();
+  const unsigned int* zero = g_zero16;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int b = w * 8 + i;
+    const void* src;
+    if (KMAJ) {
+      const int R = b * 8 + (lane >> 3);
+      const int kc = (lane & 7) ^ ((R >> 1) & 7);
+      const int64_t mn = mn0 + R, k = k0 + kc * 8;
+      const bool ok = mn < op.mn_bound && k + 8 <= op.k_bound;
+      src = ok ? static_cast<const void*>(op.ptr + mn * op.ld + k) : static_cast<const void*>(zero);
+    } else {
+      const int kr = b * 2 + (lane >> 5);
+      const int c = (lane & 31) ^ (4 * (kr & 3));
+      const int64_t k = k0 + kr, mn = mn0 + c * 8;
+      const bool ok = k < op.k_bound && mn + 8 <= op.mn_bound;
+      src = ok ? static_cast<const void*>(op.ptr + k * op.ld + mn) : static_cast<const void*>(zero);
+    }
+    __builtin_amdgcn_global_load_lds(src, FLCE_LDS(lds + b * 512), 16, 0, 0);
+  }
+}
+
+template <bool KMAJ>
+__device__ __forceinline__ void load_stage(const Operand& op, int64_t mn0, int64_t k0, bf16_t* lds,
+                                           const uint32_t (&off)[2]) {
+  const bool interior = mn0 + TM <= op.mn_bound && k0 + TK <= op.k_bound;
+  if (interior)
+    load_stage_fast<KMAJ>(op, mn0, k0, lds, off);
+  else
+    load_stage_edge<KMAJ>(op, mn0, k0, lds);
+}
+
+// Per-lane LDS byte offsets of the fragment reads of a wave whose operand rows
+// start at wbase (multiple of 128).  Fragment (subtile i, k-step ks) holds
+// operand rows wbase + 32 i + (lane % 32) and k = 16 ks + 8 (lane / 32) + 0..7.
+//  k-major : offset = fo[ks] + 4096 i            (one 16-byte read)
+//  mn-major: offset = fo[i] + 8192 ks (+ 2048)   (two transpose reads: k + 0..3, k + 4..7)
+template <bool KMAJ>
+__device__ __forceinline__ void lane_frag_offsets(int wbase, uint32_t (&fo)[4]) {
+  const int lane = threadIdx.x & 63;
+  if (KMAJ) {
+    const int r = lane & 31, h = lane >> 5;
+    const int sw = (r >> 1) & 7;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) fo[ks] = static_cast<uint32_t>((wbase + r) * 128 + 16 * ((2 * ks + h) ^ sw));
+  } else {
+    // 16-lane groups: lane s of group g points at k = kb + s / 4, mn = nb + 4 (s % 4);
+    // the transpose read hands lane s the 4 consecutive k of column nb + s.
+    const int g = lane >> 4, s = lane & 15, q = s >> 2;
+    const int low = 2 * (g & 1) + ((s & 3) >> 1);
+    const int base = (8 * (g >> 1) + q) * 512 + 2 * wbase + 16 * low + 8 * (s & 1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fo[i] = static_cast<uint32_t>(base + 64 * (i ^ q));
+  }
+}
+
+template <bool KMAJ>
+__device__ __forceinline__ bf16x8 read_frag(const bf16_t* lds, const uint32_t (&fo)[4], int i, int ks) {
+  const char* b = reinterpret_cast<const char*>(lds);
+  if (KMAJ) {
+    return *reinterpret_cast<const bf16x8*>(b + fo[ks] + 4096 * i);
+  } else {
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4i16*)(b + fo[i] + 8192 * ks));
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4i16*)(b + fo[i] + 8192 * ks + 2048));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
+}
+
+// XCD-aware remap: hardware block b runs on XCD b % 8; give XCD x the
+// contiguous tile range [start(x), start(x) + count(x)).
+__device__ __forceinline__ int64_t xcd_remap(int64_t b, int64_t nb) {
+  const int64_t per = nb / 8, rem = nb % 8;
+  const int64_t x = b % 8, i = b / 8;
+  return x * per + (x < rem ? x : rem) + i;
+}
+
+struct Acc {
+  floatx16 c[4][4];
+};
+
+// Main loop: acc += A[m0 .. m0+255, k_lo .. k_hi) * B[n0 .. n0+255, k_lo .. k_hi)^T
+template <bool A_KMAJ, bool B_KMAJ>
+__device__ __forceinline__ void tile_loop(const Operand& A, const Operand& B, int64_t m0, int64_t n0, int64_t k_lo,
+                                          int64_t k_hi, Acc& acc) {
+  __shared__ __attribute__((aligned(16))) bf16_t lds[2][2][kStageElems];
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc.c[i][j][r] = 0.0f;
+
+  uint32_t offa[2], offb[2], foa[4], fob[4];
+  lane_load_offsets<A_KMAJ>(A.ld, offa);
+  lane_load_offsets<B_KMAJ>(B.ld, offb);
+  lane_frag_offsets<A_KMAJ>(wm * 128, foa);
+  lane_frag_offsets<B_KMAJ>(wn * 128, fob);
+
+  const int64_t nk = (k_hi - k_lo + TK - 1) / TK;  // 0 leaves acc at zero (the first stage loads zeros)
+  load_stage<A_KMAJ>(A, m0, k_lo, lds[0][0], offa);
+  load_stage<B_KMAJ>(B, n0, k_lo, lds[0][1], offb);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  for (int64_t it = 0; it < nk; ++it) {
+    const int cur = static_cast<int>(it & 1);
+    if (it + 1 < nk) {
+      load_stage<A_KMAJ>(A, m0, k_lo + (it + 1) * TK, lds[cur ^ 1][0], offa);
+      load_stage<B_KMAJ>(B, n0, k_lo + (it + 1) * TK, lds[cur ^ 1][1], offb);
+    }
+    const bf16_t* la = lds[cur][0];
+    const bf16_t* lb = lds[cur][1];
+#pragma unroll
+    for (int ks = 0; ks < TK / 16; ++ks) {
+      bf16x8 fa[4], fb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) fa[i] = read_frag<A_KMAJ>(la, foa, i, ks);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) fb[j] = read_frag<B_KMAJ>(lb, fob, j, ks);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc.c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc.c[i][j], 0, 0, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+}
+
+// Row (MFMA M index) of accumulator register r in MFMA tile (i, *) for this lane,
+// relative to the wave's 128-row range.
+__device__ __forceinline__ int acc_row(int i, int r, int lane) { return i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
+
+// ---- logits: tile rows = vocabulary, tile cols = chunk tokens -------------------------
+
+struct LogitsArgs {
+  Operand w, h;
+  int64_t v, vp, rows, C;
+  const int64_t* labels;
+  float* zy;
+  float* pm;
+  float* ps;
+  bf16_t* prob;  // nullptr: statistics only
+  int64_t tiles_m, tiles_n;
+};
+
+__global__ __launch_bounds__(kThreads) void mfma_logits_kernel(LogitsArgs a) {
+  const int64_t nb = a.tiles_m * a.tiles_n;
+  const int64_t t = xcd_remap(blockIdx.x, nb);
+  const int64_t tm = t / a.tiles_n, tn = t % a.tiles_n;  // tokens fastest: neighbours share the W tile
+  const int64_t m0 = tm * TM, n0 = tn * TN;
+  Acc acc;
+  tile_loop<true, true>(a.w, a.h, m0, n0, 0, a.w.k_bound, acc);
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int half = lane >> 5;
+  const int64_t vbase = m0 + wm * 128;  // this wave's 128-wide vocabulary group
+  const int64_t g = vbase / 128;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t tok = n0 + wn * 128 + j * 32 + (lane & 31);
+    const bool live = tok < a.rows;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (vbase + acc_row(i, r, lane) < a.v) mx = fmaxf(mx, acc.c[i][j][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float e[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int r = q * 4 + u;
+          e[u] = vbase + acc_row(i, r, lane) < a.v ? fast_exp(acc.c[i][j][r] - mx) : 0.0f;
+          s += e[u];
+        }
+        if (a.prob != nullptr && live) {
+          const int64_t col = vbase + i * 32 + 8 * q + 4 * half;
+          uint2 pk;
+          pk.x = pack_bf16x2(e[0], e[1]);
+          pk.y = pack_bf16x2(e[2], e[3]);
+          *reinterpret_cast<uint2*>(a.prob + tok * a.vp + col) = pk;
+        }
+      }
+    }
+    s += __shfl_xor(s, 32);
+    if (live && vbase < a.v) {
+      if (half == 0) {
+        a.pm[g * a.C + tok] = mx;
+        a.ps[g * a.C + tok] = s;
+      }
+      const int64_t q = a.labels[tok] - vbase;
+      const int o = static_cast<int>(q & 31);
+      if (q >= 0 && q < 128 && ((o >> 2) & 1) == half) {
+        const int it = static_cast<int>(q >> 5);
+        const int rt = (o >> 3) * 4 + (o & 3);
+        float z = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) z = (i == it && r == rt) ? acc.c[i][j][r] : z;
+        a.zy[tok] = z;
+      }
+    }
+  }
+}
+
+// ---- dH: tile rows = chunk tokens, tile cols = hidden; K = vocabulary (split) ----------
+
+struct DhArgs {
+  Operand g, w;
+  int64_t rows, d;
+  int64_t k_split;  // vocabulary columns per split (multiple of TK)
+  int64_t tiles_m, tiles_n, splits;
+  bf16_t* out_bf16;  // direct output (splits == 1, bf16)
+  float* out_f32;    // direct fp32 output (splits == 1, fp32) or split partials [splits][C][d]
+  int64_t part_stride;
+};
+
+__global__ __launch_bounds__(kThreads) void mfma_dh_kernel(DhArgs a) {
+  const int64_t nb = a.tiles_m * a.tiles_n * a.splits;
+  const int64_t t = xcd_remap(blockIdx.x, nb);
+  const int64_t tn = t % a.tiles_n;
+  const int64_t tm = (t / a.tiles_n) % a.tiles_m;
+  const int64_t sp = t / (a.tiles_n * a.tiles_m);
+  const int64_t m0 = tm * TM, n0 = tn * TN;
+  const int64_t k_lo = sp * a.k_split;
+  const int64_t k_hi = k_lo + a.k_split < a.g.k_bound ? k_lo + a.k_split : a.g.k_bound;
+  Acc acc;
+  tile_loop<true, false>(a.g, a.w, m0, n0, k_lo, k_hi, acc);
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t col = n0 + wn * 128 + j * 32 + (lane & 31);
+      if (col >= a.d) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = m0 + wm * 128 + acc_row(i, r, lane);
+        if (row >= a.rows) continue;
+        const float x = acc.c[i][j][r];
+        if (a.out_bf16 != nullptr)
+          a.out_bf16[row * a.d + col] = f32_to_bf16(x);
+        else
+          a.out_f32[sp * a.part_stride + row * a.d + col] = x;
+      }
+    }
+}
+
+// ---- dW: tile rows = vocabulary, tile cols = hidden; K = chunk tokens ----------------
+
+struct DwArgs {
+  Operand gt, h;
+  int64_t v, d;
+  int64_t tiles_m, tiles_n;
+  float* acc_buf;
+  bf16_t* out_bf16;
+  float* out_f32;
+  int mode;
+};
+
+__global__ __launch_bounds__(kThreads) void mfma_dw_kernel(DwArgs a) {
+  const int64_t nb = a.tiles_m * a.tiles_n;
+  const int64_t t = xcd_remap(blockIdx.x, nb);
+  const int64_t tm = t / a.tiles_n, tn = t % a.tiles_n;  // hidden fastest: neighbours share the G tile
+  const int64_t m0 = tm * TM, n0 = tn * TN;
+  Acc acc;
+  tile_loop<false, false>(a.gt, a.h, m0, n0, 0, a.gt.k_bound, acc);
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  // The mode is uniform: one fully unrolled store loop per mode.
+  auto for_each = [&](auto&& f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t col = n0 + wn * 128 + j * 32 + (lane & 31);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t row = m0 + wm * 128 + acc_row(i, r, lane);
+          if (col < a.d && row < a.v) f(row * a.d + col, acc.c[i][j][r]);
+        }
+      }
+  };
+  if (a.mode == DW_FIRST) {
+    for_each([&](int64_t o, float x) { a.acc_buf[o] = x; });
+  } else if (a.mode == DW_MID) {
+    for_each([&](int64_t o, float x) { a.acc_buf[o] += x; });
+  } else if (a.mode == DW_LAST) {
+    if (a.out_bf16 != nullptr)
+      for_each([&](int64_t o, float x) { a.out_bf16[o] = f32_to_bf16(a.acc_buf[o] + x); });
+    else
+      for_each([&](int64_t o, float x) { a.out_f32[o] = a.acc_buf[o] + x; });
+  } else {
+    if (a.out_bf16 != nullptr)
+      for_each([&](int64_t o, float x) { a.out_bf16[o] = f32_to_bf16(x); });
+    else
+      for_each([&](int64_t o, float x) { a.out_f32[o] = x; });
+  }
+}
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace
+
+hipError_t mfma_logits(const Plan& p, const Work& w, const ChunkArgs& c, int store_prob, hipStream_t s) {
+  LogitsArgs a;
+  a.w = Operand{static_cast<const bf16_t*>(c.w), p.d, p.v, p.d};
+  a.h = Operand{static_cast<const bf16_t*>(c.h), p.d, c.rows, p.d};
+  a.v = p.v;
+  a.vp = p.vp;
+  a.rows = c.rows;
+  a.C = p.chunk;
+  a.labels = c.labels;
+  a.zy = w.zy;
+  a.pm = w.pm;
+  a.ps = w.ps;
+  a.prob = store_prob ? static_cast<bf16_t*>(w.prob) : nullptr;
+  a.tiles_m = p.vp / TM;
+  a.tiles_n = cdiv(c.rows, TN);
+  mfma_logits_kernel<<<static_cast<unsigned>(a.tiles_m * a.tiles_n), kThreads, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t mfma_dh(const Plan& p, const Work& w, const ChunkArgs& c, hipStream_t s) {
+  DhArgs a;
+  a.g = Operand{static_cast<const bf16_t*>(w.prob), p.vp, c.rows, p.vp};
+  a.w = Operand{static_cast<const bf16_t*>(c.w), p.d, p.d, p.v};
+  a.rows = c.rows;
+  a.d = p.d;
+  a.splits = p.dh_splits;
+  a.k_split = cdiv(cdiv(p.vp, p.dh_splits), TK) * TK;
+  a.tiles_m = cdiv(c.rows, TM);
+  a.tiles_n = cdiv(p.d, TN);
+  a.part_stride = p.chunk * p.d;
+  a.out_bf16 = nullptr;
+  a.out_f32 = nullptr;
+  if (p.dh_splits > 1)
+    a.out_f32 = w.dhpart;
+  else if (p.dtype == FLCE_BF16)
+    a.out_bf16 = static_cast<bf16_t*>(c.dh);
+  else
+    a.out_f32 = static_cast<float*>(c.dh);
+  mfma_dh_kernel<<<static_cast<unsigned>(a.tiles_m * a.tiles_n * a.splits), kThreads, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t mfma_dw(const Plan& p, const Work& w, const ChunkArgs& c, hipStream_t s) {
+  DwArgs a;
+  a.gt = Operand{static_cast<const bf16_t*>(w.prob), p.vp, p.vp, c.rows};
+  a.h = Operand{static_cast<const bf16_t*>(c.h), p.d, p.d, c.rows};
+  a.v = p.v;
+  a.d = p.d;
+  a.tiles_m = p.vp / TM;
+  a.tiles_n = cdiv(p.d, TN);
+  a.acc_buf = w.dwacc;
+  a.out_bf16 = p.dtype == FLCE_BF16 ? static_cast<bf16_t*>(c.dw) : nullptr;
+  a.out_f32 = p.dtype == FLCE_BF16 ? nullptr : static_cast<float*>(c.dw);
+  a.mode = c.dw_mode;
+  mfma_dw_kernel<<<static_cast<unsigned>(a.tiles_m * a.tiles_n), kThreads, 0, s>>>(a);
+  return hipGetLastError();
+}
 
 }  // namespace flce

@@ -51,7 +51,7 @@ int make_plan(int64_t n, int64_t d, int64_t v, int32_t dtype, int32_t with_bwd, 
   q.v = v;
   q.dtype = dtype;
   q.with_bwd = with_bwd ? 1 : 0;
-  q.engine = ENGINE_FMA;
+  q.engine = dtype == FLCE_BF16 ? ENGINE_MFMA : ENGINE_FMA;
   q.group = q.engine == ENGINE_MFMA ? 128 : 64;
   const int64_t prob_elem = q.engine == ENGINE_MFMA ? 2 : 4;
   q.vp = (v + kVocabPad - 1) / kVocabPad * kVocabPad;
@@ -67,7 +67,18 @@ int make_plan(int64_t n, int64_t d, int64_t v, int32_t dtype, int32_t with_bwd, 
   if (c > n) c = n;
   q.chunk = c;
   q.nchunks = (n + c - 1) / c;
+  // dH = G.W has only ceil(C/256) x ceil(d/256) output tiles; split its
+  // vocabulary reduction until about 512 workgroups fill the 256 CUs, keeping
+  // at least 4096 vocabulary columns per split.
   q.dh_splits = 1;
+  if (q.engine == ENGINE_MFMA && with_bwd) {
+    const int64_t tiles = ((q.chunk + 255) / 256) * ((d + 255) / 256);
+    int64_t s = (512 + tiles - 1) / tiles;
+    const int64_t smax = q.vp / 4096;
+    if (s > smax) s = smax;
+    if (s > 8) s = 8;
+    q.dh_splits = s < 1 ? 1 : s;
+  }
   q.dw_acc = (with_bwd && dtype == FLCE_BF16 && q.nchunks > 1) ? 1 : 0;
   if (!mul_ok(q.chunk, q.vp) || !mul_ok(q.ngroups, q.chunk)) return FLCE_ERR_INVALID_ARG;
 

@@ -151,3 +151,18 @@ def test_dw_rows_sum_to_zero():
     wl, (h, w, y) = _case(300, 128, 1000, "f32", sigma_w=0.2, seed=22)
     _, _, _, dw = run_lib(h, w, y)
     assert np.max(np.abs(dw.sum(axis=0))) <= 1e-4 * np.max(np.abs(dw))
+
+
+def test_dh_split_vocab_bf16():
+    """Vocabulary large enough that dH = G.W splits its vocabulary reduction."""
+    wl, inp = _case(300, 256, 20000, "bf16", sigma_w=0.05, seed=23)
+    assert flce.flce_plan_info(300, 256, 20000, flce.FLCE_BF16, 1)["dh_splits"] > 1
+    _parity(wl, inp, "dh split")
+
+
+@pytest.mark.parametrize("shape", [(513, 520, 2100), (64, 8, 300), (1, 16, 5)])
+def test_mfma_tails_bf16(shape):
+    """Ragged token, hidden and vocabulary tails of the 256x256x64 tiles."""
+    n, d, v = shape
+    wl, inp = _case(n, d, v, "bf16", sigma_w=0.1, seed=24)
+    _parity(wl, inp, f"tails {shape}")
