@@ -39,7 +39,9 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 constexpr int TM = 256;       // tile rows (MFMA M)
 constexpr int TN = 256;       // tile cols (MFMA N)
-constexpr int TK = 64;        // k per LDS stage
+constexpr int TK = 64;        // k per LDS stage: 128-byte row segments, whole cache lines
+constexpr int kSlots = 5;     // LDS ring of operand-stage slots: 5 x 32 KB
+constexpr int KSTEPS = TK / 16;
 constexpr int kThreads = 256;
 constexpr int kStageElems = TM * TK;  // one operand, one stage: 32 KB
 
@@ -59,16 +61,17 @@ struct Operand {
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 // Stage layouts in LDS (bf16 elements, one operand, one stage = 256 x 64):
-//  k-major : row R (= mn) of 64 k, 8 chunks of 8 k; position p of row R holds
-//            k-chunk p ^ ((R >> 1) & 7).
-//  mn-major: row k of 256 mn, 32 chunks of 8 mn; position p of row k holds
+//  k-major : row R (= mn) of 64 k = 8 chunks of 8 k; position p of row R
+//            holds k-chunk p ^ ((R >> 1) & 7).
+//  mn-major: row k of 256 mn = 32 chunks of 8 mn; position p of row k holds
 //            mn-chunk p ^ (4 (k & 3)).
 // A stage is filled by 8 direct 16-byte loads per wave: load i of wave w
 // fills LDS bytes [1024 (8w + i), +1024), lane L landing at +16 L, i.e.
 //  k-major : rows R = 64 w + 8 i + L / 8, position L % 8;
 //  mn-major: rows k = 16 w + 2 i + L / 32, position L % 32.
-// The swizzle depends on i only through its parity, so a lane needs two
-// byte offsets (even / odd i) relative to a per-load uniform base.
+// The swizzle depends on i only through its parity, so a lane needs two byte
+// offsets (even / odd i) relative to a per-load uniform base.
+constexpr int kLoadsPerStage = 8;  // per wave and operand
 
 template <bool KMAJ>
 __device__ __forceinline__ void lane_load_offsets(int64_t ld, uint32_t (&off)[2]) {
@@ -91,10 +94,10 @@ __device__ __forceinline__ void load_stage_fast(const Operand& op, int64_t mn0, 
                                                 const uint32_t (&off)[2]) {
   const int w = wave_id();
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < kLoadsPerStage; ++i) {
     const int64_t row0 = KMAJ ? (mn0 + 64 * w + 8 * i) * op.ld + k0 : (k0 + 16 * w + 2 * i) * op.ld + mn0;
     const char* base = reinterpret_cast<const char*>(op.ptr + row0);
-    __builtin_amdgcn_global_load_lds(base + off[i & 1], FLCE_LDS(lds + (w * 8 + i) * 512), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(base + off[i & 1], FLCE_LDS(lds + (w * kLoadsPerStage + i) * 512), 16, 0, 0);
   }
 }
 
@@ -105,8 +108,8 @@ __device__ __forceinline__ void load_stage_edge(const Operand& op, int64_t mn0, 
   const int w = wave_id();
   const unsigned int* zero = g_zero16;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int b = w * 8 + i;
+  for (int i = 0; i < kLoadsPerStage; ++i) {
+    const int b = w * kLoadsPerStage + i;
     const void* src;
     if (KMAJ) {
       const int R = b * 8 + (lane >> 3);
@@ -185,11 +188,67 @@ struct Acc {
   floatx16 c[4][4];
 };
 
+struct Frags {
+  bf16x8 a[4], b[4];
+};
+
+// Wait until at most `n` operand-stages (8 direct loads each, per wave) are
+// still in flight: s_waitcnt vmcnt(8 n), lgkmcnt and expcnt left alone (gfx9
+// encoding: vmcnt bits [3:0] and [15:14]).
+__device__ __forceinline__ void wait_stages(int n) {
+  static_assert(kLoadsPerStage == 8, "vmcnt immediates assume 8 loads per operand-stage");
+  switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+    case 1: __builtin_amdgcn_s_waitcnt(0x0F78); break;
+    case 2: __builtin_amdgcn_s_waitcnt(0x4F70); break;
+    default: __builtin_amdgcn_s_waitcnt(0x4F78); break;
+  }
+}
+
+// Workgroup barrier without the memory fence of __syncthreads(): the direct
+// loads are waited for explicitly.  The empty asm statements keep the
+// compiler from moving memory accesses across it.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Instruction-class masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100;
+
+// Ask the scheduler to alternate the 16 MFMAs of a k-step with `reads` LDS reads.
+template <int reads>
+__device__ __forceinline__ void interleave_hint() {
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    if (k < reads) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+  }
+  if (reads > 16) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, reads - 16, 0);
+}
+
 // Main loop: acc += A[m0 .. m0+255, k_lo .. k_hi) * B[n0 .. n0+255, k_lo .. k_hi)^T
+//
+// LDS is a ring of 5 operand-stage slots of 32 KB (the whole 160 KB):
+// operand-stage q (A_s is q = 2s, B_s is q = 2s + 1) lives in slot q % 5.
+// While stage it is computed from two slots, B_{it+1}, A_{it+1} and A_{it+2}
+// are in flight or landed, so the A operand is fetched two stages ahead and
+// the B operand one.  Every iteration issues exactly one B and one A stage
+// (stages past the end load zeros and are never consumed), so the number of
+// loads in flight is the same every time and the waits are constants.
+// Iteration it computes stage it in four k-steps; the fragments of each
+// k-step are read from LDS while the MFMAs of the previous one run:
+//   k-steps 0..2: MFMAs | reads of the next k-step of stage it
+//   wait until only A_{it+2} may still be in flight; barrier  (all of stage
+//     it+1 has landed and every wave has read all of stage it)
+//   issue B_{it+2} and A_{it+3} into the two slots stage it used
+//   k-step 3: MFMAs | reads of k-step 0 of stage it+1
 template <bool A_KMAJ, bool B_KMAJ>
 __device__ __forceinline__ void tile_loop(const Operand& A, const Operand& B, int64_t m0, int64_t n0, int64_t k_lo,
                                           int64_t k_hi, Acc& acc) {
-  __shared__ __attribute__((aligned(16))) bf16_t lds[2][2][kStageElems];
+  __shared__ __attribute__((aligned(16))) bf16_t lds[kSlots][kStageElems];
+  constexpr int kReads = (A_KMAJ ? 4 : 8) + (B_KMAJ ? 4 : 8);  // LDS reads per k-step
   const int wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 #pragma unroll
@@ -205,36 +264,57 @@ __device__ __forceinline__ void tile_loop(const Operand& A, const Operand& B, in
   lane_frag_offsets<A_KMAJ>(wm * 128, foa);
   lane_frag_offsets<B_KMAJ>(wn * 128, fob);
 
-  const int64_t nk = (k_hi - k_lo + TK - 1) / TK;  // 0 leaves acc at zero (the first stage loads zeros)
-  load_stage<A_KMAJ>(A, m0, k_lo, lds[0][0], offa);
-  load_stage<B_KMAJ>(B, n0, k_lo, lds[0][1], offb);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  const int64_t nk = (k_hi - k_lo + TK - 1) / TK;
+  auto k_of = [&](int64_t st) { return st < nk ? k_lo + st * TK : k_hi; };  // past the end: zeros
+  auto issue_a = [&](int64_t st) { load_stage<A_KMAJ>(A, m0, k_of(st), lds[(2 * st) % kSlots], offa); };
+  auto issue_b = [&](int64_t st) { load_stage<B_KMAJ>(B, n0, k_of(st), lds[(2 * st + 1) % kSlots], offb); };
+  auto read = [&](int sa, int sb, int ks, Frags& f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f.a[i] = read_frag<A_KMAJ>(lds[sa], foa, i, ks);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) f.b[j] = read_frag<B_KMAJ>(lds[sb], fob, j, ks);
+  };
+  auto mma = [&](const Frags& f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc.c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc.c[i][j], 0, 0, 0);
+  };
+
+  // Prologue: A_0 B_0 A_1 B_1 A_2 in flight; wait for A_0 and B_0.
+  issue_a(0);
+  issue_b(0);
+  issue_a(1);
+  issue_b(1);
+  issue_a(2);
+  wait_stages(3);
+  stage_barrier();
+  Frags f0, f1;
+  int sa = 0, sb = 1;
+  read(sa, sb, 0, f0);
 
   for (int64_t it = 0; it < nk; ++it) {
-    const int cur = static_cast<int>(it & 1);
-    if (it + 1 < nk) {
-      load_stage<A_KMAJ>(A, m0, k_lo + (it + 1) * TK, lds[cur ^ 1][0], offa);
-      load_stage<B_KMAJ>(B, n0, k_lo + (it + 1) * TK, lds[cur ^ 1][1], offb);
-    }
-    const bf16_t* la = lds[cur][0];
-    const bf16_t* lb = lds[cur][1];
-#pragma unroll
-    for (int ks = 0; ks < TK / 16; ++ks) {
-      bf16x8 fa[4], fb[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) fa[i] = read_frag<A_KMAJ>(la, foa, i, ks);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) fb[j] = read_frag<B_KMAJ>(lb, fob, j, ks);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc.c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc.c[i][j], 0, 0, 0);
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    read(sa, sb, 1, f1);
+    mma(f0);
+    interleave_hint<kReads>();
+    read(sa, sb, 2, f0);
+    mma(f1);
+    interleave_hint<kReads>();
+    read(sa, sb, 3, f1);
+    mma(f0);
+    interleave_hint<kReads>();
+    wait_stages(1);
+    stage_barrier();
+    issue_b(it + 2);
+    issue_a(it + 3);
+    sa = sa + 2 >= kSlots ? sa + 2 - kSlots : sa + 2;
+    sb = sb + 2 >= kSlots ? sb + 2 - kSlots : sb + 2;
+    read(sa, sb, 0, f0);
+    mma(f1);
+    interleave_hint<kReads>();
   }
+  wait_stages(0);  // no direct load may still target this workgroup's LDS when it exits
 }
 
 // Row (MFMA M index) of accumulator register r in MFMA tile (i, *) for this lane,

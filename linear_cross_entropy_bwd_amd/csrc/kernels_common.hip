@@ -106,25 +106,63 @@ __global__ __launch_bounds__(kMergeRows* kMergeSlices) void lse_merge_kernel(
 }
 
 // G = P * factor(group, row), the target column takes the precomputed value;
-// columns in [v, vp) stay 0.  8 consecutive columns per thread.
+// columns in [v, vp) stay 0.  Each thread rewrites 8 consecutive columns
+// (one 16-byte vector for bf16, two for fp32); a group holds whole vectors.
+template <typename TP>
+__device__ __forceinline__ void grad_vec8(TP* p, float f, int64_t c0, int64_t v, int64_t y, float gt);
+
+template <>
+__device__ __forceinline__ void grad_vec8<bf16_t>(bf16_t* p, float f, int64_t c0, int64_t v, int64_t y, float gt) {
+  uint4 x = *reinterpret_cast<const uint4*>(p);
+  uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int64_t c = c0 + 2 * k;
+    float lo = bf16_to_f32(static_cast<bf16_t>(w[k] & 0xffffu)) * f;
+    float hi = bf16_to_f32(static_cast<bf16_t>(w[k] >> 16)) * f;
+    if (c == y) lo = gt;
+    if (c + 1 == y) hi = gt;
+    if (c >= v) lo = 0.0f;
+    if (c + 1 >= v) hi = 0.0f;
+    w[k] = pack_bf16x2(lo, hi);
+  }
+  *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+template <>
+__device__ __forceinline__ void grad_vec8<float>(float* p, float f, int64_t c0, int64_t v, int64_t y, float gt) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    float4 x = *reinterpret_cast<const float4*>(p + 4 * h);
+    float e[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int64_t c = c0 + 4 * h + k;
+      float g = e[k] * f;
+      if (c == y) g = gt;
+      if (c >= v) g = 0.0f;
+      e[k] = g;
+    }
+    *reinterpret_cast<float4*>(p + 4 * h) = make_float4(e[0], e[1], e[2], e[3]);
+  }
+}
+
+constexpr int kGradVecs = 4;  // 8-column vectors per thread
+
 template <typename TP>
 __global__ __launch_bounds__(256) void grad_kernel(TP* __restrict__ prob, int64_t vp, int64_t v, int64_t group,
                                                    const float* __restrict__ factor, int64_t C,
                                                    const float* __restrict__ gy, const int64_t* __restrict__ labels) {
   const int64_t t = blockIdx.x;
-  const int64_t c0 = (static_cast<int64_t>(blockIdx.y) * 256 + threadIdx.x) * 8;
-  if (c0 >= vp) return;
-  const float f = c0 < v ? factor[(c0 / group) * C + t] : 0.0f;
   const int64_t y = labels[t];
   const float gt = gy[t];
   TP* row = prob + t * vp;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const int64_t c = c0 + k;
-    float g = Elem<TP>::ld(row, c) * f;
-    if (c == y) g = gt;
-    if (c >= v) g = 0.0f;
-    Elem<TP>::st(row, c, g);
+  for (int q = 0; q < kGradVecs; ++q) {
+    const int64_t c0 = ((static_cast<int64_t>(blockIdx.y) * kGradVecs + q) * 256 + threadIdx.x) * 8;
+    if (c0 >= vp) return;
+    const float f = c0 < v ? factor[(c0 / group) * C + t] : 0.0f;
+    grad_vec8<TP>(row + c0, f, c0, v, y, gt);
   }
 }
 
@@ -176,7 +214,7 @@ hipError_t launch_lse_merge(const Plan& p, const Work& w, const ChunkArgs& a, in
 }
 
 hipError_t launch_grad(const Plan& p, const Work& w, const ChunkArgs& a, hipStream_t s) {
-  dim3 grid(static_cast<unsigned>(a.rows), static_cast<unsigned>((p.vp / 8 + 255) / 256));
+  dim3 grid(static_cast<unsigned>(a.rows), static_cast<unsigned>((p.vp / 8 + 256 * kGradVecs - 1) / (256 * kGradVecs)));
   if (p.engine == ENGINE_MFMA)
     grad_kernel<bf16_t><<<grid, 256, 0, s>>>(static_cast<bf16_t*>(w.prob), p.vp, p.v, p.group, w.pm, p.chunk, w.gy,
                                              a.labels);
