@@ -6,10 +6,11 @@
 //   dW      dW[j, k]  = sum_t G[t, j] H[t, k]    A = G^T (m-major), B = H   (n-major)
 //
 // One 256x256 output tile per 256-thread block (4 waves, 2x2, 128x128 per
-// wave = 4x4 MFMA tiles of 32x32).  K advances 64 at a time through two LDS
-// stages.  Operand tiles go from global memory straight into LDS with 16-byte
-// direct loads (no register staging); while the MFMAs consume one stage the
-// next stage is in flight.  Tiles whose k index is contiguous in memory sit in
+// wave = 4x4 MFMA tiles of 32x32).  K advances 64 at a time.  Operand tiles
+// go from global memory straight into LDS with 16-byte direct loads (no
+// register staging) through a ring of five 32 KB operand-stage slots, so the
+// A operand is fetched two stages and the B operand one stage ahead of the
+// MFMAs (see tile_loop).  Tiles whose k index is contiguous in memory sit in
 // LDS as [256 rows][64 k] and feed the fragments with 16-byte reads; tiles
 // whose k index is strided (the n-major W of dH, the m-major G^T and n-major H
 // of dW) sit in LDS as they are in memory, [64 k][256 mn], and are transposed
@@ -347,38 +348,34 @@ __global__ __launch_bounds__(kThreads) void mfma_logits_kernel(LogitsArgs a) {
   const int half = lane >> 5;
   const int64_t vbase = m0 + wm * 128;  // this wave's 128-wide vocabulary group
   const int64_t g = vbase / 128;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int64_t tok = n0 + wn * 128 + j * 32 + (lane & 31);
+  static_for<4>([&](auto J) {
+    const int64_t tok = n0 + wn * 128 + J * 32 + (lane & 31);
     const bool live = tok < a.rows;
     float mx = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (vbase + acc_row(i, r, lane) < a.v) mx = fmaxf(mx, acc.c[i][j][r]);
+    static_for<4>([&](auto I) {
+      static_for<16>([&](auto R) {
+        if (vbase + acc_row(I, R, lane) < a.v) mx = fmaxf(mx, acc.c[I][J][R.value]);
+      });
+    });
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     float s = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
+    static_for<4>([&](auto I) {
+      static_for<4>([&](auto Q) {
         float e[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int r = q * 4 + u;
-          e[u] = vbase + acc_row(i, r, lane) < a.v ? fast_exp(acc.c[i][j][r] - mx) : 0.0f;
-          s += e[u];
-        }
+        static_for<4>([&](auto U) {
+          constexpr int r = Q * 4 + U;
+          e[U] = vbase + acc_row(I, r, lane) < a.v ? fast_exp(acc.c[I][J][r] - mx) : 0.0f;
+          s += e[U];
+        });
         if (a.prob != nullptr && live) {
-          const int64_t col = vbase + i * 32 + 8 * q + 4 * half;
+          const int64_t col = vbase + I * 32 + 8 * Q + 4 * half;
           uint2 pk;
           pk.x = pack_bf16x2(e[0], e[1]);
           pk.y = pack_bf16x2(e[2], e[3]);
           *reinterpret_cast<uint2*>(a.prob + tok * a.vp + col) = pk;
         }
-      }
-    }
+      });
+    });
     s += __shfl_xor(s, 32);
     if (live && vbase < a.v) {
       if (half == 0) {
@@ -391,14 +388,13 @@ __global__ __launch_bounds__(kThreads) void mfma_logits_kernel(LogitsArgs a) {
         const int it = static_cast<int>(q >> 5);
         const int rt = (o >> 3) * 4 + (o & 3);
         float z = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) z = (i == it && r == rt) ? acc.c[i][j][r] : z;
+        static_for<4>([&](auto I) {
+          static_for<16>([&](auto R) { z = (I == it && R == rt) ? acc.c[I][J][R.value] : z; });
+        });
         a.zy[tok] = z;
       }
     }
-  }
+  });
 }
 
 // ---- dH: tile rows = chunk tokens, tile cols = hidden; K = vocabulary (split) ----------
@@ -427,23 +423,21 @@ __global__ __launch_bounds__(kThreads) void mfma_dh_kernel(DhArgs a) {
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t col = n0 + wn * 128 + j * 32 + (lane & 31);
-      if (col >= a.d) continue;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t row = m0 + wm * 128 + acc_row(i, r, lane);
-        if (row >= a.rows) continue;
-        const float x = acc.c[i][j][r];
-        if (a.out_bf16 != nullptr)
-          a.out_bf16[row * a.d + col] = f32_to_bf16(x);
-        else
-          a.out_f32[sp * a.part_stride + row * a.d + col] = x;
-      }
-    }
+  static_for<4>([&](auto I) {
+    static_for<4>([&](auto J) {
+      const int64_t col = n0 + wn * 128 + J * 32 + (lane & 31);
+      static_for<16>([&](auto R) {
+        const int64_t row = m0 + wm * 128 + acc_row(I, R, lane);
+        if (col < a.d && row < a.rows) {
+          const float x = acc.c[I][J][R.value];
+          if (a.out_bf16 != nullptr)
+            a.out_bf16[row * a.d + col] = f32_to_bf16(x);
+          else
+            a.out_f32[sp * a.part_stride + row * a.d + col] = x;
+        }
+      });
+    });
+  });
 }
 
 // ---- dW: tile rows = vocabulary, tile cols = hidden; K = chunk tokens ----------------
@@ -468,35 +462,36 @@ __global__ __launch_bounds__(kThreads) void mfma_dw_kernel(DwArgs a) {
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  // The mode is uniform: one fully unrolled store loop per mode.
-  auto for_each = [&](auto&& f) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t col = n0 + wn * 128 + j * 32 + (lane & 31);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t row = m0 + wm * 128 + acc_row(i, r, lane);
-          if (col < a.d && row < a.v) f(row * a.d + col, acc.c[i][j][r]);
+  // The mode is uniform.  Per 32x32 subtile, a lane owns 16 rows of one
+  // column; all 16 accumulator loads are issued before any store so their
+  // latencies overlap.
+  const float* __restrict__ src = a.acc_buf;
+  float* __restrict__ dst_acc = a.acc_buf;
+  const bool read_acc = a.mode == DW_MID || a.mode == DW_LAST;
+  static_for<4>([&](auto I) {
+    static_for<4>([&](auto J) {
+      const int64_t col = n0 + wn * 128 + J * 32 + (lane & 31);
+      const bool col_ok = col < a.d;
+      float prev[16];
+      static_for<16>([&](auto R) {
+        const int64_t row = m0 + wm * 128 + acc_row(I, R, lane);
+        prev[R] = (read_acc && col_ok && row < a.v) ? src[row * a.d + col] : 0.0f;
+      });
+      static_for<16>([&](auto R) {
+        const int64_t row = m0 + wm * 128 + acc_row(I, R, lane);
+        if (col_ok && row < a.v) {
+          const int64_t o = row * a.d + col;
+          const float x = acc.c[I][J][R.value] + prev[R];
+          if (a.mode == DW_FIRST || a.mode == DW_MID)
+            dst_acc[o] = x;
+          else if (a.out_bf16 != nullptr)
+            a.out_bf16[o] = f32_to_bf16(x);
+          else
+            a.out_f32[o] = x;
         }
-      }
-  };
-  if (a.mode == DW_FIRST) {
-    for_each([&](int64_t o, float x) { a.acc_buf[o] = x; });
-  } else if (a.mode == DW_MID) {
-    for_each([&](int64_t o, float x) { a.acc_buf[o] += x; });
-  } else if (a.mode == DW_LAST) {
-    if (a.out_bf16 != nullptr)
-      for_each([&](int64_t o, float x) { a.out_bf16[o] = f32_to_bf16(a.acc_buf[o] + x); });
-    else
-      for_each([&](int64_t o, float x) { a.out_f32[o] = a.acc_buf[o] + x; });
-  } else {
-    if (a.out_bf16 != nullptr)
-      for_each([&](int64_t o, float x) { a.out_bf16[o] = f32_to_bf16(x); });
-    else
-      for_each([&](int64_t o, float x) { a.out_f32[o] = x; });
-  }
+      });
+    });
+  });
 }
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
