@@ -12,18 +12,18 @@ typedef uint16_t bf16_t;  // raw bfloat16 bits
 
 __device__ __forceinline__ float bf16_to_f32(bf16_t x) { return __uint_as_float(static_cast<uint32_t>(x) << 16); }
 
-// fp32 -> bf16, round to nearest even; NaN stays NaN (quietened).
-__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<bf16_t>(u >> 16);
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float floatx2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> packed pair of bf16 (lo in bits 0..15), round to nearest even:
+// one v_cvt_pk_bf16_f32 on gfx950.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const floatx2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
-// Two fp32 -> packed pair of bf16 (lo in bits 0..15).
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
-}
+// fp32 -> bf16, round to nearest even.
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) { return static_cast<bf16_t>(pack_bf16x2(f, 0.0f) & 0xffffu); }
 
 template <typename T>
 struct Elem;

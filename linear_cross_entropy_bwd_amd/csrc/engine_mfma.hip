@@ -185,6 +185,20 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t b, int64_t nb) {
   return x * per + (x < rem ? x : rem) + i;
 }
 
+// Tile coordinates of linear tile t in a tiles_m x tiles_n grid, walked in
+// groups of group_m tile rows: inside a group the row index runs fastest, so
+// a run of consecutive tiles covers a group_m x k block of the output and its
+// operand tiles (group_m A tiles, k B tiles) are shared in L2.
+__device__ __forceinline__ void tile_coords(int64_t t, int64_t tiles_m, int64_t tiles_n, int64_t group_m,
+                                            int64_t& tm, int64_t& tn) {
+  const int64_t per_group = group_m * tiles_n;
+  const int64_t grp = t / per_group, in = t % per_group;
+  const int64_t first = grp * group_m;
+  const int64_t gm = tiles_m - first < group_m ? tiles_m - first : group_m;
+  tm = first + in % gm;
+  tn = in / gm;
+}
+
 struct Acc {
   floatx16 c[4][4];
 };
@@ -332,13 +346,14 @@ struct LogitsArgs {
   float* pm;
   float* ps;
   bf16_t* prob;  // nullptr: statistics only
-  int64_t tiles_m, tiles_n;
+  int64_t tiles_m, tiles_n, group_m;
 };
 
 __global__ __launch_bounds__(kThreads) void mfma_logits_kernel(LogitsArgs a) {
   const int64_t nb = a.tiles_m * a.tiles_n;
   const int64_t t = xcd_remap(blockIdx.x, nb);
-  const int64_t tm = t / a.tiles_n, tn = t % a.tiles_n;  // tokens fastest: neighbours share the W tile
+  int64_t tm, tn;
+  tile_coords(t, a.tiles_m, a.tiles_n, a.group_m, tm, tn);
   const int64_t m0 = tm * TM, n0 = tn * TN;
   Acc acc;
   tile_loop<true, true>(a.w, a.h, m0, n0, 0, a.w.k_bound, acc);
@@ -348,53 +363,62 @@ __global__ __launch_bounds__(kThreads) void mfma_logits_kernel(LogitsArgs a) {
   const int half = lane >> 5;
   const int64_t vbase = m0 + wm * 128;  // this wave's 128-wide vocabulary group
   const int64_t g = vbase / 128;
-  static_for<4>([&](auto J) {
-    const int64_t tok = n0 + wn * 128 + J * 32 + (lane & 31);
-    const bool live = tok < a.rows;
-    float mx = -INFINITY;
-    static_for<4>([&](auto I) {
-      static_for<16>([&](auto R) {
-        if (vbase + acc_row(I, R, lane) < a.v) mx = fmaxf(mx, acc.c[I][J][R.value]);
-      });
-    });
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    float s = 0.0f;
-    static_for<4>([&](auto I) {
-      static_for<4>([&](auto Q) {
-        float e[4];
-        static_for<4>([&](auto U) {
-          constexpr int r = Q * 4 + U;
-          e[U] = vbase + acc_row(I, r, lane) < a.v ? fast_exp(acc.c[I][J][r] - mx) : 0.0f;
-          s += e[U];
+  // FULL: every vocabulary row of the group exists (no per-element masks).
+  auto epilogue = [&](auto FULL) {
+    auto in_vocab = [&](int r_row) { return FULL || vbase + r_row < a.v; };
+    static_for<4>([&](auto J) {
+      const int64_t tok = n0 + wn * 128 + J * 32 + (lane & 31);
+      const bool live = tok < a.rows;
+      float mx = -INFINITY;
+      static_for<4>([&](auto I) {
+        static_for<16>([&](auto R) {
+          if (in_vocab(acc_row(I, R, lane))) mx = fmaxf(mx, acc.c[I][J][R.value]);
         });
-        if (a.prob != nullptr && live) {
-          const int64_t col = vbase + I * 32 + 8 * Q + 4 * half;
-          uint2 pk;
-          pk.x = pack_bf16x2(e[0], e[1]);
-          pk.y = pack_bf16x2(e[2], e[3]);
-          *reinterpret_cast<uint2*>(a.prob + tok * a.vp + col) = pk;
+      });
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mxl = mx * kLog2e;
+      float s = 0.0f;
+      static_for<4>([&](auto I) {
+        static_for<4>([&](auto Q) {
+          float e[4];
+          static_for<4>([&](auto U) {
+            constexpr int r = Q * 4 + U;
+            e[U] = in_vocab(acc_row(I, r, lane)) ? __builtin_amdgcn_exp2f(fmaf(acc.c[I][J][r], kLog2e, -mxl)) : 0.0f;
+            s += e[U];
+          });
+          if (a.prob != nullptr && live) {
+            const int64_t col = vbase + I * 32 + 8 * Q + 4 * half;
+            uint2 pk;
+            pk.x = pack_bf16x2(e[0], e[1]);
+            pk.y = pack_bf16x2(e[2], e[3]);
+            *reinterpret_cast<uint2*>(a.prob + tok * a.vp + col) = pk;
+          }
+        });
+      });
+      s += __shfl_xor(s, 32);
+      if (live && vbase < a.v) {
+        if (half == 0) {
+          a.pm[g * a.C + tok] = mx;
+          a.ps[g * a.C + tok] = s;
         }
-      });
+        const int64_t q = a.labels[tok] - vbase;
+        const int o = static_cast<int>(q & 31);
+        if (q >= 0 && q < 128 && ((o >> 2) & 1) == half) {
+          const int it = static_cast<int>(q >> 5);
+          const int rt = (o >> 3) * 4 + (o & 3);
+          float z = 0.0f;
+          static_for<4>([&](auto I) {
+            static_for<16>([&](auto R) { z = (I == it && R == rt) ? acc.c[I][J][R.value] : z; });
+          });
+          a.zy[tok] = z;
+        }
+      }
     });
-    s += __shfl_xor(s, 32);
-    if (live && vbase < a.v) {
-      if (half == 0) {
-        a.pm[g * a.C + tok] = mx;
-        a.ps[g * a.C + tok] = s;
-      }
-      const int64_t q = a.labels[tok] - vbase;
-      const int o = static_cast<int>(q & 31);
-      if (q >= 0 && q < 128 && ((o >> 2) & 1) == half) {
-        const int it = static_cast<int>(q >> 5);
-        const int rt = (o >> 3) * 4 + (o & 3);
-        float z = 0.0f;
-        static_for<4>([&](auto I) {
-          static_for<16>([&](auto R) { z = (I == it && R == rt) ? acc.c[I][J][R.value] : z; });
-        });
-        a.zy[tok] = z;
-      }
-    }
-  });
+  };
+  if (vbase + 128 <= a.v)
+    epilogue(std::true_type{});
+  else
+    epilogue(std::false_type{});
 }
 
 // ---- dH: tile rows = chunk tokens, tile cols = hidden; K = vocabulary (split) ----------
@@ -403,7 +427,7 @@ struct DhArgs {
   Operand g, w;
   int64_t rows, d;
   int64_t k_split;  // vocabulary columns per split (multiple of TK)
-  int64_t tiles_m, tiles_n, splits;
+  int64_t tiles_m, tiles_n, splits, group_m;
   bf16_t* out_bf16;  // direct output (splits == 1, bf16)
   float* out_f32;    // direct fp32 output (splits == 1, fp32) or split partials [splits][C][d]
   int64_t part_stride;
@@ -412,9 +436,10 @@ struct DhArgs {
 __global__ __launch_bounds__(kThreads) void mfma_dh_kernel(DhArgs a) {
   const int64_t nb = a.tiles_m * a.tiles_n * a.splits;
   const int64_t t = xcd_remap(blockIdx.x, nb);
-  const int64_t tn = t % a.tiles_n;
-  const int64_t tm = (t / a.tiles_n) % a.tiles_m;
-  const int64_t sp = t / (a.tiles_n * a.tiles_m);
+  const int64_t per_split = a.tiles_n * a.tiles_m;
+  const int64_t sp = t / per_split;
+  int64_t tm, tn;
+  tile_coords(t % per_split, a.tiles_m, a.tiles_n, a.group_m, tm, tn);
   const int64_t m0 = tm * TM, n0 = tn * TN;
   const int64_t k_lo = sp * a.k_split;
   const int64_t k_hi = k_lo + a.k_split < a.g.k_bound ? k_lo + a.k_split : a.g.k_bound;
@@ -445,7 +470,7 @@ __global__ __launch_bounds__(kThreads) void mfma_dh_kernel(DhArgs a) {
 struct DwArgs {
   Operand gt, h;
   int64_t v, d;
-  int64_t tiles_m, tiles_n;
+  int64_t tiles_m, tiles_n, group_m;
   float* acc_buf;
   bf16_t* out_bf16;
   float* out_f32;
@@ -455,7 +480,8 @@ struct DwArgs {
 __global__ __launch_bounds__(kThreads) void mfma_dw_kernel(DwArgs a) {
   const int64_t nb = a.tiles_m * a.tiles_n;
   const int64_t t = xcd_remap(blockIdx.x, nb);
-  const int64_t tm = t / a.tiles_n, tn = t % a.tiles_n;  // hidden fastest: neighbours share the G tile
+  int64_t tm, tn;
+  tile_coords(t, a.tiles_m, a.tiles_n, a.group_m, tm, tn);
   const int64_t m0 = tm * TM, n0 = tn * TN;
   Acc acc;
   tile_loop<false, false>(a.gt, a.h, m0, n0, 0, a.gt.k_bound, acc);
@@ -513,6 +539,7 @@ hipError_t mfma_logits(const Plan& p, const Work& w, const ChunkArgs& c, int sto
   a.prob = store_prob ? static_cast<bf16_t*>(w.prob) : nullptr;
   a.tiles_m = p.vp / TM;
   a.tiles_n = cdiv(c.rows, TN);
+  a.group_m = p.group_m[0];
   mfma_logits_kernel<<<static_cast<unsigned>(a.tiles_m * a.tiles_n), kThreads, 0, s>>>(a);
   return hipGetLastError();
 }
@@ -527,6 +554,7 @@ hipError_t mfma_dh(const Plan& p, const Work& w, const ChunkArgs& c, hipStream_t
   a.k_split = cdiv(cdiv(p.vp, p.dh_splits), TK) * TK;
   a.tiles_m = cdiv(c.rows, TM);
   a.tiles_n = cdiv(p.d, TN);
+  a.group_m = p.group_m[1];
   a.part_stride = p.chunk * p.d;
   a.out_bf16 = nullptr;
   a.out_f32 = nullptr;
@@ -548,6 +576,7 @@ hipError_t mfma_dw(const Plan& p, const Work& w, const ChunkArgs& c, hipStream_t
   a.d = p.d;
   a.tiles_m = p.vp / TM;
   a.tiles_n = cdiv(p.d, TN);
+  a.group_m = p.group_m[2];
   a.acc_buf = w.dwacc;
   a.out_bf16 = p.dtype == FLCE_BF16 ? static_cast<bf16_t*>(c.dw) : nullptr;
   a.out_f32 = p.dtype == FLCE_BF16 ? nullptr : static_cast<float*>(c.dw);

@@ -33,6 +33,7 @@ struct Plan {
   int64_t ngroups;
   int64_t dh_splits;   // split of the K = vocabulary reduction of dH
   int32_t dw_acc;      // dW accumulates across chunks in an fp32 workspace buffer
+  int64_t group_m[3];  // tile-row group of the logits, dH and dW tile orders
   // byte offsets inside the single workspace allocation
   size_t off_nvalid, off_zy, off_gy, off_lse, off_loss, off_pm, off_ps, off_prob, off_dwacc, off_dhpart;
   size_t total;

@@ -45,8 +45,8 @@ __device__ __forceinline__ float row_scale(int32_t nvalid, int32_t reduction) {
 // row's NLL lse - z_y.  With the gradient, each partial max is replaced by
 // the factor scale_i * exp(m_g - lse) that turns the stored exp(z - m_g) into
 // the scaled softmax, and the value the target column takes is precomputed.
-constexpr int kMergeRows = 32;
-constexpr int kMergeSlices = 8;
+constexpr int kMergeRows = 16;
+constexpr int kMergeSlices = 16;
 
 __global__ __launch_bounds__(kMergeRows* kMergeSlices) void lse_merge_kernel(
     float* __restrict__ pm, const float* __restrict__ ps, int64_t C, int64_t G, int64_t rows,
