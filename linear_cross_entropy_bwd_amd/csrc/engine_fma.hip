@@ -154,16 +154,15 @@ __global__ __launch_bounds__(256) void fma_dh_kernel(const float* __restrict__ G
   }
 }
 
-// dW contribution of one chunk: partial[j, :] = sum_t G[t, j] H[t, :], merged
-// into the fp32 accumulator / output according to the chunk's mode.
-template <typename T>
-__global__ __launch_bounds__(256) void fma_dw_kernel(const float* __restrict__ G, int64_t vp, const T* __restrict__ H,
-                                                     int64_t rows, int64_t d, int64_t v, float* __restrict__ acc_buf,
-                                                     T* __restrict__ out, int mode) {
+// dW contribution of one chunk: partial[j, :] = sum_t G[t, j] H[t, :];
+// DW_SINGLE writes it, DW_MID adds it to dW.
+__global__ __launch_bounds__(256) void fma_dw_kernel(const float* __restrict__ G, int64_t vp, const float* __restrict__ H,
+                                                     int64_t rows, int64_t d, int64_t v, float* __restrict__ out,
+                                                     int mode) {
   const int64_t m0 = static_cast<int64_t>(blockIdx.x) * BM;
   const int64_t n0 = static_cast<int64_t>(blockIdx.y) * BN;
   float acc[4][4];
-  TileLoop<float, T, false, false>::run(G, vp, H, d, v, d, rows, m0, n0, acc);
+  TileLoop<float, float, false, false>::run(G, vp, H, d, v, d, rows, m0, n0, acc);
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -174,13 +173,7 @@ __global__ __launch_bounds__(256) void fma_dw_kernel(const float* __restrict__ G
       const int64_t n = n0 + tx * 4 + q;
       if (n >= d) continue;
       const int64_t o = j * d + n;
-      const float x = acc[i][q];
-      switch (mode) {
-        case DW_SINGLE: Elem<T>::st(out, o, x); break;
-        case DW_FIRST: acc_buf[o] = x; break;
-        case DW_MID: acc_buf[o] += x; break;
-        default: Elem<T>::st(out, o, acc_buf[o] + x); break;
-      }
+      out[o] = mode == DW_SINGLE ? acc[i][q] : out[o] + acc[i][q];
     }
   }
 }
@@ -192,42 +185,29 @@ inline dim3 grid2(int64_t m, int64_t n) {
 }  // namespace
 
 hipError_t fma_logits(const Plan& p, const Work& w, const ChunkArgs& a, int store_prob, hipStream_t s) {
+  if (p.dtype != FLCE_F32) return hipErrorInvalidValue;
   float* prob = store_prob ? static_cast<float*>(w.prob) : nullptr;
-  const dim3 grid = grid2(a.rows, p.v);
-  if (p.dtype == FLCE_F32)
-    fma_logits_kernel<float><<<grid, 256, 0, s>>>(static_cast<const float*>(a.h), static_cast<const float*>(a.w),
-                                                  a.rows, p.d, p.v, p.vp, a.labels, w.zy, w.pm, w.ps, p.chunk, prob);
-  else
-    fma_logits_kernel<bf16_t><<<grid, 256, 0, s>>>(static_cast<const bf16_t*>(a.h), static_cast<const bf16_t*>(a.w),
-                                                   a.rows, p.d, p.v, p.vp, a.labels, w.zy, w.pm, w.ps, p.chunk, prob);
+  fma_logits_kernel<float><<<grid2(a.rows, p.v), 256, 0, s>>>(static_cast<const float*>(a.h),
+                                                             static_cast<const float*>(a.w), a.rows, p.d, p.v, p.vp,
+                                                             a.labels, w.zy, w.pm, w.ps, p.chunk, prob);
   return hipGetLastError();
 }
 
 hipError_t fma_dh(const Plan& p, const Work& w, const ChunkArgs& a, hipStream_t s) {
-  const dim3 grid = grid2(a.rows, p.d);
-  const float* G = static_cast<const float*>(w.prob);
-  if (p.dtype == FLCE_F32)
-    fma_dh_kernel<float><<<grid, 256, 0, s>>>(G, p.vp, static_cast<const float*>(a.w), a.rows, p.d, p.v,
-                                              static_cast<float*>(a.dh));
-  else
-    fma_dh_kernel<bf16_t><<<grid, 256, 0, s>>>(G, p.vp, static_cast<const bf16_t*>(a.w), a.rows, p.d, p.v,
-                                               static_cast<bf16_t*>(a.dh));
+  if (p.dtype != FLCE_F32) return hipErrorInvalidValue;
+  fma_dh_kernel<float><<<grid2(a.rows, p.d), 256, 0, s>>>(static_cast<const float*>(w.prob), p.vp,
+                                                         static_cast<const float*>(a.w), a.rows, p.d, p.v,
+                                                         static_cast<float*>(a.dh));
   return hipGetLastError();
 }
 
+// dw_out (fp32) doubles as the accumulator: the first chunk writes, later chunks add.
 hipError_t fma_dw(const Plan& p, const Work& w, const ChunkArgs& a, hipStream_t s) {
-  const dim3 grid = grid2(p.v, p.d);
-  const float* G = static_cast<const float*>(w.prob);
-  if (p.dtype == FLCE_F32) {
-    // fp32 output doubles as the accumulator
-    float* out = static_cast<float*>(a.dw);
-    int mode = a.dw_mode == DW_FIRST ? DW_FIRST : (a.dw_mode == DW_SINGLE ? DW_SINGLE : DW_MID);
-    fma_dw_kernel<float><<<grid, 256, 0, s>>>(G, p.vp, static_cast<const float*>(a.h), a.rows, p.d, p.v, out, out,
-                                              mode);
-  } else {
-    fma_dw_kernel<bf16_t><<<grid, 256, 0, s>>>(G, p.vp, static_cast<const bf16_t*>(a.h), a.rows, p.d, p.v, w.dwacc,
-                                               static_cast<bf16_t*>(a.dw), a.dw_mode);
-  }
+  if (p.dtype != FLCE_F32) return hipErrorInvalidValue;
+  float* out = static_cast<float*>(a.dw);
+  const int mode = (a.dw_mode == DW_FIRST || a.dw_mode == DW_SINGLE) ? DW_SINGLE : DW_MID;
+  fma_dw_kernel<<<grid2(p.v, p.d), 256, 0, s>>>(static_cast<const float*>(w.prob), p.vp,
+                                               static_cast<const float*>(a.h), a.rows, p.d, p.v, out, mode);
   return hipGetLastError();
 }
 

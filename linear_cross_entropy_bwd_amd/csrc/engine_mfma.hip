@@ -471,9 +471,8 @@ struct DwArgs {
   Operand gt, h;
   int64_t v, d;
   int64_t tiles_m, tiles_n, group_m;
-  float* acc_buf;
-  bf16_t* out_bf16;
-  float* out_f32;
+  bf16_t* lo;        // [v][d] low bf16 half of the running sum (out holds the high half)
+  bf16_t* out;       // dw_out
   int mode;
 };
 
@@ -488,12 +487,12 @@ __global__ __launch_bounds__(kThreads) void mfma_dw_kernel(DwArgs a) {
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  // The mode is uniform.  Per 32x32 subtile, a lane owns 16 rows of one
-  // column; all 16 accumulator loads are issued before any store so their
-  // latencies overlap.
-  const float* __restrict__ src = a.acc_buf;
-  float* __restrict__ dst_acc = a.acc_buf;
+  // The running dW sum across chunks is the pair (hi, lo) of bf16 values
+  // whose sum carries about 16 significant bits: hi lives in dw_out, lo in
+  // the workspace.  The mode is uniform.  Per 32x32 subtile a lane owns 16
+  // rows of one column; all loads are issued before any store.
   const bool read_acc = a.mode == DW_MID || a.mode == DW_LAST;
+  const bool keep_split = a.mode == DW_FIRST || a.mode == DW_MID;
   static_for<4>([&](auto I) {
     static_for<4>([&](auto J) {
       const int64_t col = n0 + wn * 128 + J * 32 + (lane & 31);
@@ -501,19 +500,20 @@ __global__ __launch_bounds__(kThreads) void mfma_dw_kernel(DwArgs a) {
       float prev[16];
       static_for<16>([&](auto R) {
         const int64_t row = m0 + wm * 128 + acc_row(I, R, lane);
-        prev[R] = (read_acc && col_ok && row < a.v) ? src[row * a.d + col] : 0.0f;
+        prev[R] = 0.0f;
+        if (read_acc && col_ok && row < a.v) {
+          const int64_t o = row * a.d + col;
+          prev[R] = bf16_to_f32(a.out[o]) + bf16_to_f32(a.lo[o]);
+        }
       });
       static_for<16>([&](auto R) {
         const int64_t row = m0 + wm * 128 + acc_row(I, R, lane);
         if (col_ok && row < a.v) {
           const int64_t o = row * a.d + col;
           const float x = acc.c[I][J][R.value] + prev[R];
-          if (a.mode == DW_FIRST || a.mode == DW_MID)
-            dst_acc[o] = x;
-          else if (a.out_bf16 != nullptr)
-            a.out_bf16[o] = f32_to_bf16(x);
-          else
-            a.out_f32[o] = x;
+          const bf16_t hi = f32_to_bf16(x);
+          a.out[o] = hi;
+          if (keep_split) a.lo[o] = f32_to_bf16(x - bf16_to_f32(hi));
         }
       });
     });
@@ -577,9 +577,8 @@ hipError_t mfma_dw(const Plan& p, const Work& w, const ChunkArgs& c, hipStream_t
   a.tiles_m = p.vp / TM;
   a.tiles_n = cdiv(p.d, TN);
   a.group_m = p.group_m[2];
-  a.acc_buf = w.dwacc;
-  a.out_bf16 = p.dtype == FLCE_BF16 ? static_cast<bf16_t*>(c.dw) : nullptr;
-  a.out_f32 = p.dtype == FLCE_BF16 ? nullptr : static_cast<float*>(c.dw);
+  a.lo = w.dwlo;
+  a.out = static_cast<bf16_t*>(c.dw);
   a.mode = c.dw_mode;
   mfma_dw_kernel<<<static_cast<unsigned>(a.tiles_m * a.tiles_n), kThreads, 0, s>>>(a);
   return hipGetLastError();

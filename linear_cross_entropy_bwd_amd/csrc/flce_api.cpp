@@ -101,7 +101,7 @@ int make_plan(int64_t n, int64_t d, int64_t v, int32_t dtype, int32_t with_bwd, 
   q.off_ps = take(sizeof(float) * q.ngroups * q.chunk);
   q.prob_bytes = with_bwd ? static_cast<size_t>(q.chunk * q.vp * prob_elem) : 0;
   q.off_prob = take(q.prob_bytes);
-  q.off_dwacc = take(q.dw_acc ? sizeof(float) * static_cast<size_t>(v * d) : 0);
+  q.off_dwacc = take(q.dw_acc ? sizeof(uint16_t) * static_cast<size_t>(v * d) : 0);
   q.off_dhpart = take(with_bwd && q.dh_splits > 1 ? sizeof(float) * q.dh_splits * q.chunk * d : 0);
   q.total = off;
   *p = q;
@@ -197,7 +197,7 @@ Work carve(const Plan& p, char* base) {
   w.pm = reinterpret_cast<float*>(base + p.off_pm);
   w.ps = reinterpret_cast<float*>(base + p.off_ps);
   w.prob = base + p.off_prob;
-  w.dwacc = reinterpret_cast<float*>(base + p.off_dwacc);
+  w.dwlo = reinterpret_cast<uint16_t*>(base + p.off_dwacc);
   w.dhpart = reinterpret_cast<float*>(base + p.off_dhpart);
   return w;
 }

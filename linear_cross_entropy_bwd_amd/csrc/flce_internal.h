@@ -32,7 +32,7 @@ struct Plan {
   int64_t group;       // vocabulary columns per partial (max, sum-exp) pair
   int64_t ngroups;
   int64_t dh_splits;   // split of the K = vocabulary reduction of dH
-  int32_t dw_acc;      // dW accumulates across chunks in an fp32 workspace buffer
+  int32_t dw_acc;      // dW's running sum needs a workspace low half (bf16 path, several chunks)
   int64_t group_m[3];  // tile-row group of the logits, dH and dW tile orders
   // byte offsets inside the single workspace allocation
   size_t off_nvalid, off_zy, off_gy, off_lse, off_loss, off_pm, off_ps, off_prob, off_dwacc, off_dhpart;
@@ -52,7 +52,7 @@ struct Work {
   float* pm;         // [G][C] partial row max per vocabulary group; becomes the softmax factor
   float* ps;         // [G][C] partial sum of exp(z - max) per group
   void* prob;        // [C][vp] exp(z - group max), turned into G in place (dtype of the engine)
-  float* dwacc;      // [v][d] fp32 dW accumulator (when Plan::dw_acc)
+  uint16_t* dwlo;    // [v][d] bf16 low half of the running dW sum; dw_out holds the high half
   float* dhpart;     // [S][C][d] fp32 split-vocabulary partials of dH (when dh_splits > 1)
 };
 
@@ -95,7 +95,7 @@ hipError_t launch_grad(const Plan& p, const Work& w, const ChunkArgs& a, hipStre
 hipError_t launch_loss_reduce(const Plan& p, const Work& w, int32_t reduction, float* loss_out, hipStream_t s);
 hipError_t launch_dh_reduce(const Plan& p, const Work& w, const ChunkArgs& a, hipStream_t s);
 
-// fp32 FMA engine (engine_fma.hip): any dtype, used for FLCE_F32.
+// fp32 FMA engine (engine_fma.hip): FLCE_F32 (dw_out itself accumulates).
 hipError_t fma_logits(const Plan& p, const Work& w, const ChunkArgs& a, int store_prob, hipStream_t s);
 hipError_t fma_dh(const Plan& p, const Work& w, const ChunkArgs& a, hipStream_t s);
 hipError_t fma_dw(const Plan& p, const Work& w, const ChunkArgs& a, hipStream_t s);
