@@ -22,6 +22,29 @@ sys.path.insert(0, ROOT)
 METRIC = "fused linear-CE fwd+bwd tokens/s (N=8192,D=4096,V=128256 bf16); MFMA %"
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}      # MI355X dense matrix peaks
 GEMM_KINDS = ("logits_lse", "dh_gemm", "dw_gemm")
+COPY_BYTES = 1 << 30
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dw_gemm_llama3_8b_head_traffic.txt")
+ENGINE_SRC = os.path.join(ROOT, "linear_cross_entropy_bwd_amd", "csrc", "engine_mfma.hip")
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or None when
+    there is none or the engine source changed since the counters were taken."""
+    import hashlib
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    digest = hashlib.sha256(open(ENGINE_SRC, "rb").read()).hexdigest()
+    if kv.get("engine_sha256") != digest or kv.get("kernel") != kernel:
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def log(msg: str) -> None:
@@ -50,8 +73,11 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="llama3_8b_head")
-    ap.add_argument("--cpu-rows", type=int, default=768, help="tokens in the oracle's CPU-baseline sample")
+XX
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="run a 1 GiB device copy (counter calibration) and one step, print nothing else; "
+                         "meant to run under rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -81,6 +107,19 @@ def main() -> int:
         flce.linear_cross_entropy(hd, wd, yd, reduction=wl.reduction, out=out)
     torch.cuda.synchronize()
     log(f"[bench] {args.warmup} warm-up steps done")
+
+    if args.traffic_probe:
+        # A plain copy of exactly COPY_BYTES (read COPY_BYTES, write COPY_BYTES) calibrates
+        # the FETCH_SIZE / WRITE_SIZE counters against a known byte count.
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        flce.linear_cross_entropy(hd, wd, yd, reduction=wl.reduction, out=out)
+        torch.cuda.synchronize()
+        log("[bench] traffic probe done")
+        return 0
 
     # peak extra device memory of one call
     flce.flce_memory_high_water(reset=True)
@@ -134,7 +173,7 @@ def main() -> int:
         "mfma_pct": 100.0 * flops_step / (ms_step * 1e-3) / (peak * 1e12),
         "tflops": flops_step / (ms_step * 1e-3) / 1e12,
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                     "frac": achieved / peak, "traffic": None,
+                     "frac": achieved / peak, "traffic": measured_traffic(dom),
                      "avg_launch_ms": dom_avg_ms, "flop_per_launch": flops_launch},
         "kernels_ms_per_step": {k: v[1] / args.steps for k, v in kern.items() if v[0]},
         "memory": {"extra_device_bytes": extra, "logits_bytes_avoided": logits_bytes_avoided(wl.n, wl.v),
