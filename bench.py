@@ -73,7 +73,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="llama3_8b_head")
-XX
+    ap.add_argument("--cpu-rows", type=int, default=3072, help="tokens in the oracle's CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run a 1 GiB device copy (counter calibration) and one step, print nothing else; "

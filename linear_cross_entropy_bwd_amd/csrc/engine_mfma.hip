@@ -465,6 +465,46 @@ __global__ __launch_bounds__(kThreads) void mfma_dh_kernel(DhArgs a) {
   });
 }
 
+// dW epilogue of an interior tile.  Between chunks the running sum (hi, lo)
+// is kept in a fragment-native order: the two 32x32 subtiles (i, 2p) and
+// (i, 2p+1) of a wave store their 32 values per lane inside the very 32x64
+// block of the region (dw_out for hi, the workspace for lo) that their
+// row-major result covers, as four 1 KB pieces of 8 full 128-byte rows; lane L
+// of piece (u, h) holds values 8h .. 8h+7 of subtile 2p+u at row 8(2u+h) + L/8,
+// bytes 16 (L % 8).  Each block is read, updated and written by its own wave
+// only, so blocks need no synchronisation and the last chunk can overwrite a
+// block with the row-major result as soon as it has folded it.
+__device__ __forceinline__ uint4* dw_piece(char* block, int64_t row_bytes, int u, int h, uint32_t lane_off) {
+  return reinterpret_cast<uint4*>(block + 8 * (2 * u + h) * row_bytes + lane_off);
+}
+
+__device__ __forceinline__ void split_store(const floatx16& x, uint4* hi0, uint4* hi1, uint4* lo0, uint4* lo1) {
+  uint32_t h[8], l[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float a0 = x[2 * k], a1 = x[2 * k + 1];
+    h[k] = pack_bf16x2(a0, a1);
+    const float r0 = a0 - bf16_to_f32(static_cast<bf16_t>(h[k] & 0xffffu));
+    const float r1 = a1 - bf16_to_f32(static_cast<bf16_t>(h[k] >> 16));
+    l[k] = pack_bf16x2(r0, r1);
+  }
+  *hi0 = make_uint4(h[0], h[1], h[2], h[3]);
+  *hi1 = make_uint4(h[4], h[5], h[6], h[7]);
+  *lo0 = make_uint4(l[0], l[1], l[2], l[3]);
+  *lo1 = make_uint4(l[4], l[5], l[6], l[7]);
+}
+
+__device__ __forceinline__ void add_pair(floatx16& x, const uint4& hi0, const uint4& hi1, const uint4& lo0,
+                                         const uint4& lo1) {
+  const uint32_t h[8] = {hi0.x, hi0.y, hi0.z, hi0.w, hi1.x, hi1.y, hi1.z, hi1.w};
+  const uint32_t l[8] = {lo0.x, lo0.y, lo0.z, lo0.w, lo1.x, lo1.y, lo1.z, lo1.w};
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    x[2 * k] += bf16_to_f32(static_cast<bf16_t>(h[k] & 0xffffu)) + bf16_to_f32(static_cast<bf16_t>(l[k] & 0xffffu));
+    x[2 * k + 1] += bf16_to_f32(static_cast<bf16_t>(h[k] >> 16)) + bf16_to_f32(static_cast<bf16_t>(l[k] >> 16));
+  }
+}
+
 // ---- dW: tile rows = vocabulary, tile cols = hidden; K = chunk tokens ----------------
 
 struct DwArgs {
@@ -473,9 +513,65 @@ struct DwArgs {
   int64_t tiles_m, tiles_n, group_m;
   bf16_t* lo;        // [v][d] low bf16 half of the running sum (out holds the high half)
   bf16_t* out;       // dw_out
-  int mode;
 };
 
+template <int MODE>
+__device__ __forceinline__ void dw_epilogue_tiled(const DwArgs& a, Acc& acc, int64_t m0, int64_t n0, int wave,
+                                                  int lane) {
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t row_bytes = a.d * static_cast<int64_t>(sizeof(bf16_t));
+  const int64_t wave_off = ((m0 + 128 * wm) * a.d + n0 + 128 * wn) * static_cast<int64_t>(sizeof(bf16_t));
+  char* hi_base = reinterpret_cast<char*>(a.out) + wave_off;
+  char* lo_base = reinterpret_cast<char*>(a.lo) + wave_off;
+  const uint32_t lane_off = static_cast<uint32_t>((lane >> 3) * row_bytes) + static_cast<uint32_t>(lane & 7) * 16u;
+  constexpr bool fold = MODE == DW_MID || MODE == DW_LAST;
+  constexpr bool keep_split = MODE == DW_FIRST || MODE == DW_MID;
+  // block b = (i, p) = (b / 2, b % 2) starts at row 32 i, column 64 p of the wave's quadrant
+  auto block_off = [&](int b) { return (32 * (b >> 1)) * row_bytes + 128 * (b & 1); };
+  uint4 buf[2][2][4];
+  auto fetch = [&](int b, uint4 (&dst)[2][4]) {
+    char* hb = hi_base + block_off(b);
+    char* lb = lo_base + block_off(b);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      dst[u][0] = *dw_piece(hb, row_bytes, u, 0, lane_off);
+      dst[u][1] = *dw_piece(hb, row_bytes, u, 1, lane_off);
+      dst[u][2] = *dw_piece(lb, row_bytes, u, 0, lane_off);
+      dst[u][3] = *dw_piece(lb, row_bytes, u, 1, lane_off);
+    }
+  };
+  if constexpr (fold) fetch(0, buf[0]);
+  static_for<8>([&](auto B) {
+    constexpr int I = B / 2, P = B % 2;
+    if constexpr (fold) {
+      // the next block's stored sum is in flight while this one is finished
+      if constexpr (B < 7) fetch(B + 1, buf[(B + 1) & 1]);
+      static_for<2>([&](auto U) {
+        add_pair(acc.c[I][2 * P + U], buf[B & 1][U][0], buf[B & 1][U][1], buf[B & 1][U][2], buf[B & 1][U][3]);
+      });
+    }
+    if constexpr (keep_split) {
+      char* hb = hi_base + block_off(B);
+      char* lb = lo_base + block_off(B);
+      static_for<2>([&](auto U) {
+        split_store(acc.c[I][2 * P + U], dw_piece(hb, row_bytes, U, 0, lane_off), dw_piece(hb, row_bytes, U, 1, lane_off),
+                    dw_piece(lb, row_bytes, U, 0, lane_off), dw_piece(lb, row_bytes, U, 1, lane_off));
+      });
+    } else {
+      // DW_LAST / DW_SINGLE: the block's row-major bf16 result
+      static_for<2>([&](auto U) {
+        constexpr int J = 2 * P + U;
+        const int64_t col = n0 + wn * 128 + J * 32 + (lane & 31);
+        static_for<16>([&](auto R) {
+          const int64_t row = m0 + wm * 128 + acc_row(I, R, lane);
+          a.out[row * a.d + col] = f32_to_bf16(acc.c[I][J][R.value]);
+        });
+      });
+    }
+  });
+}
+
+template <int MODE>
 __global__ __launch_bounds__(kThreads) void mfma_dw_kernel(DwArgs a) {
   const int64_t nb = a.tiles_m * a.tiles_n;
   const int64_t t = xcd_remap(blockIdx.x, nb);
@@ -485,14 +581,20 @@ __global__ __launch_bounds__(kThreads) void mfma_dw_kernel(DwArgs a) {
   Acc acc;
   tile_loop<false, false>(a.gt, a.h, m0, n0, 0, a.gt.k_bound, acc);
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_id();
   const int wm = wave >> 1, wn = wave & 1;
   // The running dW sum across chunks is the pair (hi, lo) of bf16 values
-  // whose sum carries about 16 significant bits: hi lives in dw_out, lo in
-  // the workspace.  The mode is uniform.  Per 32x32 subtile a lane owns 16
-  // rows of one column; all loads are issued before any store.
-  const bool read_acc = a.mode == DW_MID || a.mode == DW_LAST;
-  const bool keep_split = a.mode == DW_FIRST || a.mode == DW_MID;
+  // whose sum carries about 16 significant bits: hi lives in dw_out, lo in the
+  // workspace, both inside this tile's own 256x256 region.
+  const bool interior = m0 + TM <= a.v && n0 + TN <= a.d;
+  if (interior) {
+    dw_epilogue_tiled<MODE>(a, acc, m0, n0, wave, lane);
+    return;
+  }
+  // Edge tiles: row-major, element by element.  Per 32x32 subtile a lane
+  // owns 16 rows of one column; all loads are issued before any store.
+  constexpr bool read_acc = MODE == DW_MID || MODE == DW_LAST;
+  constexpr bool keep_split = MODE == DW_FIRST || MODE == DW_MID;
   static_for<4>([&](auto I) {
     static_for<4>([&](auto J) {
       const int64_t col = n0 + wn * 128 + J * 32 + (lane & 31);
@@ -579,8 +681,13 @@ hipError_t mfma_dw(const Plan& p, const Work& w, const ChunkArgs& c, hipStream_t
   a.group_m = p.group_m[2];
   a.lo = w.dwlo;
   a.out = static_cast<bf16_t*>(c.dw);
-  a.mode = c.dw_mode;
-  mfma_dw_kernel<<<static_cast<unsigned>(a.tiles_m * a.tiles_n), kThreads, 0, s>>>(a);
+  const dim3 grid(static_cast<unsigned>(a.tiles_m * a.tiles_n));
+  switch (c.dw_mode) {
+    case DW_FIRST: mfma_dw_kernel<DW_FIRST><<<grid, kThreads, 0, s>>>(a); break;
+    case DW_MID: mfma_dw_kernel<DW_MID><<<grid, kThreads, 0, s>>>(a); break;
+    case DW_LAST: mfma_dw_kernel<DW_LAST><<<grid, kThreads, 0, s>>>(a); break;
+    default: mfma_dw_kernel<DW_SINGLE><<<grid, kThreads, 0, s>>>(a); break;
+  }
   return hipGetLastError();
 }
 
