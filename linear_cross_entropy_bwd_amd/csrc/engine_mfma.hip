@@ -89,13 +89,14 @@ __device__ __forceinline__ void lane_load_offsets(int64_t ld, uint32_t (&off)[2]
   }
 }
 
+// Loads I0 .. I0 + CNT - 1 of a wave's share of one operand-stage.
 // Interior stage: every load in bounds; uniform base + lane offset.
-template <bool KMAJ>
+template <int I0, int CNT, bool KMAJ>
 __device__ __forceinline__ void load_stage_fast(const Operand& op, int64_t mn0, int64_t k0, bf16_t* lds,
                                                 const uint32_t (&off)[2]) {
   const int w = wave_id();
 #pragma unroll
-  for (int i = 0; i < kLoadsPerStage; ++i) {
+  for (int i = I0; i < I0 + CNT; ++i) {
     const int64_t row0 = KMAJ ? (mn0 + 64 * w + 8 * i) * op.ld + k0 : (k0 + 16 * w + 2 * i) * op.ld + mn0;
     const char* base = reinterpret_cast<const char*>(op.ptr + row0);
     __builtin_amdgcn_global_load_lds(base + off[i & 1], FLCE_LDS(lds + (w * kLoadsPerStage + i) * 512), 16, 0, 0);
@@ -103,13 +104,13 @@ __device__ __forceinline__ void load_stage_fast(const Operand& op, int64_t mn0, 
 }
 
 // Edge stage: per-lane bounds; out-of-range lanes read 16 zero bytes.
-template <bool KMAJ>
+template <int I0, int CNT, bool KMAJ>
 __device__ __forceinline__ void load_stage_edge(const Operand& op, int64_t mn0, int64_t k0, bf16_t* lds) {
   const int lane = threadIdx.x & 63;
   const int w = wave_id();
   const unsigned int* zero = g_zero16;
 #pragma unroll
-  for (int i = 0; i < kLoadsPerStage; ++i) {
+  for (int i = I0; i < I0 + CNT; ++i) {
     const int b = w * kLoadsPerStage + i;
     const void* src;
     if (KMAJ) {
@@ -129,14 +130,14 @@ __device__ __forceinline__ void load_stage_edge(const Operand& op, int64_t mn0, 
   }
 }
 
-template <bool KMAJ>
+template <int I0, int CNT, bool KMAJ>
 __device__ __forceinline__ void load_stage(const Operand& op, int64_t mn0, int64_t k0, bf16_t* lds,
                                            const uint32_t (&off)[2]) {
   const bool interior = mn0 + TM <= op.mn_bound && k0 + TK <= op.k_bound;
   if (interior)
-    load_stage_fast<KMAJ>(op, mn0, k0, lds, off);
+    load_stage_fast<I0, CNT, KMAJ>(op, mn0, k0, lds, off);
   else
-    load_stage_edge<KMAJ>(op, mn0, k0, lds);
+    load_stage_edge<I0, CNT, KMAJ>(op, mn0, k0, lds);
 }
 
 // Per-lane LDS byte offsets of the fragment reads of a wave whose operand rows
@@ -163,16 +164,31 @@ __device__ __forceinline__ void lane_frag_offsets(int wbase, uint32_t (&fo)[4]) 
   }
 }
 
-template <bool KMAJ>
-__device__ __forceinline__ bf16x8 read_frag(const bf16_t* lds, const uint32_t (&fo)[4], int i, int ks) {
-  const char* b = reinterpret_cast<const char*>(lds);
-  if (KMAJ) {
-    return *reinterpret_cast<const bf16x8*>(b + fo[ks] + 4096 * i);
+// LDS byte address of a shared-memory pointer.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(FLCE_LDS(p)));
+}
+
+// Fragment (subtile i, k-step KS) of the operand whose stage starts at LDS
+// byte address `slot`.  The k-major read is an ordinary LDS load.  The
+// transpose reads are issued as inline assembly: the compiler does not
+// separate the builtin's LDS access from the direct loads still filling other
+// slots and would wait for every one of them (vmcnt(0)) before each read,
+// which serializes loads and MFMAs.  The ordering these reads need is
+// explicit instead: the stage barrier (all volatile asm keeps its order)
+// before them, and wait_frags() between them and the MFMAs that use them.
+template <bool KMAJ, int KS>
+__device__ __forceinline__ bf16x8 read_frag(const bf16_t* lds, uint32_t slot, const uint32_t (&fo)[4], int i) {
+  if constexpr (KMAJ) {
+    const char* b = reinterpret_cast<const char*>(lds);
+    return *reinterpret_cast<const bf16x8*>(b + fo[KS] + 4096 * i);
   } else {
-    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) v4i16*)(b + fo[i] + 8192 * ks));
-    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) v4i16*)(b + fo[i] + 8192 * ks + 2048));
+    v4i16 lo, hi;
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %2 offset:%3\n\t"
+        "ds_read_b64_tr_b16 %1, %2 offset:%4"
+        : "=&v"(lo), "=&v"(hi)
+        : "v"(slot + fo[i]), "i"(8192 * KS), "i"(8192 * KS + 2048));
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   }
 }
@@ -207,6 +223,14 @@ struct Frags {
   bf16x8 a[4], b[4];
 };
 
+// Wait for every LDS read in flight and make the fragments' registers depend
+// on that wait, so that no MFMA reading them is scheduled before it.
+__device__ __forceinline__ void wait_frags(Frags& f) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(f.a[0]), "+v"(f.a[1]), "+v"(f.a[2]), "+v"(f.a[3]), "+v"(f.b[0]), "+v"(f.b[1]), "+v"(f.b[2]),
+                 "+v"(f.b[3]));
+}
+
 // Wait until at most `n` operand-stages (8 direct loads each, per wave) are
 // still in flight: s_waitcnt vmcnt(8 n), lgkmcnt and expcnt left alone (gfx9
 // encoding: vmcnt bits [3:0] and [15:14]).
@@ -230,35 +254,41 @@ __device__ __forceinline__ void stage_barrier() {
 }
 
 // Instruction-class masks of __builtin_amdgcn_sched_group_barrier.
-constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100;
+constexpr int kSchedMfma = 0x008, kSchedVmemRead = 0x020, kSchedDsRead = 0x100;
 
-// Ask the scheduler to alternate the 16 MFMAs of a k-step with `reads` LDS reads.
-template <int reads>
+// Ask the scheduler to alternate the `mfmas` MFMAs of a k-step with `reads`
+// LDS reads and to spread `loads` global->LDS loads evenly among them.
+template <int mfmas, int reads, int loads>
 __device__ __forceinline__ void interleave_hint() {
+  constexpr int every = loads > 0 && mfmas > 0 ? (mfmas + loads - 1) / loads : 1;
 #pragma unroll
-  for (int k = 0; k < 16; ++k) {
-    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+  for (int k = 0; k < (mfmas > reads ? mfmas : reads); ++k) {
+    if (k < mfmas) __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
     if (k < reads) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+    if (k % every == 0 && k / every < loads) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
   }
-  if (reads > 16) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, reads - 16, 0);
 }
 
 // Main loop: acc += A[m0 .. m0+255, k_lo .. k_hi) * B[n0 .. n0+255, k_lo .. k_hi)^T
 //
 // LDS is a ring of 5 operand-stage slots of 32 KB (the whole 160 KB):
 // operand-stage q (A_s is q = 2s, B_s is q = 2s + 1) lives in slot q % 5.
-// While stage it is computed from two slots, B_{it+1}, A_{it+1} and A_{it+2}
-// are in flight or landed, so the A operand is fetched two stages ahead and
-// the B operand one.  Every iteration issues exactly one B and one A stage
-// (stages past the end load zeros and are never consumed), so the number of
-// loads in flight is the same every time and the waits are constants.
-// Iteration it computes stage it in four k-steps; the fragments of each
-// k-step are read from LDS while the MFMAs of the previous one run:
-//   k-steps 0..2: MFMAs | reads of the next k-step of stage it
-//   wait until only A_{it+2} may still be in flight; barrier  (all of stage
-//     it+1 has landed and every wave has read all of stage it)
-//   issue B_{it+2} and A_{it+3} into the two slots stage it used
-//   k-step 3: MFMAs | reads of k-step 0 of stage it+1
+// Iteration j runs from one workgroup barrier to the next and computes stage
+// j in four k-steps; the fragments of each k-step are read from LDS while the
+// MFMAs of the previous one run.  At its start every wave has finished
+// reading stage j-1, so the two slots that stage used are free: the
+// iteration fills them with B_{j+1} and A_{j+2}, four direct loads per wave
+// beside each k-step's MFMAs rather than in one burst, so that the load
+// queue drains while the matrix cores keep issuing:
+//   k-step 0: MFMAs of k-step 3 of stage j-1 | reads of k-step 0 | B_{j+1} loads 0..3
+//   k-step 1: MFMAs of k-step 0              | reads of k-step 1 | B_{j+1} loads 4..7
+//   k-step 2: MFMAs of k-step 1              | reads of k-step 2 | A_{j+2} loads 0..3
+//   k-step 3: MFMAs of k-step 2              | reads of k-step 3 | A_{j+2} loads 4..7
+//   wait until only A_{j+2} may be in flight; barrier (stage j+1 has landed
+//     for every wave, and every wave has read all of stage j)
+// So A is fetched two stages and B one stage ahead of its use.  Stages past
+// the end load zeros and are never consumed, so every iteration issues the
+// same loads and the waits are constants.
 template <bool A_KMAJ, bool B_KMAJ>
 __device__ __forceinline__ void tile_loop(const Operand& A, const Operand& B, int64_t m0, int64_t n0, int64_t k_lo,
                                           int64_t k_hi, Acc& acc) {
@@ -281,13 +311,14 @@ __device__ __forceinline__ void tile_loop(const Operand& A, const Operand& B, in
 
   const int64_t nk = (k_hi - k_lo + TK - 1) / TK;
   auto k_of = [&](int64_t st) { return st < nk ? k_lo + st * TK : k_hi; };  // past the end: zeros
-  auto issue_a = [&](int64_t st) { load_stage<A_KMAJ>(A, m0, k_of(st), lds[(2 * st) % kSlots], offa); };
-  auto issue_b = [&](int64_t st) { load_stage<B_KMAJ>(B, n0, k_of(st), lds[(2 * st + 1) % kSlots], offb); };
-  auto read = [&](int sa, int sb, int ks, Frags& f) {
+  const uint32_t lds0 = lds_addr(lds[0]);
+  auto read = [&](int sa, int sb, auto ks, Frags& f) {
+    constexpr int KS = decltype(ks)::value;
+    const uint32_t slot_a = lds0 + sa * kStageElems * 2, slot_b = lds0 + sb * kStageElems * 2;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) f.a[i] = read_frag<A_KMAJ>(lds[sa], foa, i, ks);
+    for (int i = 0; i < 4; ++i) f.a[i] = read_frag<A_KMAJ, KS>(lds[sa], slot_a, foa, i);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) f.b[j] = read_frag<B_KMAJ>(lds[sb], fob, j, ks);
+    for (int j = 0; j < 4; ++j) f.b[j] = read_frag<B_KMAJ, KS>(lds[sb], slot_b, fob, j);
   };
   auto mma = [&](const Frags& f) {
 #pragma unroll
@@ -296,38 +327,81 @@ __device__ __forceinline__ void tile_loop(const Operand& A, const Operand& B, in
       for (int j = 0; j < 4; ++j)
         acc.c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc.c[i][j], 0, 0, 0);
   };
+  auto next = [](int s, int d) { return s + d >= kSlots ? s + d - kSlots : s + d; };
 
-  // Prologue: A_0 B_0 A_1 B_1 A_2 in flight; wait for A_0 and B_0.
-  issue_a(0);
-  issue_b(0);
-  issue_a(1);
-  issue_b(1);
-  issue_a(2);
-  wait_stages(3);
+  // Prologue: A_0, B_0, A_1 in flight; wait for A_0 and B_0.
+  load_stage<0, kLoadsPerStage, A_KMAJ>(A, m0, k_of(0), lds[0], offa);
+  load_stage<0, kLoadsPerStage, B_KMAJ>(B, n0, k_of(0), lds[1], offb);
+  load_stage<0, kLoadsPerStage, A_KMAJ>(A, m0, k_of(1), lds[2], offa);
+  wait_stages(1);
   stage_barrier();
-  Frags f0, f1;
-  int sa = 0, sb = 1;
-  read(sa, sb, 0, f0);
 
-  for (int64_t it = 0; it < nk; ++it) {
-    read(sa, sb, 1, f1);
+  Frags f0, f1;
+  int sa = 0, sb = 1;  // slots of stage j
+  // One iteration.  FIRST: there is no k-step 3 of a previous stage to
+  // finish.  FAST: both loaded stages lie inside their operands, so the loads
+  // need no bounds checks and the iteration is one basic block, in which the
+  // scheduler can interleave loads, LDS reads and MFMAs.
+  auto body = [&](int64_t j, auto first, auto fast) {
+    constexpr bool kFirst = decltype(first)::value;
+    constexpr bool kFast = decltype(fast)::value;
+    constexpr int kPrevMfma = kFirst ? 0 : 16;
+    bf16_t* slot_b = lds[next(sb, 2)];  // B_{j+1}: slot of A_{j-1}
+    bf16_t* slot_a = lds[next(sa, 4)];  // A_{j+2}: slot of B_{j-1}
+    const int64_t kb = k_of(j + 1), ka = k_of(j + 2);
+    auto load_b = [&](auto i0) {
+      if constexpr (kFast)
+        load_stage_fast<decltype(i0)::value, 4, B_KMAJ>(B, n0, kb, slot_b, offb);
+      else
+        load_stage<decltype(i0)::value, 4, B_KMAJ>(B, n0, kb, slot_b, offb);
+    };
+    auto load_a = [&](auto i0) {
+      if constexpr (kFast)
+        load_stage_fast<decltype(i0)::value, 4, A_KMAJ>(A, m0, ka, slot_a, offa);
+      else
+        load_stage<decltype(i0)::value, 4, A_KMAJ>(A, m0, ka, slot_a, offa);
+    };
+    if constexpr (!kFirst) wait_frags(f1);
+    read(sa, sb, std::integral_constant<int, 0>{}, f0);
+    if constexpr (!kFirst) mma(f1);
+    load_b(std::integral_constant<int, 0>{});
+    interleave_hint<kPrevMfma, kReads, 4>();
+    wait_frags(f0);
+    read(sa, sb, std::integral_constant<int, 1>{}, f1);
     mma(f0);
-    interleave_hint<kReads>();
-    read(sa, sb, 2, f0);
+    load_b(std::integral_constant<int, 4>{});
+    interleave_hint<16, kReads, 4>();
+    wait_frags(f1);
+    read(sa, sb, std::integral_constant<int, 2>{}, f0);
     mma(f1);
-    interleave_hint<kReads>();
-    read(sa, sb, 3, f1);
+    load_a(std::integral_constant<int, 0>{});
+    interleave_hint<16, kReads, 4>();
+    wait_frags(f0);
+    read(sa, sb, std::integral_constant<int, 3>{}, f1);
     mma(f0);
-    interleave_hint<kReads>();
+    load_a(std::integral_constant<int, 4>{});
+    interleave_hint<16, kReads, 4>();
     wait_stages(1);
     stage_barrier();
-    issue_b(it + 2);
-    issue_a(it + 3);
-    sa = sa + 2 >= kSlots ? sa + 2 - kSlots : sa + 2;
-    sb = sb + 2 >= kSlots ? sb + 2 - kSlots : sb + 2;
-    read(sa, sb, 0, f0);
+    sa = next(sa, 2);
+    sb = next(sb, 2);
+  };
+  // Leading stages that lie wholly inside each operand; iteration j loads
+  // B_{j+1} and A_{j+2}, so it is fast while j + 1 < inside_b and j + 2 < inside_a.
+  auto inside = [&](const Operand& op, int64_t mn0) -> int64_t {
+    if (mn0 + TM > op.mn_bound) return 0;
+    const int64_t full = (op.k_bound - k_lo) / TK;
+    return full < nk ? full : nk;
+  };
+  const int64_t ia = inside(A, m0), ib = inside(B, n0);
+  const int64_t fast_end = ib - 1 < ia - 2 ? ib - 1 : ia - 2;
+  if (nk > 0) body(0, std::true_type{}, std::false_type{});
+  int64_t j = 1;
+  for (; j < fast_end; ++j) body(j, std::false_type{}, std::true_type{});
+  for (; j < nk; ++j) body(j, std::false_type{}, std::false_type{});
+  if (nk > 0) {  // k-step 3 of the last stage
+    wait_frags(f1);
     mma(f1);
-    interleave_hint<kReads>();
   }
   wait_stages(0);  // no direct load may still target this workgroup's LDS when it exits
 }
