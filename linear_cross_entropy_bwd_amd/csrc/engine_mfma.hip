@@ -223,12 +223,21 @@ struct Frags {
   bf16x8 a[4], b[4];
 };
 
-// Wait for every LDS read in flight and make the fragments' registers depend
-// on that wait, so that no MFMA reading them is scheduled before it.
+// Wait for every LDS read in flight and make the registers of the fragments
+// read by inline assembly (the transposed operands) depend on that wait, so
+// that no MFMA reading them is scheduled before it.  Fragments read by plain
+// loads are tracked by the compiler, which waits for exactly what it needs.
+template <bool A_KMAJ, bool B_KMAJ>
 __device__ __forceinline__ void wait_frags(Frags& f) {
-  asm volatile("s_waitcnt lgkmcnt(0)"
-               : "+v"(f.a[0]), "+v"(f.a[1]), "+v"(f.a[2]), "+v"(f.a[3]), "+v"(f.b[0]), "+v"(f.b[1]), "+v"(f.b[2]),
-                 "+v"(f.b[3]));
+  if constexpr (!A_KMAJ && !B_KMAJ) {
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(f.a[0]), "+v"(f.a[1]), "+v"(f.a[2]), "+v"(f.a[3]), "+v"(f.b[0]), "+v"(f.b[1]), "+v"(f.b[2]),
+                   "+v"(f.b[3]));
+  } else if constexpr (!A_KMAJ) {
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(f.a[0]), "+v"(f.a[1]), "+v"(f.a[2]), "+v"(f.a[3]));
+  } else if constexpr (!B_KMAJ) {
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(f.b[0]), "+v"(f.b[1]), "+v"(f.b[2]), "+v"(f.b[3]));
+  }
 }
 
 // Wait until at most `n` operand-stages (8 direct loads each, per wave) are
@@ -245,27 +254,36 @@ __device__ __forceinline__ void wait_stages(int n) {
 }
 
 // Workgroup barrier without the memory fence of __syncthreads(): the direct
-// loads are waited for explicitly.  The empty asm statements keep the
-// compiler from moving memory accesses across it.
+// loads are waited for explicitly.  The wave's own LDS reads complete first,
+// so that a slot the barrier frees is no longer being read by anyone.  The
+// asm statements keep the compiler from moving memory accesses across it.
 __device__ __forceinline__ void stage_barrier() {
-  asm volatile("" ::: "memory");
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
 
+// The workgroup's LDS: the ring of operand-stage slots of the main loop.
+// After tile_loop returns, wave w may reuse bytes [8192 w, 8192 w + 8192) of
+// every slot as private scratch: only its own direct loads ever wrote there
+// (all drained), and no wave reads the ring after the last stage barrier.
+__device__ __forceinline__ bf16_t (*ring())[kStageElems] {
+  __shared__ __attribute__((aligned(16))) bf16_t lds[kSlots][kStageElems];
+  return lds;
+}
+constexpr int kWaveScratchBytes = 8192;
+
 // Instruction-class masks of __builtin_amdgcn_sched_group_barrier.
-constexpr int kSchedMfma = 0x008, kSchedVmemRead = 0x020, kSchedDsRead = 0x100;
+constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100;
 
 // Ask the scheduler to alternate the `mfmas` MFMAs of a k-step with `reads`
-// LDS reads and to spread `loads` global->LDS loads evenly among them.
-template <int mfmas, int reads, int loads>
+// LDS reads (the global->LDS loads it places by itself).
+template <int mfmas, int reads>
 __device__ __forceinline__ void interleave_hint() {
-  constexpr int every = loads > 0 && mfmas > 0 ? (mfmas + loads - 1) / loads : 1;
 #pragma unroll
   for (int k = 0; k < (mfmas > reads ? mfmas : reads); ++k) {
     if (k < mfmas) __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
     if (k < reads) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-    if (k % every == 0 && k / every < loads) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
   }
 }
 
@@ -278,8 +296,7 @@ __device__ __forceinline__ void interleave_hint() {
 // MFMAs of the previous one run.  At its start every wave has finished
 // reading stage j-1, so the two slots that stage used are free: the
 // iteration fills them with B_{j+1} and A_{j+2}, four direct loads per wave
-// beside each k-step's MFMAs rather than in one burst, so that the load
-// queue drains while the matrix cores keep issuing:
+// beside each k-step's MFMAs rather than in one burst:
 //   k-step 0: MFMAs of k-step 3 of stage j-1 | reads of k-step 0 | B_{j+1} loads 0..3
 //   k-step 1: MFMAs of k-step 0              | reads of k-step 1 | B_{j+1} loads 4..7
 //   k-step 2: MFMAs of k-step 1              | reads of k-step 2 | A_{j+2} loads 0..3
@@ -292,7 +309,7 @@ __device__ __forceinline__ void interleave_hint() {
 template <bool A_KMAJ, bool B_KMAJ>
 __device__ __forceinline__ void tile_loop(const Operand& A, const Operand& B, int64_t m0, int64_t n0, int64_t k_lo,
                                           int64_t k_hi, Acc& acc) {
-  __shared__ __attribute__((aligned(16))) bf16_t lds[kSlots][kStageElems];
+  bf16_t (*lds)[kStageElems] = ring();
   constexpr int kReads = (A_KMAJ ? 4 : 8) + (B_KMAJ ? 4 : 8);  // LDS reads per k-step
   const int wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -361,26 +378,26 @@ __device__ __forceinline__ void tile_loop(const Operand& A, const Operand& B, in
       else
         load_stage<decltype(i0)::value, 4, A_KMAJ>(A, m0, ka, slot_a, offa);
     };
-    if constexpr (!kFirst) wait_frags(f1);
+    if constexpr (!kFirst) wait_frags<A_KMAJ, B_KMAJ>(f1);
     read(sa, sb, std::integral_constant<int, 0>{}, f0);
     if constexpr (!kFirst) mma(f1);
     load_b(std::integral_constant<int, 0>{});
-    interleave_hint<kPrevMfma, kReads, 4>();
-    wait_frags(f0);
+    interleave_hint<kPrevMfma, kReads>();
+    wait_frags<A_KMAJ, B_KMAJ>(f0);
     read(sa, sb, std::integral_constant<int, 1>{}, f1);
     mma(f0);
     load_b(std::integral_constant<int, 4>{});
-    interleave_hint<16, kReads, 4>();
-    wait_frags(f1);
+    interleave_hint<16, kReads>();
+    wait_frags<A_KMAJ, B_KMAJ>(f1);
     read(sa, sb, std::integral_constant<int, 2>{}, f0);
     mma(f1);
     load_a(std::integral_constant<int, 0>{});
-    interleave_hint<16, kReads, 4>();
-    wait_frags(f0);
+    interleave_hint<16, kReads>();
+    wait_frags<A_KMAJ, B_KMAJ>(f0);
     read(sa, sb, std::integral_constant<int, 3>{}, f1);
     mma(f0);
     load_a(std::integral_constant<int, 4>{});
-    interleave_hint<16, kReads, 4>();
+    interleave_hint<16, kReads>();
     wait_stages(1);
     stage_barrier();
     sa = next(sa, 2);
@@ -400,7 +417,7 @@ __device__ __forceinline__ void tile_loop(const Operand& A, const Operand& B, in
   for (; j < fast_end; ++j) body(j, std::false_type{}, std::true_type{});
   for (; j < nk; ++j) body(j, std::false_type{}, std::false_type{});
   if (nk > 0) {  // k-step 3 of the last stage
-    wait_frags(f1);
+    wait_frags<A_KMAJ, B_KMAJ>(f1);
     mma(f1);
   }
   wait_stages(0);  // no direct load may still target this workgroup's LDS when it exits
@@ -443,6 +460,7 @@ __global__ __launch_bounds__(kThreads) void mfma_logits_kernel(LogitsArgs a) {
     static_for<4>([&](auto J) {
       const int64_t tok = n0 + wn * 128 + J * 32 + (lane & 31);
       const bool live = tok < a.rows;
+      char* stage = reinterpret_cast<char*>(ring()[J]) + kWaveScratchBytes * wave;
       float mx = -INFINITY;
       static_for<4>([&](auto I) {
         static_for<16>([&](auto R) {
@@ -460,15 +478,28 @@ __global__ __launch_bounds__(kThreads) void mfma_logits_kernel(LogitsArgs a) {
             e[U] = in_vocab(acc_row(I, r, lane)) ? __builtin_amdgcn_exp2f(fmaf(acc.c[I][J][r], kLog2e, -mxl)) : 0.0f;
             s += e[U];
           });
-          if (a.prob != nullptr && live) {
-            const int64_t col = vbase + I * 32 + 8 * Q + 4 * half;
+          if (a.prob != nullptr) {
+            // staging row t = token, 16-byte chunk I*4+Q (XOR-swizzled by the row)
+            const int t = lane & 31;
+            const int chunk = (I * 4 + Q) ^ (t & 15);
             uint2 pk;
             pk.x = pack_bf16x2(e[0], e[1]);
             pk.y = pack_bf16x2(e[2], e[3]);
-            *reinterpret_cast<uint2*>(a.prob + tok * a.vp + col) = pk;
+            *reinterpret_cast<uint2*>(stage + t * 256 + chunk * 16 + 8 * half) = pk;
           }
         });
       });
+      if (a.prob != nullptr) {
+        // The wave's 32 tokens x 128 vocabulary entries of P, 256 bytes per
+        // token, go out as four whole token rows per store.
+        __builtin_amdgcn_wave_barrier();
+        static_for<8>([&](auto Rr) {
+          const int t = 4 * Rr + (lane >> 4), c = lane & 15;
+          const uint4 v = *reinterpret_cast<const uint4*>(stage + t * 256 + ((c ^ (t & 15)) * 16));
+          const int64_t tk = n0 + wn * 128 + J * 32 + t;
+          if (tk < a.rows) *reinterpret_cast<uint4*>(a.prob + tk * a.vp + vbase + 8 * c) = v;
+        });
+      }
       s += __shfl_xor(s, 32);
       if (live && vbase < a.v) {
         if (half == 0) {

@@ -81,7 +81,7 @@ int make_plan(int64_t n, int64_t d, int64_t v, int32_t dtype, int32_t with_bwd, 
   }
   q.dw_acc = (with_bwd && dtype == FLCE_BF16 && q.nchunks > 1) ? 1 : 0;
   // Tile orders (see tile_coords): consecutive tiles share operand tiles in L2.
-  q.group_m[0] = env_i64("FLCE_GROUP_LOGITS", 1);
+  q.group_m[0] = env_i64("FLCE_GROUP_LOGITS", 8);
   q.group_m[1] = env_i64("FLCE_GROUP_DH", 8);
   q.group_m[2] = env_i64("FLCE_GROUP_DW", 4);
   if (!mul_ok(q.chunk, q.vp) || !mul_ok(q.ngroups, q.chunk)) return FLCE_ERR_INVALID_ARG;
