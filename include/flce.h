@@ -74,7 +74,8 @@ typedef enum { FLCE_MEAN = 0, FLCE_SUM = 1 } flce_reduction;
 
 enum {
   FLCE_OK = 0,
-  FLCE_ERR_INVALID_ARG = -1, /* null required pointer, n/d/v <= 0, unknown enum, size overflow */
+  FLCE_ERR_INVALID_ARG = -1, /* null required pointer, n/d/v <= 0, d > 2^24, v > 2^24 - 256, unknown enum,
+                                size overflow */
   FLCE_ERR_ALIGNMENT = -2,   /* pointer or row pitch not aligned as documented above */
   FLCE_ERR_OOM = -3,         /* workspace allocation failed */
   FLCE_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed */

@@ -19,6 +19,7 @@ namespace {
 constexpr size_t kAlign = 256;
 constexpr size_t kDefaultProbBudget = size_t(1) << 30;  // bytes for the chunk's [C, vp] buffer
 constexpr int64_t kVocabPad = 256;
+constexpr int64_t kMaxDim = int64_t(1) << 24;  // d <= 2^24, v <= 2^24 - 256
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -44,6 +45,9 @@ int make_plan(int64_t n, int64_t d, int64_t v, int32_t dtype, int32_t with_bwd, 
   if (dtype != FLCE_BF16 && dtype != FLCE_F32) return FLCE_ERR_INVALID_ARG;
   if (!mul_ok(n, d) || !mul_ok(v, d) || v > (int64_t(1) << 40) || n > (int64_t(1) << 40))
     return FLCE_ERR_INVALID_ARG;
+  // Row strides (d, and v rounded up to 256) stay below 2^24 elements, so the
+  // 32-bit offsets of the matrix engine's buffer loads cannot overflow.
+  if (d > kMaxDim || v > kMaxDim - 256) return FLCE_ERR_INVALID_ARG;
   Plan q;
   memset(&q, 0, sizeof(q));
   q.n = n;

@@ -74,6 +74,17 @@ def test_invalid_sizes():
         flce.flce_plan_info(8, 8, 0, flce.FLCE_F32, 1)
 
 
+def test_dimension_limits():
+    # row strides stay below 2^24 elements: d <= 2^24, v <= 2^24 - 256
+    big = 1 << 24
+    flce.flce_plan_info(8, big, 8, flce.FLCE_BF16, 1)
+    flce.flce_plan_info(8, 8, big - 256, flce.FLCE_BF16, 1)
+    for d, v in ((big + 1, 8), (8, big - 255)):
+        with pytest.raises(flce.FlceError):
+            flce.flce_plan_info(8, d, v, flce.FLCE_BF16, 1)
+        assert flce.flce_workspace_bytes(8, d, v, flce.FLCE_BF16, 1) == 0
+
+
 def test_argument_errors_before_any_device_work():
     # All of these fail validation before the library makes a HIP call.
     A = 1 << 20  # fake, 16-byte aligned addresses: never dereferenced
