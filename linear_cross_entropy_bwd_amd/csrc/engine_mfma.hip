@@ -646,6 +646,8 @@ __device__ __forceinline__ void dw_epilogue_tiled(const DwArgs& a, Acc& acc, int
   const int wm = wave >> 1, wn = wave & 1;
   const int64_t row_bytes = a.d * static_cast<int64_t>(sizeof(bf16_t));
   const int64_t wave_off = ((m0 + 128 * wm) * a.d + n0 + 128 * wn) * static_cast<int64_t>(sizeof(bf16_t));
+  // this wave's private 8 KB of the (now idle) operand ring
+  char* scratch = reinterpret_cast<char*>(ring()[0]) + kWaveScratchBytes * wave;
   char* hi_base = reinterpret_cast<char*>(a.out) + wave_off;
   char* lo_base = reinterpret_cast<char*>(a.lo) + wave_off;
   const uint32_t lane_off = static_cast<uint32_t>((lane >> 3) * row_bytes) + static_cast<uint32_t>(lane & 7) * 16u;
@@ -683,14 +685,35 @@ __device__ __forceinline__ void dw_epilogue_tiled(const DwArgs& a, Acc& acc, int
                     dw_piece(lb, row_bytes, U, 0, lane_off), dw_piece(lb, row_bytes, U, 1, lane_off));
       });
     } else {
-      // DW_LAST / DW_SINGLE: the block's row-major bf16 result
+      // DW_LAST / DW_SINGLE: the block's row-major bf16 result, staged in
+      // the wave's LDS scratch so that it leaves as whole 128-byte rows.
+      // Neighbouring lanes hold neighbouring columns of the same 16 rows; one
+      // swap per row pair gives each lane two columns of one row (a 4-byte
+      // LDS write).  Block rows are 128 bytes, their 16-byte chunks XOR-
+      // swizzled by the row, so rows r and r+4 use different banks.
+      char* blk = scratch + (B & 1) * 4096;
+      const int par = lane & 1;
       static_for<2>([&](auto U) {
         constexpr int J = 2 * P + U;
-        const int64_t col = n0 + wn * 128 + J * 32 + (lane & 31);
-        static_for<16>([&](auto R) {
-          const int64_t row = m0 + wm * 128 + acc_row(I, R, lane);
-          a.out[row * a.d + col] = f32_to_bf16(acc.c[I][J][R.value]);
+        const int cpair = 32 * U + (lane & 30);  // block column of the pair's even lane
+        static_for<8>([&](auto Q) {
+          constexpr int R0 = 2 * Q;
+          const float x0 = acc.c[I][J][R0], x1 = acc.c[I][J][R0 + 1];
+          const float recv =
+              __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(par ? x0 : x1), 0xB1, 0xF, 0xF, false));
+          const float lo = par ? recv : x0, hi = par ? x1 : recv;  // columns cpair, cpair + 1
+          const int rb = 8 * (R0 >> 2) + 4 * (lane >> 5) + (R0 & 3) + par;
+          const int chunk = (cpair >> 3) ^ (rb & 7);
+          *reinterpret_cast<uint32_t*>(blk + rb * 128 + chunk * 16 + (cpair & 7) * 2) = pack_bf16x2(lo, hi);
         });
+      });
+      __builtin_amdgcn_wave_barrier();
+      static_for<4>([&](auto Rr) {
+        const int rb = 8 * Rr + (lane >> 3), c = lane & 7;
+        const uint4 v = *reinterpret_cast<const uint4*>(blk + rb * 128 + ((c ^ (rb & 7)) * 16));
+        const int64_t row = m0 + wm * 128 + I * 32 + rb;
+        const int64_t col = n0 + wn * 128 + 64 * P + 8 * c;
+        *reinterpret_cast<uint4*>(a.out + row * a.d + col) = v;
       });
     }
   });

@@ -134,6 +134,17 @@ def test_chunk_size_invariance(monkeypatch, chunk):
     check(run_lib(h, w, y), ref, torch.float32, f"chunk {chunk}")
 
 
+@pytest.mark.parametrize("chunk", ["64", "512"])
+def test_chunk_modes_bf16(monkeypatch, chunk):
+    """The matrix engine's dW accumulation modes on interior 256x256 tiles: 64-row
+    chunks give a first, three middle and a last chunk; 512 rows a single chunk."""
+    wl, inp = _case(300, 256, 1500, "bf16", sigma_w=0.1, seed=25)
+    monkeypatch.setenv("FLCE_CHUNK_ROWS", chunk)
+    p = flce.flce_plan_info(300, 256, 1500, flce.FLCE_BF16, 1)
+    assert p["num_chunks"] == (5 if chunk == "64" else 1)
+    _parity(wl, inp, f"bf16 chunk {chunk}")
+
+
 def test_ignored_rows_exact_zero_and_isolation():
     wl, (h, w, y) = _case(200, 128, 1200, "bf16", sigma_w=0.1, ignore_frac=0.25, seed=21)
     loss, lse, dh, dw = run_lib(h, w, y)
