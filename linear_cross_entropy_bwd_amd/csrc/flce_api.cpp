@@ -20,6 +20,7 @@ constexpr size_t kAlign = 256;
 constexpr size_t kDefaultProbBudget = size_t(1) << 30;  // bytes for the chunk's [C, vp] buffer
 constexpr int64_t kVocabPad = 256;
 constexpr int64_t kMaxDim = int64_t(1) << 24;  // d <= 2^24, v <= 2^24 - 256
+constexpr int64_t kCus = 256;                   // compute units of an MI355X
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -72,15 +73,19 @@ int make_plan(int64_t n, int64_t d, int64_t v, int32_t dtype, int32_t with_bwd, 
   q.chunk = c;
   q.nchunks = (n + c - 1) / c;
   // dH = G.W has only ceil(C/256) x ceil(d/256) output tiles; split its
-  // vocabulary reduction until about 512 workgroups fill the 256 CUs, keeping
-  // at least 4096 vocabulary columns per split.
+  // vocabulary reduction until there is about one workgroup per CU (256 on
+  // MI355X; each needs a whole CU's LDS), keeping at least 4096 vocabulary
+  // columns per split.  Unsplit is best once the tiles alone fill the chip:
+  // splits add fp32 partials and a reduction pass.
   q.dh_splits = 1;
   if (q.engine == ENGINE_MFMA && with_bwd) {
     const int64_t tiles = ((q.chunk + 255) / 256) * ((d + 255) / 256);
-    int64_t s = (512 + tiles - 1) / tiles;
+    int64_t s = (kCus + tiles - 1) / tiles;
     const int64_t smax = q.vp / 4096;
     if (s > smax) s = smax;
     if (s > 8) s = 8;
+    s = env_i64("FLCE_DH_SPLITS", s);
+    if (s > q.vp / 64) s = q.vp / 64;  // every split keeps at least one 64-column stage
     q.dh_splits = s < 1 ? 1 : s;
   }
   q.dw_acc = (with_bwd && dtype == FLCE_BF16 && q.nchunks > 1) ? 1 : 0;
