@@ -7,8 +7,9 @@
 //
 // One 256x256 output tile per 256-thread block (4 waves, 2x2, 128x128 per
 // wave = 4x4 MFMA tiles of 32x32).  K advances 64 at a time.  Operand tiles
-// go from global memory straight into LDS with 16-byte direct loads (no
-// register staging) through a ring of five 32 KB operand-stage slots, so the
+// go from global memory straight into LDS with 16-byte loads (no register
+// staging; buffer loads inside the operands, direct global->LDS loads at
+// their edges) through a ring of five 32 KB operand-stage slots, so the
 // A operand is fetched two stages and the B operand one stage ahead of the
 // MFMAs (see tile_loop).  Tiles whose k index is contiguous in memory sit in
 // LDS as [256 rows][64 k] and feed the fragments with 16-byte reads; tiles
@@ -90,36 +91,31 @@ __device__ __forceinline__ void lane_load_offsets(int64_t ld, uint32_t (&off)[2]
 }
 
 // Loads I0 .. I0 + CNT - 1 of a wave's share of one operand-stage.
-// Interior stage: every load in bounds; uniform base + lane offset.  BUF
-// issues them as buffer loads: one descriptor per call whose base is the
-// wave's first row of the stage, the row step of load i as the scalar offset
-// and the lane's part as a 32-bit vector offset (lane and row offsets stay
-// below 2^31 for leading dimensions below 2^24, which the plan enforces).
-// That moves half of each lane's address from vector to scalar registers;
-// on gfx950 it measured faster for the logits and dH contractions and slower
-// for dW, whose operands are both strided.
-template <int I0, int CNT, bool KMAJ, bool BUF>
+// Interior stage: every load in bounds, issued as buffer loads: one
+// descriptor per call whose base is the wave's first row of the stage, the
+// row step of load i as the scalar offset and the lane's part as a 32-bit
+// vector offset (lane and row offsets stay below 2^31 for leading dimensions
+// below 2^24, which the plan enforces), so only 4 bytes of each lane's
+// address live in vector registers.
+template <int I0, int CNT, bool KMAJ>
 __device__ __forceinline__ void load_stage_fast(const Operand& op, int64_t mn0, int64_t k0, bf16_t* lds,
                                                 const uint32_t (&off)[2]) {
   const int w = wave_id();
-  if constexpr (BUF) {
-    const int64_t first = KMAJ ? (mn0 + 64 * w) * op.ld + k0 : (k0 + 16 * w) * op.ld + mn0;
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(op.ptr + first), 0, 0x7fffffff, 0x00020000);
-    const uint32_t row_bytes = static_cast<uint32_t>(op.ld) * 2u;
+  // the row offset is uniform; saying so keeps the descriptor in scalar
+  // registers (the compiler otherwise wraps each load in a waterfall loop)
+  const int64_t first0 = KMAJ ? (mn0 + 64 * w) * op.ld + k0 : (k0 + 16 * w) * op.ld + mn0;
+  const uint64_t fu = static_cast<uint64_t>(first0);
+  const int64_t first = static_cast<int64_t>(
+      (static_cast<uint64_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(fu >> 32))) << 32) |
+      static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(fu))));
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(op.ptr + first), 0, 0x7fffffff, 0x00020000);
+  const uint32_t row_bytes = static_cast<uint32_t>(op.ld) * 2u;
 #pragma unroll
-    for (int i = I0; i < I0 + CNT; ++i) {
-      const uint32_t soff = static_cast<uint32_t>(KMAJ ? 8 * i : 2 * i) * row_bytes;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, FLCE_LDS(lds + (w * kLoadsPerStage + i) * 512), 16, off[i & 1],
-                                               soff, 0, 0);
-    }
-  } else {
-#pragma unroll
-    for (int i = I0; i < I0 + CNT; ++i) {
-      const int64_t row0 = KMAJ ? (mn0 + 64 * w + 8 * i) * op.ld + k0 : (k0 + 16 * w + 2 * i) * op.ld + mn0;
-      const char* base = reinterpret_cast<const char*>(op.ptr + row0);
-      __builtin_amdgcn_global_load_lds(base + off[i & 1], FLCE_LDS(lds + (w * kLoadsPerStage + i) * 512), 16, 0, 0);
-    }
+  for (int i = I0; i < I0 + CNT; ++i) {
+    const uint32_t soff = static_cast<uint32_t>(KMAJ ? 8 * i : 2 * i) * row_bytes;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, FLCE_LDS(lds + (w * kLoadsPerStage + i) * 512), 16, off[i & 1], soff,
+                                             0, 0);
   }
 }
 
@@ -150,12 +146,12 @@ __device__ __forceinline__ void load_stage_edge(const Operand& op, int64_t mn0, 
   }
 }
 
-template <int I0, int CNT, bool KMAJ, bool BUF>
+template <int I0, int CNT, bool KMAJ>
 __device__ __forceinline__ void load_stage(const Operand& op, int64_t mn0, int64_t k0, bf16_t* lds,
                                            const uint32_t (&off)[2]) {
   const bool interior = mn0 + TM <= op.mn_bound && k0 + TK <= op.k_bound;
   if (interior)
-    load_stage_fast<I0, CNT, KMAJ, BUF>(op, mn0, k0, lds, off);
+    load_stage_fast<I0, CNT, KMAJ>(op, mn0, k0, lds, off);
   else
     load_stage_edge<I0, CNT, KMAJ>(op, mn0, k0, lds);
 }
@@ -326,7 +322,7 @@ __device__ __forceinline__ void interleave_hint() {
 // So A is fetched two stages and B one stage ahead of its use.  Stages past
 // the end load zeros and are never consumed, so every iteration issues the
 // same loads and the waits are constants.
-template <bool A_KMAJ, bool B_KMAJ, bool BUF>
+template <bool A_KMAJ, bool B_KMAJ>
 __device__ __forceinline__ void tile_loop(const Operand& A, const Operand& B, int64_t m0, int64_t n0, int64_t k_lo,
                                           int64_t k_hi, Acc& acc) {
   bf16_t (*lds)[kStageElems] = ring();
@@ -367,9 +363,9 @@ __device__ __forceinline__ void tile_loop(const Operand& A, const Operand& B, in
   auto next = [](int s, int d) { return s + d >= kSlots ? s + d - kSlots : s + d; };
 
   // Prologue: A_0, B_0, A_1 in flight; wait for A_0 and B_0.
-  load_stage<0, kLoadsPerStage, A_KMAJ, BUF>(A, m0, k_of(0), lds[0], offa);
-  load_stage<0, kLoadsPerStage, B_KMAJ, BUF>(B, n0, k_of(0), lds[1], offb);
-  load_stage<0, kLoadsPerStage, A_KMAJ, BUF>(A, m0, k_of(1), lds[2], offa);
+  load_stage<0, kLoadsPerStage, A_KMAJ>(A, m0, k_of(0), lds[0], offa);
+  load_stage<0, kLoadsPerStage, B_KMAJ>(B, n0, k_of(0), lds[1], offb);
+  load_stage<0, kLoadsPerStage, A_KMAJ>(A, m0, k_of(1), lds[2], offa);
   wait_stages(1);
   stage_barrier();
 
@@ -388,15 +384,15 @@ __device__ __forceinline__ void tile_loop(const Operand& A, const Operand& B, in
     const int64_t kb = k_of(j + 1), ka = k_of(j + 2);
     auto load_b = [&](auto i0) {
       if constexpr (kFast)
-        load_stage_fast<decltype(i0)::value, 4, B_KMAJ, BUF>(B, n0, kb, slot_b, offb);
+        load_stage_fast<decltype(i0)::value, 4, B_KMAJ>(B, n0, kb, slot_b, offb);
       else
-        load_stage<decltype(i0)::value, 4, B_KMAJ, BUF>(B, n0, kb, slot_b, offb);
+        load_stage<decltype(i0)::value, 4, B_KMAJ>(B, n0, kb, slot_b, offb);
     };
     auto load_a = [&](auto i0) {
       if constexpr (kFast)
-        load_stage_fast<decltype(i0)::value, 4, A_KMAJ, BUF>(A, m0, ka, slot_a, offa);
+        load_stage_fast<decltype(i0)::value, 4, A_KMAJ>(A, m0, ka, slot_a, offa);
       else
-        load_stage<decltype(i0)::value, 4, A_KMAJ, BUF>(A, m0, ka, slot_a, offa);
+        load_stage<decltype(i0)::value, 4, A_KMAJ>(A, m0, ka, slot_a, offa);
     };
     if constexpr (!kFirst) wait_frags<A_KMAJ, B_KMAJ>(f1);
     read(sa, sb, std::integral_constant<int, 0>{}, f0);
@@ -467,7 +463,7 @@ __global__ __launch_bounds__(kThreads) void mfma_logits_kernel(LogitsArgs a) {
   tile_coords(t, a.tiles_m, a.tiles_n, a.group_m, tm, tn);
   const int64_t m0 = tm * TM, n0 = tn * TN;
   Acc acc;
-  tile_loop<true, true, true>(a.w, a.h, m0, n0, 0, a.w.k_bound, acc);
+  tile_loop<true, true>(a.w, a.h, m0, n0, 0, a.w.k_bound, acc);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -569,7 +565,7 @@ __global__ __launch_bounds__(kThreads) void mfma_dh_kernel(DhArgs a) {
   const int64_t k_lo = sp * a.k_split;
   const int64_t k_hi = k_lo + a.k_split < a.g.k_bound ? k_lo + a.k_split : a.g.k_bound;
   Acc acc;
-  tile_loop<true, false, true>(a.g, a.w, m0, n0, k_lo, k_hi, acc);
+  tile_loop<true, false>(a.g, a.w, m0, n0, k_lo, k_hi, acc);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -727,7 +723,7 @@ __global__ __launch_bounds__(kThreads) void mfma_dw_kernel(DwArgs a) {
   tile_coords(t, a.tiles_m, a.tiles_n, a.group_m, tm, tn);
   const int64_t m0 = tm * TM, n0 = tn * TN;
   Acc acc;
-  tile_loop<false, false, false>(a.gt, a.h, m0, n0, 0, a.gt.k_bound, acc);
+  tile_loop<false, false>(a.gt, a.h, m0, n0, 0, a.gt.k_bound, acc);
 
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int wm = wave >> 1, wn = wave & 1;
