@@ -23,7 +23,8 @@ METRIC = "fused linear-CE fwd+bwd tokens/s (N=8192,D=4096,V=128256 bf16); MFMA %
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}      # MI355X dense matrix peaks
 GEMM_KINDS = ("logits_lse", "dh_gemm", "dw_gemm")
 COPY_BYTES = 1 << 30
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dw_gemm_llama3_8b_head_traffic.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_llama3_8b_head_traffic.txt")
+TRAFFIC_KEYS = {"logits_lse": "logits", "dh_gemm": "dh", "dw_gemm": "dw"}
 ENGINE_SRC = os.path.join(ROOT, "linear_cross_entropy_bwd_amd", "csrc", "engine_mfma.hip")
 
 
@@ -31,7 +32,7 @@ def measured_traffic(kernel: str):
     """HBM bytes per launch of `kernel` from the committed counter summary, or None when
     there is none or the engine source changed since the counters were taken."""
     import hashlib
-    if not os.path.exists(TRAFFIC_FILE):
+    if not os.path.exists(TRAFFIC_FILE) or kernel not in TRAFFIC_KEYS:
         return None
     kv = {}
     for line in open(TRAFFIC_FILE):
@@ -39,10 +40,10 @@ def measured_traffic(kernel: str):
             k, v = line.split("=", 1)
             kv[k.strip()] = v.strip()
     digest = hashlib.sha256(open(ENGINE_SRC, "rb").read()).hexdigest()
-    if kv.get("engine_sha256") != digest or kv.get("kernel") != kernel:
+    if kv.get("engine_sha256") != digest:
         return None
     try:
-        return float(kv["traffic_bytes_per_launch"])
+        return float(kv[f"{TRAFFIC_KEYS[kernel]}_traffic_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
 
@@ -82,7 +83,8 @@ def main() -> int:
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the fused linear cross-entropy path here has no multi-GPU "
-              "mode (see DESIGN.md for how it would shard); run with --gpus 1", file=sys.stderr)
+              "mode (it would shard by tokens, with one all-reduce of dW, or by vocabulary rows, with an "
+              "all-gather of the per-token LSE partials); run with --gpus 1", file=sys.stderr)
         return 2
 
     import torch
