@@ -1,6 +1,8 @@
 """CPU oracle (test infrastructure only; never used by the product path)."""
 from .flce_oracle import (  # noqa: F401
     IGNORE_INDEX,
+    ce_on_logits,
+    flce_backward_from_lse,
     flce_forward,
     flce_forward_backward,
     flce_dw_rows,

@@ -21,6 +21,15 @@ written from the pages:
   ``dL/dH = (dL/dZ) . W`` and ``dL/dW = (dL/dZ)^T . H`` -- same page, section
   "2. In-Kernel Gradient Computation During the Backward Pass" (the softmax
   there carries a denominator that is identically 1 and is dropped here);
+* the backward from the saved per-token LSE alone, recomputing the tile
+  logits -- blog page, section "2. In-Kernel Gradient Computation During the
+  Backward Pass" (the forward keeps only the LSE; the backward recomputes the
+  logits and forms the softmax from it); the gradient of an upstream scalar
+  ``g . loss`` is ``g`` times the loss gradient;
+* cross-entropy on logits that are already materialised (the
+  ``LigerCrossEntropyLoss`` call of the lecture page and the "Chunked
+  CrossEntropy" row of the third page): the same LSE, target and gradient
+  formulas applied to a given ``[N, V]`` logits array;
 * ``reduction="mean"`` as in the loss module call on the lecture page
   ("GPU MODE lecture 028 - Liger Kernel", the LigerCrossEntropyLoss example);
   the mean is taken over the rows whose label is not ``ignore_index``, and a
@@ -213,3 +222,49 @@ def flce_dw_rows(h, w, labels, lse, vocab_rows, ignore_index: int = IGNORE_INDEX
         g *= scale
         out += g.T @ hb
     return out
+
+
+def flce_backward_from_lse(h, w, labels, lse, grad_out: float = 1.0, ignore_index: int = IGNORE_INDEX,
+                           reduction: str = "mean", block_rows: int = 1024):
+    """(dH[N, D], dW[V, D]) float64 of ``grad_out * loss`` from the saved per-row LSE.
+
+    The logits are recomputed block by block and the softmax is formed as
+    exp(z - lse) from the LSE handed in, as the backward pass of the blog page
+    does; with the forward's LSE this equals ``flce_forward_backward``'s
+    gradients times ``grad_out``.
+    """
+    hd, wd, y = _as_f64(h), _as_f64(w), _as_labels(labels)
+    n, d = hd.shape
+    v = wd.shape[0]
+    lse = np.asarray(lse, dtype=np.float64)
+    valid = valid_rows(y, v, ignore_index)
+    scale = float(grad_out) * reduction_scale(int(valid.sum()), reduction)
+    dh = np.zeros((n, d), dtype=np.float64)
+    dw = np.zeros((v, d), dtype=np.float64)
+    for r0 in range(0, n, block_rows):
+        r1 = min(n, r0 + block_rows)
+        z = hd[r0:r1] @ wd.T                       # recomputed logits block
+        g = np.exp(z - lse[r0:r1, None])           # softmax from the saved LSE
+        rows = np.flatnonzero(valid[r0:r1])
+        g[rows, y[r0 + rows]] -= 1.0
+        g[~valid[r0:r1]] = 0.0
+        g *= scale
+        dh[r0:r1] = g @ wd
+        dw += g.T @ hd[r0:r1]
+    return dh, dw
+
+
+def ce_on_logits(z, labels, ignore_index: int = IGNORE_INDEX, reduction: str = "mean"):
+    """Cross-entropy on given logits: (loss, lse[N], dL/dz[N, V]), float64."""
+    zd, y = _as_f64(z), _as_labels(labels)
+    n, v = zd.shape
+    valid = valid_rows(y, v, ignore_index)
+    scale = reduction_scale(int(valid.sum()), reduction)
+    lse = log_sum_exp(zd)
+    rows = np.flatnonzero(valid)
+    loss = scale * float(np.sum(lse[rows] - zd[rows, y[rows]]))
+    g = np.exp(zd - lse[:, None])
+    g[rows, y[rows]] -= 1.0
+    g[~valid] = 0.0
+    g *= scale
+    return loss, lse, g

@@ -17,7 +17,8 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import flce_dw_rows, flce_forward, flce_forward_backward, flce_rows, log_sum_exp
+from oracle import (ce_on_logits, flce_backward_from_lse, flce_dw_rows, flce_forward, flce_forward_backward, flce_rows,
+                    log_sum_exp)
 
 RTOL = 1e-12
 
@@ -350,3 +351,94 @@ def test_dw_rows_and_threaded_forward_match_full(reduction):
     _close(lse2, lse)
     cols = [0, 5, 39, 17]
     _close(flce_dw_rows(h, w, y, lse2, cols, reduction=reduction, block_rows=11), dw[cols])
+
+
+# --- backward from the saved LSE (recompute) and CE on given logits ----------------
+
+@pytest.mark.parametrize("reduction", ["mean", "sum"])
+@pytest.mark.parametrize("shape", [(16, 8, 10), (33, 17, 64)])
+def test_backward_from_lse_torch_autograd(reduction, shape):
+    """Library routine: torch cross-entropy autograd (float64) with a non-unit upstream
+    gradient, against the backward formed from the forward's saved LSE."""
+    n, d, v = shape
+    h, w, y = _rand(40 + n, n, d, v, sigma_w=0.7, ignore=(1,))
+    _, lse = flce_forward(h, w, y, reduction=reduction)
+    g_up = -0.37
+    dh, dw = flce_backward_from_lse(h, w, y, lse, grad_out=g_up, reduction=reduction, block_rows=5)
+    ht = torch.tensor(h, requires_grad=True)
+    wt = torch.tensor(w, requires_grad=True)
+    lt = torch.nn.functional.cross_entropy(ht @ wt.T, torch.tensor(y), ignore_index=-100, reduction=reduction)
+    lt.backward(torch.tensor(g_up, dtype=torch.float64))
+    _close(dh, ht.grad.numpy())
+    _close(dw, wt.grad.numpy())
+
+
+def test_backward_from_lse_finite_differences():
+    """Central differences of grad_out * loss, every entry of dH and dW."""
+    n, d, v = 3, 2, 4
+    h, w, y = _rand(44, n, d, v, sigma_w=0.9)
+    _, lse = flce_forward(h, w, y)
+    g_up, eps = 2.5, 1e-6
+    dh, dw = flce_backward_from_lse(h, w, y, lse, grad_out=g_up)
+
+    def f(hh, ww):
+        return g_up * flce_forward(hh, ww, y)[0]
+
+    for i in range(n):
+        for k in range(d):
+            hp, hm = h.copy(), h.copy()
+            hp[i, k] += eps
+            hm[i, k] -= eps
+            assert dh[i, k] == pytest.approx((f(hp, w) - f(hm, w)) / (2 * eps), rel=1e-6, abs=1e-9)
+    for j in range(v):
+        for k in range(d):
+            wp, wm = w.copy(), w.copy()
+            wp[j, k] += eps
+            wm[j, k] -= eps
+            assert dw[j, k] == pytest.approx((f(h, wp) - f(h, wm)) / (2 * eps), rel=1e-6, abs=1e-9)
+
+
+def test_backward_from_lse_uses_the_given_lse():
+    """Closed form: with lse + c the softmax part scales by exp(-c) and the one-hot part
+    does not, so dH(lse + c) - exp(-c) dH(lse) = (exp(-c) - 1) * scale * W[y] row by row
+    (from dH = scale (P W - W[y]))."""
+    n, d, v = 6, 4, 9
+    h, w, y = _rand(45, n, d, v, ignore=(3,))
+    _, lse = flce_forward(h, w, y)
+    c = 0.75
+    dh0, _ = flce_backward_from_lse(h, w, y, lse)
+    dh1, _ = flce_backward_from_lse(h, w, y, lse + c)
+    valid = y != -100
+    onehot_w = np.zeros((n, d))
+    onehot_w[valid] = w[y[valid]]
+    _close(dh1 - math.exp(-c) * dh0, (math.exp(-c) - 1.0) * onehot_w / valid.sum())
+
+
+@pytest.mark.parametrize("reduction", ["mean", "sum"])
+def test_ce_on_logits_torch(reduction):
+    """Library routine: torch cross-entropy on the same logits (float64)."""
+    g = np.random.default_rng(46)
+    z = 3.0 * g.standard_normal((21, 37))
+    y = g.integers(0, 37, 21).astype(np.int64)
+    y[[0, 7]] = -100
+    loss, lse, grad = ce_on_logits(z, y, reduction=reduction)
+    zt = torch.tensor(z, requires_grad=True)
+    lt = torch.nn.functional.cross_entropy(zt, torch.tensor(y), ignore_index=-100, reduction=reduction)
+    lt.backward()
+    assert loss == pytest.approx(lt.item(), rel=1e-12)
+    _close(lse, torch.logsumexp(zt.detach(), dim=1).numpy())
+    _close(grad, zt.grad.numpy())
+
+
+def test_ce_on_logits_uniform_closed_form():
+    """Equal logits: loss = log V, gradient (1/V - onehot)/n_valid, LSE = z0 + log V."""
+    n, v = 5, 8
+    z = np.full((n, v), 1.25)
+    y = np.array([0, 3, -100, 7, 7], dtype=np.int64)
+    loss, lse, grad = ce_on_logits(z, y)
+    assert loss == pytest.approx(math.log(v), rel=1e-14)
+    _close(lse, np.full(n, 1.25 + math.log(v)))
+    ref = np.full((n, v), 1.0 / v)
+    ref[[0, 1, 3, 4], [0, 3, 7, 7]] -= 1.0
+    ref[2] = 0.0
+    _close(grad, ref / 4.0)
