@@ -117,8 +117,33 @@ int flce_fwd(const void* h, const void* w, const int64_t* labels,
              float* loss_out, float* lse_out, hipStream_t stream);
 
 /*
+ * Backward pass from the saved per-token LSE, recomputing the logits: the
+ * backward of the blog page "Liger Kernel: Fused Triton Kernels for LLM
+ * Training", section "2. In-Kernel Gradient Computation During the Backward
+ * Pass" (the forward keeps only the LSE; the backward recomputes the tile
+ * logits and forms softmax - one-hot from it).  Together with flce_fwd it
+ * splits flce_fwd_bwd into the forward and backward halves an autograd
+ * function needs, at 8 N D V flop instead of 6.
+ *
+ *   lse       device, [n] fp32: the LSE flce_fwd (or flce_fwd_bwd) returned
+ *             for these h, w; read only.
+ *   grad_out  device, one fp32: the upstream gradient of the loss (the
+ *             scalar autograd passes to the loss's backward), or NULL for 1.
+ *             Read by the kernels, so no host synchronisation is needed.
+ *   dh_out    device, [n, d] in dtype: overwritten with grad_out * dloss/dH.
+ *   dw_out    device, [v, d] in dtype: overwritten with grad_out * dloss/dW.
+ * Other arguments, layouts, ownership, stream semantics and error codes as
+ * for flce_fwd_bwd.  h, w, labels and ignore_index/reduction must be those
+ * of the forward call; a different lse gives the gradient of a different
+ * function, which is not checked.
+ */
+int flce_bwd(const void* h, const void* w, const int64_t* labels, const float* lse, const float* grad_out,
+             int64_t n, int64_t d, int64_t v, flce_dtype dtype, int64_t ignore_index, flce_reduction reduction,
+             void* dh_out, void* dw_out, hipStream_t stream);
+
+/*
  * Bytes of device workspace one call allocates (with_bwd = 1 for
- * flce_fwd_bwd, 0 for flce_fwd); 0 for invalid sizes.  Honours the
+ * flce_fwd_bwd and flce_bwd, 0 for flce_fwd); 0 for invalid sizes.  Honours the
  * FLCE_CHUNK_ROWS and FLCE_WORKSPACE_CAP_BYTES environment overrides exactly
  * as the calls do.
  */

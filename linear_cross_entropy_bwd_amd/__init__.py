@@ -25,6 +25,7 @@ ENGINE_MFMA, ENGINE_FMA = 0, 1
 EXPORTED = (
     "flce_fwd_bwd",
     "flce_fwd",
+    "flce_bwd",
     "flce_workspace_bytes",
     "flce_plan_info",
     "flce_strerror",
@@ -74,6 +75,8 @@ def lib() -> ctypes.CDLL:
     L.flce_fwd_bwd.restype = i32
     L.flce_fwd.argtypes = [p, p, p, i64, i64, i64, i32, i64, i32, p, p, p]
     L.flce_fwd.restype = i32
+    L.flce_bwd.argtypes = [p, p, p, p, p, i64, i64, i64, i32, i64, i32, p, p, p]
+    L.flce_bwd.restype = i32
     L.flce_workspace_bytes.argtypes = [i64, i64, i64, i32, i32]
     L.flce_workspace_bytes.restype = ctypes.c_size_t
     L.flce_plan_info.argtypes = [i64, i64, i64, i32, i32, ctypes.POINTER(PlanInfo)]
@@ -127,6 +130,11 @@ def flce_fwd_bwd(h, w, labels, n, d, v, dtype, ignore_index, reduction, loss_out
 def flce_fwd(h, w, labels, n, d, v, dtype, ignore_index, reduction, loss_out, lse_out, stream) -> int:
     return lib().flce_fwd(_ptr(h), _ptr(w), _ptr(labels), n, d, v, dtype, ignore_index, reduction,
                           _ptr(loss_out), _ptr(lse_out), _stream(stream))
+
+
+def flce_bwd(h, w, labels, lse, grad_out, n, d, v, dtype, ignore_index, reduction, dh_out, dw_out, stream) -> int:
+    return lib().flce_bwd(_ptr(h), _ptr(w), _ptr(labels), _ptr(lse), _ptr(grad_out), n, d, v, dtype, ignore_index,
+                          reduction, _ptr(dh_out), _ptr(dw_out), _stream(stream))
 
 
 def flce_workspace_bytes(n, d, v, dtype, with_bwd) -> int:
@@ -246,3 +254,27 @@ def linear_cross_entropy_forward(h, w, labels, ignore_index: int = -100, reducti
     if st != FLCE_OK:
         raise FlceError(st, "flce_fwd")
     return loss, lse
+
+
+def linear_cross_entropy_backward(h, w, labels, lse, grad_out=None, ignore_index: int = -100, reduction: str = "mean",
+                                  out=None):
+    """dH and dW of ``grad_out * loss`` from the saved per-row LSE, recomputing the logits (flce_bwd).
+
+    ``lse`` is the fp32 [n] tensor the forward returned; ``grad_out`` a one-element
+    fp32 device tensor (the upstream gradient) or None for 1.  ``out`` may supply
+    preallocated (dh, dw).
+    """
+    import torch
+    _check_inputs(h, w, labels)
+    n, d = h.shape
+    v = w.shape[0]
+    if lse.dtype != torch.float32 or lse.shape != (n,) or not lse.is_contiguous() or not lse.is_cuda:
+        raise ValueError("lse must be a contiguous fp32 [n] device tensor")
+    if grad_out is not None and (grad_out.dtype != torch.float32 or grad_out.numel() != 1 or not grad_out.is_cuda):
+        raise ValueError("grad_out must be a one-element fp32 device tensor")
+    dh, dw = (torch.empty_like(h), torch.empty_like(w)) if out is None else out
+    st = flce_bwd(h, w, labels, lse, grad_out, n, d, v, _dtype_code(h), ignore_index, _red_code(reduction), dh, dw,
+                  torch.cuda.current_stream(h.device))
+    if st != FLCE_OK:
+        raise FlceError(st, "flce_bwd")
+    return dh, dw

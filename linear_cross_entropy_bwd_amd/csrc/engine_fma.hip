@@ -90,18 +90,45 @@ struct TileLoop {
 // Logits tile (rows = chunk tokens, cols = vocabulary): per-row max and
 // sum-exp over the tile's 64 columns (one vocabulary group), the target
 // logit, and optionally exp(z - group max) into the chunk's buffer.
+// Recompute mode (lse_in != nullptr, the backward from the saved LSE): the
+// buffer gets G = (exp(z - lse) - [j = y]) * scale directly, scale = upstream
+// gradient times 1/n_valid (mean) or 1 (sum), 0 for ignored rows.
 template <typename T>
 __global__ __launch_bounds__(256) void fma_logits_kernel(const T* __restrict__ H, const T* __restrict__ W,
                                                          int64_t rows, int64_t d, int64_t v, int64_t vp,
                                                          const int64_t* __restrict__ labels, float* __restrict__ zy,
                                                          float* __restrict__ pm, float* __restrict__ ps, int64_t C,
-                                                         float* __restrict__ prob) {
+                                                         float* __restrict__ prob, const float* __restrict__ lse_in,
+                                                         const float* __restrict__ grad_out,
+                                                         const int32_t* __restrict__ nvalid, int32_t reduction,
+                                                         int64_t ignore_index) {
   const int64_t m0 = static_cast<int64_t>(blockIdx.x) * BM;
   const int64_t n0 = static_cast<int64_t>(blockIdx.y) * BN;
   float acc[4][4];
   TileLoop<T, T, true, true>::run(H, d, W, d, rows, v, d, m0, n0, acc);
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
   const int64_t g = blockIdx.y;
+  if (lse_in != nullptr) {
+    const float go = grad_out != nullptr ? *grad_out : 1.0f;
+    const int32_t nv = *nvalid;
+    const float red = reduction == FLCE_SUM ? 1.0f : (nv > 0 ? 1.0f / static_cast<float>(nv) : 0.0f);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t t = m0 + ty * 4 + i;
+      if (t >= rows) continue;
+      const int64_t y = labels[t];
+      const float sc = y != ignore_index ? go * red : 0.0f;
+      const float l = lse_in[t];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t n = n0 + tx * 4 + j;
+        if (n >= vp) continue;
+        const float gv = n < v ? (expf(acc[i][j] - l) - (n == y ? 1.0f : 0.0f)) * sc : 0.0f;
+        prob[t * vp + n] = gv;
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int64_t t = m0 + ty * 4 + i;
@@ -184,12 +211,15 @@ inline dim3 grid2(int64_t m, int64_t n) {
 
 }  // namespace
 
-hipError_t fma_logits(const Plan& p, const Work& w, const ChunkArgs& a, int store_prob, hipStream_t s) {
+hipError_t fma_logits(const Plan& p, const Work& w, const ChunkArgs& a, int mode, hipStream_t s) {
   if (p.dtype != FLCE_F32) return hipErrorInvalidValue;
-  float* prob = store_prob ? static_cast<float*>(w.prob) : nullptr;
-  fma_logits_kernel<float><<<grid2(a.rows, p.v), 256, 0, s>>>(static_cast<const float*>(a.h),
-                                                             static_cast<const float*>(a.w), a.rows, p.d, p.v, p.vp,
-                                                             a.labels, w.zy, w.pm, w.ps, p.chunk, prob);
+  float* prob = mode != LOGITS_STATS ? static_cast<float*>(w.prob) : nullptr;
+  const float* lse_in = mode == LOGITS_GRAD_FROM_LSE ? a.lse_in : nullptr;
+  // the grid spans the buffer's padded columns so that recompute mode clears them
+  const int64_t cols = mode == LOGITS_GRAD_FROM_LSE ? p.vp : p.v;
+  fma_logits_kernel<float><<<grid2(a.rows, cols), 256, 0, s>>>(
+      static_cast<const float*>(a.h), static_cast<const float*>(a.w), a.rows, p.d, p.v, p.vp, a.labels, w.zy, w.pm,
+      w.ps, p.chunk, prob, lse_in, a.grad_out, w.nvalid, a.reduction, a.ignore_index);
   return hipGetLastError();
 }
 

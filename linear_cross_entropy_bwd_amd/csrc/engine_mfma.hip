@@ -454,8 +454,76 @@ struct LogitsArgs {
   float* ps;
   bf16_t* prob;  // nullptr: statistics only
   int64_t tiles_m, tiles_n, group_m;
+  // recompute mode (backward from the saved LSE): G straight from the logits
+  const float* lse_in;    // chunk rows' saved LSE
+  const float* grad_out;  // upstream gradient of the loss (device scalar) or nullptr for 1
+  const int32_t* nvalid;
+  int32_t reduction;
+  int64_t ignore_index;
 };
 
+// Recompute-mode epilogue of one wave's 128 vocabulary rows x 128 tokens:
+// G = (exp(z - lse) - [j = y]) * scale from the recomputed logits and the
+// saved LSE (the backward of the blog's section "2. In-Kernel Gradient
+// Computation During the Backward Pass"), scale = upstream gradient times
+// 1/n_valid (mean) or 1 (sum), 0 for ignored rows.  G leaves through the
+// wave's LDS scratch as whole token rows; the target column's value is
+// computed in fp32 and written over its staged slot.
+template <bool FULL>
+__device__ __forceinline__ void logits_grad_epilogue(const LogitsArgs& a, Acc& acc, int64_t n0, int64_t vbase, int wn,
+                                                     int wave, int lane) {
+  const int half = lane >> 5;
+  const float go = a.grad_out != nullptr ? *a.grad_out : 1.0f;
+  const int32_t nv = *a.nvalid;
+  const float red = a.reduction == FLCE_SUM ? 1.0f : (nv > 0 ? 1.0f / static_cast<float>(nv) : 0.0f);
+  auto in_vocab = [&](int r_row) { return FULL || vbase + r_row < a.v; };
+  static_for<4>([&](auto J) {
+    const int64_t tok = n0 + wn * 128 + J * 32 + (lane & 31);
+    const bool live = tok < a.rows;
+    char* stage = reinterpret_cast<char*>(ring()[J]) + kWaveScratchBytes * wave;
+    const int64_t lab = live ? a.labels[tok] : a.ignore_index;
+    const bool valid = live && lab != a.ignore_index;
+    const float sc = valid ? go * red : 0.0f;
+    const float l2 = live ? a.lse_in[tok] * kLog2e : 0.0f;
+    const int t = lane & 31;
+    static_for<4>([&](auto I) {
+      static_for<4>([&](auto Q) {
+        float e[4];
+        static_for<4>([&](auto U) {
+          constexpr int r = Q * 4 + U;
+          e[U] = in_vocab(acc_row(I, r, lane)) ? __builtin_amdgcn_exp2f(fmaf(acc.c[I][J][r], kLog2e, -l2)) * sc : 0.0f;
+        });
+        const int chunk = (I * 4 + Q) ^ (t & 15);
+        uint2 pk;
+        pk.x = pack_bf16x2(e[0], e[1]);
+        pk.y = pack_bf16x2(e[2], e[3]);
+        *reinterpret_cast<uint2*>(stage + t * 256 + chunk * 16 + 8 * half) = pk;
+      });
+    });
+    const int64_t q = lab - vbase;
+    const int o = static_cast<int>(q & 31);
+    if (valid && lab >= 0 && lab < a.v && q >= 0 && q < 128 && ((o >> 2) & 1) == half) {
+      const int it = static_cast<int>(q >> 5);
+      const int rt = (o >> 3) * 4 + (o & 3);
+      float z = 0.0f;
+      static_for<4>([&](auto I) {
+        static_for<16>([&](auto R) { z = (I == it && R == rt) ? acc.c[I][J][R.value] : z; });
+      });
+      const float gt = (__builtin_amdgcn_exp2f(fmaf(z, kLog2e, -l2)) - 1.0f) * sc;
+      const int qc = static_cast<int>(q);
+      *reinterpret_cast<bf16_t*>(stage + t * 256 + (((qc >> 3) ^ (t & 15)) * 16) + (qc & 7) * 2) = f32_to_bf16(gt);
+    }
+    __builtin_amdgcn_wave_barrier();
+    static_for<8>([&](auto Rr) {
+      const int tr = 4 * Rr + (lane >> 4), c = lane & 15;
+      const uint4 val = *reinterpret_cast<const uint4*>(stage + tr * 256 + ((c ^ (tr & 15)) * 16));
+      const int64_t tk = n0 + wn * 128 + J * 32 + tr;
+      if (tk < a.rows) *reinterpret_cast<uint4*>(a.prob + tk * a.vp + vbase + 8 * c) = val;
+    });
+  });
+}
+
+template <bool RECOMP>
 __global__ __launch_bounds__(kThreads) void mfma_logits_kernel(LogitsArgs a) {
   const int64_t nb = a.tiles_m * a.tiles_n;
   const int64_t t = xcd_remap(blockIdx.x, nb);
@@ -470,6 +538,13 @@ __global__ __launch_bounds__(kThreads) void mfma_logits_kernel(LogitsArgs a) {
   const int half = lane >> 5;
   const int64_t vbase = m0 + wm * 128;  // this wave's 128-wide vocabulary group
   const int64_t g = vbase / 128;
+  if constexpr (RECOMP) {
+    if (vbase + 128 <= a.v)
+      logits_grad_epilogue<true>(a, acc, n0, vbase, wn, wave, lane);
+    else
+      logits_grad_epilogue<false>(a, acc, n0, vbase, wn, wave, lane);
+    return;
+  }
   // FULL: every vocabulary row of the group exists (no per-element masks).
   auto epilogue = [&](auto FULL) {
     auto in_vocab = [&](int r_row) { return FULL || vbase + r_row < a.v; };
@@ -770,7 +845,7 @@ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 }  // namespace
 
-hipError_t mfma_logits(const Plan& p, const Work& w, const ChunkArgs& c, int store_prob, hipStream_t s) {
+hipError_t mfma_logits(const Plan& p, const Work& w, const ChunkArgs& c, int mode, hipStream_t s) {
   LogitsArgs a;
   a.w = Operand{static_cast<const bf16_t*>(c.w), p.d, p.v, p.d};
   a.h = Operand{static_cast<const bf16_t*>(c.h), p.d, c.rows, p.d};
@@ -782,11 +857,20 @@ hipError_t mfma_logits(const Plan& p, const Work& w, const ChunkArgs& c, int sto
   a.zy = w.zy;
   a.pm = w.pm;
   a.ps = w.ps;
-  a.prob = store_prob ? static_cast<bf16_t*>(w.prob) : nullptr;
+  a.prob = mode != LOGITS_STATS ? static_cast<bf16_t*>(w.prob) : nullptr;
   a.tiles_m = p.vp / TM;
   a.tiles_n = cdiv(c.rows, TN);
   a.group_m = p.group_m[0];
-  mfma_logits_kernel<<<static_cast<unsigned>(a.tiles_m * a.tiles_n), kThreads, 0, s>>>(a);
+  a.lse_in = c.lse_in;
+  a.grad_out = c.grad_out;
+  a.nvalid = w.nvalid;
+  a.reduction = c.reduction;
+  a.ignore_index = c.ignore_index;
+  const dim3 grid(static_cast<unsigned>(a.tiles_m * a.tiles_n));
+  if (mode == LOGITS_GRAD_FROM_LSE)
+    mfma_logits_kernel<true><<<grid, kThreads, 0, s>>>(a);
+  else
+    mfma_logits_kernel<false><<<grid, kThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 

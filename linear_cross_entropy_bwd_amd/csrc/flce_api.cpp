@@ -232,9 +232,12 @@ hipError_t run(const Plan& p, const Work& wk, const void* h, const void* w, cons
     a.dh = dh_out != nullptr ? static_cast<char*>(dh_out) + a.row0 * p.d * elem : nullptr;
     a.dw = dw_out;
     a.dw_mode = p.nchunks == 1 ? DW_SINGLE : (c == 0 ? DW_FIRST : (c == p.nchunks - 1 ? DW_LAST : DW_MID));
+    a.lse_in = nullptr;
+    a.grad_out = nullptr;
 
+    const int mode = p.with_bwd ? LOGITS_PROB : LOGITS_STATS;
     e = timed(K_LOGITS, s, [&] {
-      return p.engine == ENGINE_MFMA ? mfma_logits(p, wk, a, p.with_bwd, s) : fma_logits(p, wk, a, p.with_bwd, s);
+      return p.engine == ENGINE_MFMA ? mfma_logits(p, wk, a, mode, s) : fma_logits(p, wk, a, mode, s);
     });
     if (e != hipSuccess) return e;
     e = timed(K_LSE_MERGE, s, [&] { return launch_lse_merge(p, wk, a, p.with_bwd, s); });
@@ -254,6 +257,65 @@ hipError_t run(const Plan& p, const Work& wk, const void* h, const void* w, cons
   return timed(K_LOSS, s, [&] { return launch_loss_reduce(p, wk, reduction, loss_out, s); });
 }
 
+// The backward from the saved LSE (recompute): per chunk the logits are
+// recomputed and their epilogue writes G directly; then dH and dW as above.
+hipError_t run_bwd(const Plan& p, const Work& wk, const void* h, const void* w, const int64_t* labels,
+                   const float* lse, const float* grad_out, int64_t ignore_index, int32_t reduction, void* dh_out,
+                   void* dw_out, hipStream_t s) {
+  const int64_t elem = p.dtype == FLCE_BF16 ? 2 : 4;
+  hipError_t e = timed(K_LABEL_SCAN, s, [&] { return launch_label_scan(p, wk, labels, ignore_index, s); });
+  if (e != hipSuccess) return e;
+  for (int64_t c = 0; c < p.nchunks; ++c) {
+    ChunkArgs a;
+    a.row0 = c * p.chunk;
+    a.rows = p.n - a.row0 < p.chunk ? p.n - a.row0 : p.chunk;
+    a.h = static_cast<const char*>(h) + a.row0 * p.d * elem;
+    a.w = w;
+    a.labels = labels + a.row0;
+    a.ignore_index = ignore_index;
+    a.reduction = reduction;
+    a.lse_rows = nullptr;
+    a.dh = static_cast<char*>(dh_out) + a.row0 * p.d * elem;
+    a.dw = dw_out;
+    a.dw_mode = p.nchunks == 1 ? DW_SINGLE : (c == 0 ? DW_FIRST : (c == p.nchunks - 1 ? DW_LAST : DW_MID));
+    a.lse_in = lse + a.row0;
+    a.grad_out = grad_out;
+    e = timed(K_LOGITS, s, [&] {
+      return p.engine == ENGINE_MFMA ? mfma_logits(p, wk, a, LOGITS_GRAD_FROM_LSE, s)
+                                     : fma_logits(p, wk, a, LOGITS_GRAD_FROM_LSE, s);
+    });
+    if (e != hipSuccess) return e;
+    e = timed(K_DH, s, [&] { return p.engine == ENGINE_MFMA ? mfma_dh(p, wk, a, s) : fma_dh(p, wk, a, s); });
+    if (e != hipSuccess) return e;
+    if (p.dh_splits > 1) {
+      e = timed(K_DH_REDUCE, s, [&] { return launch_dh_reduce(p, wk, a, s); });
+      if (e != hipSuccess) return e;
+    }
+    e = timed(K_DW, s, [&] { return p.engine == ENGINE_MFMA ? mfma_dw(p, wk, a, s) : fma_dw(p, wk, a, s); });
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// Allocate the call's workspace from the device's pool, run `body`, free it.
+template <class Body>
+int with_workspace(const Plan& p, hipStream_t stream, Body&& body) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FLCE_ERR_HIP;
+  hipMemPool_t pool;
+  if (device_pool(dev, &pool) != hipSuccess) return FLCE_ERR_HIP;
+  void* base = nullptr;
+  if (hipMallocFromPoolAsync(&base, p.total, pool, stream) != hipSuccess || base == nullptr) {
+    (void)hipGetLastError();
+    return FLCE_ERR_OOM;
+  }
+  const Work wk = carve(p, static_cast<char*>(base));
+  hipError_t e = body(wk);
+  hipError_t f = hipFreeAsync(base, stream);
+  if (e != hipSuccess) return FLCE_ERR_HIP;
+  return status_of(f);
+}
+
 int call(const void* h, const void* w, const int64_t* labels, int64_t n, int64_t d, int64_t v, flce_dtype dtype,
          int64_t ignore_index, flce_reduction reduction, float* loss_out, float* lse_out, void* dh_out,
          void* dw_out, hipStream_t stream, int with_bwd) {
@@ -266,20 +328,26 @@ int call(const void* h, const void* w, const int64_t* labels, int64_t n, int64_t
   Plan p;
   st = make_plan(n, d, v, dtype, with_bwd, &p);
   if (st != FLCE_OK) return st;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return FLCE_ERR_HIP;
-  hipMemPool_t pool;
-  if (device_pool(dev, &pool) != hipSuccess) return FLCE_ERR_HIP;
-  void* base = nullptr;
-  if (hipMallocFromPoolAsync(&base, p.total, pool, stream) != hipSuccess || base == nullptr) {
-    (void)hipGetLastError();
-    return FLCE_ERR_OOM;
-  }
-  const Work wk = carve(p, static_cast<char*>(base));
-  hipError_t e = run(p, wk, h, w, labels, ignore_index, reduction, loss_out, lse_out, dh_out, dw_out, stream);
-  hipError_t f = hipFreeAsync(base, stream);
-  if (e != hipSuccess) return FLCE_ERR_HIP;
-  return status_of(f);
+  return with_workspace(p, stream, [&](const Work& wk) {
+    return run(p, wk, h, w, labels, ignore_index, reduction, loss_out, lse_out, dh_out, dw_out, stream);
+  });
+}
+
+int call_bwd(const void* h, const void* w, const int64_t* labels, const float* lse, const float* grad_out, int64_t n,
+             int64_t d, int64_t v, flce_dtype dtype, int64_t ignore_index, flce_reduction reduction, void* dh_out,
+             void* dw_out, hipStream_t stream) {
+  if (lse == nullptr || dh_out == nullptr || dw_out == nullptr) return FLCE_ERR_INVALID_ARG;
+  // check_common wants a loss pointer; the saved LSE stands in (same alignment rule)
+  int st = check_common(h, w, labels, n, d, v, dtype, reduction, lse, nullptr);
+  if (st != FLCE_OK) return st;
+  if (!aligned(dh_out, 16) || !aligned(dw_out, 16) || (grad_out != nullptr && !aligned(grad_out, 4)))
+    return FLCE_ERR_ALIGNMENT;
+  Plan p;
+  st = make_plan(n, d, v, dtype, 1, &p);
+  if (st != FLCE_OK) return st;
+  return with_workspace(p, stream, [&](const Work& wk) {
+    return run_bwd(p, wk, h, w, labels, lse, grad_out, ignore_index, reduction, dh_out, dw_out, stream);
+  });
 }
 
 }  // namespace
@@ -298,6 +366,12 @@ int flce_fwd(const void* h, const void* w, const int64_t* labels, int64_t n, int
              int64_t ignore_index, flce_reduction reduction, float* loss_out, float* lse_out, hipStream_t stream) {
   return flce::call(h, w, labels, n, d, v, dtype, ignore_index, reduction, loss_out, lse_out, nullptr, nullptr,
                     stream, 0);
+}
+
+int flce_bwd(const void* h, const void* w, const int64_t* labels, const float* lse, const float* grad_out, int64_t n,
+             int64_t d, int64_t v, flce_dtype dtype, int64_t ignore_index, flce_reduction reduction, void* dh_out,
+             void* dw_out, hipStream_t stream) {
+  return flce::call_bwd(h, w, labels, lse, grad_out, n, d, v, dtype, ignore_index, reduction, dh_out, dw_out, stream);
 }
 
 size_t flce_workspace_bytes(int64_t n, int64_t d, int64_t v, flce_dtype dtype, int with_bwd) {

@@ -69,6 +69,13 @@ enum Kind : int {
   K_NUM_KINDS = 8
 };
 
+// What the logits contraction's epilogue produces.
+enum LogitsMode : int32_t {
+  LOGITS_STATS = 0,          // per-group (max, sum-exp) partials and the target logit
+  LOGITS_PROB = 1,           // ... and exp(z - group max) into the chunk's buffer
+  LOGITS_GRAD_FROM_LSE = 2   // the gradient G itself, from the saved per-row LSE (recompute backward)
+};
+
 // --- per-chunk launch arguments --------------------------------------------------
 
 struct ChunkArgs {
@@ -83,6 +90,8 @@ struct ChunkArgs {
   void* dh;                 // chunk's first row of dH output
   void* dw;                 // dW output
   int32_t dw_mode;
+  const float* lse_in;      // chunk's slice of the saved LSE (recompute backward), else nullptr
+  const float* grad_out;    // upstream gradient of the loss (device scalar) or nullptr for 1
 };
 
 // --- launchers (each returns the launch status) ---------------------------------
@@ -96,12 +105,12 @@ hipError_t launch_loss_reduce(const Plan& p, const Work& w, int32_t reduction, f
 hipError_t launch_dh_reduce(const Plan& p, const Work& w, const ChunkArgs& a, hipStream_t s);
 
 // fp32 FMA engine (engine_fma.hip): FLCE_F32 (dw_out itself accumulates).
-hipError_t fma_logits(const Plan& p, const Work& w, const ChunkArgs& a, int store_prob, hipStream_t s);
+hipError_t fma_logits(const Plan& p, const Work& w, const ChunkArgs& a, int mode, hipStream_t s);
 hipError_t fma_dh(const Plan& p, const Work& w, const ChunkArgs& a, hipStream_t s);
 hipError_t fma_dw(const Plan& p, const Work& w, const ChunkArgs& a, hipStream_t s);
 
 // bf16 matrix-core engine (engine_mfma.hip): FLCE_BF16.
-hipError_t mfma_logits(const Plan& p, const Work& w, const ChunkArgs& a, int store_prob, hipStream_t s);
+hipError_t mfma_logits(const Plan& p, const Work& w, const ChunkArgs& a, int mode, hipStream_t s);
 hipError_t mfma_dh(const Plan& p, const Work& w, const ChunkArgs& a, hipStream_t s);
 hipError_t mfma_dw(const Plan& p, const Work& w, const ChunkArgs& a, hipStream_t s);
 

@@ -112,6 +112,28 @@ def test_argument_errors_before_any_device_work():
     assert flce.flce_fwd(None, A, A, 4, 8, 16, flce.FLCE_F32, -100, 0, A, None, None) == flce.FLCE_ERR_INVALID_ARG
 
 
+def test_bwd_argument_errors_before_any_device_work():
+    A = 1 << 20  # fake, 16-byte aligned addresses: never dereferenced
+    ok = dict(h=A, w=A, labels=A, lse=A, grad_out=None, n=4, d=8, v=16, dtype=flce.FLCE_F32, ignore_index=-100,
+              reduction=flce.FLCE_MEAN, dh_out=A, dw_out=A, stream=None)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return flce.flce_bwd(**a)
+
+    assert call(lse=None) == flce.FLCE_ERR_INVALID_ARG
+    assert call(h=None) == flce.FLCE_ERR_INVALID_ARG
+    assert call(dh_out=None) == flce.FLCE_ERR_INVALID_ARG
+    assert call(dw_out=None) == flce.FLCE_ERR_INVALID_ARG
+    assert call(v=0) == flce.FLCE_ERR_INVALID_ARG
+    assert call(reduction=7) == flce.FLCE_ERR_INVALID_ARG
+    assert call(lse=A + 2) == flce.FLCE_ERR_ALIGNMENT
+    assert call(grad_out=A + 2) == flce.FLCE_ERR_ALIGNMENT
+    assert call(dh_out=A + 4) == flce.FLCE_ERR_ALIGNMENT
+    assert call(d=6) == flce.FLCE_ERR_ALIGNMENT
+
+
 def test_no_cpu_fallback(monkeypatch, tmp_path):
     """Without the built library the binding raises instead of computing anything."""
     monkeypatch.setattr(flce, "_lib", None)

@@ -1,0 +1,110 @@
+"""Parity of the backward from the saved LSE (flce_bwd, recompute) and of its
+autograd wrapper.
+
+The saved LSE fed to flce_bwd comes from the oracle (fp64, rounded to fp32),
+so the expected gradients are the oracle's backward from that same LSE.  The
+end-to-end tests run the library's forward and then its backward and compare
+with the oracle's forward-backward gradients times the upstream gradient.
+"""
+import numpy as np
+import pytest
+import torch
+
+import linear_cross_entropy_bwd_amd as flce
+from linear_cross_entropy_bwd_amd.autograd import LinearCrossEntropyLoss
+from oracle import flce_backward_from_lse, flce_forward, flce_forward_backward
+from workloads import Workload, make_inputs
+
+from gpu_helpers import TOL, rel_max, say, to_f64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _case(n, d, v, dtype, sigma_w=0.1, ignore_frac=0.1, reduction="mean", seed=0):
+    wl = Workload(f"bwd_{n}_{d}_{v}", n, d, v, dtype, sigma_w, "uniform", ignore_frac, reduction, seed=seed)
+    return wl, make_inputs(wl, threads=4)
+
+
+def _check_grads(dh, dw, rdh, rdw, dtype, what):
+    tol = TOL[dtype]["grad"]
+    e = dict(dh=rel_max(dh, rdh), dw=rel_max(dw, rdw))
+    say(f"  {what} errors {e}")
+    assert np.all(np.isfinite(dh)) and np.all(np.isfinite(dw))
+    assert e["dh"] <= tol, f"{what} dH"
+    assert e["dw"] <= tol, f"{what} dW"
+
+
+CASES = [
+    ((64, 72, 300), "f32", "mean"),
+    ((37, 72, 1001), "bf16", "mean"),
+    ((37, 72, 1001), "f32", "sum"),
+    ((513, 520, 2100), "bf16", "mean"),
+    ((300, 256, 20000), "bf16", "sum"),     # dH splits its vocabulary reduction
+]
+
+
+@pytest.mark.parametrize("shape,dtype,reduction", CASES)
+def test_bwd_from_oracle_lse(shape, dtype, reduction):
+    n, d, v = shape
+    wl, (h, w, y) = _case(n, d, v, dtype, reduction=reduction, seed=30 + n)
+    say(f"[bwd] from oracle lse: n={n} d={d} v={v} {dtype} {reduction}")
+    _, lse64 = flce_forward(h, w, y, reduction=reduction)
+    lse32 = torch.from_numpy(lse64.astype(np.float32))
+    g_up = 0.75
+    rdh, rdw = flce_backward_from_lse(h, w, y, lse32.double().numpy(), grad_out=g_up, reduction=reduction)
+    hd, wd, yd = h.to(DEV), w.to(DEV), y.to(DEV)
+    go = torch.tensor([g_up], dtype=torch.float32, device=DEV)
+    dh, dw = flce.linear_cross_entropy_backward(hd, wd, yd, lse32.to(DEV), go, reduction=reduction)
+    torch.cuda.synchronize()
+    _check_grads(to_f64(dh), to_f64(dw), rdh, rdw, wl.torch_dtype, "bwd")
+
+
+@pytest.mark.parametrize("chunk", ["64", "512"])
+def test_bwd_chunk_modes_bf16(monkeypatch, chunk):
+    """Interior 256x256 tiles with first/middle/last and single-chunk dW accumulation."""
+    wl, (h, w, y) = _case(300, 256, 1500, "bf16", seed=33)
+    monkeypatch.setenv("FLCE_CHUNK_ROWS", chunk)
+    _, lse64 = flce_forward(h, w, y)
+    lse32 = torch.from_numpy(lse64.astype(np.float32))
+    rdh, rdw = flce_backward_from_lse(h, w, y, lse32.double().numpy())
+    dh, dw = flce.linear_cross_entropy_backward(h.to(DEV), w.to(DEV), y.to(DEV), lse32.to(DEV))
+    torch.cuda.synchronize()
+    _check_grads(to_f64(dh), to_f64(dw), rdh, rdw, torch.bfloat16, f"bwd chunk {chunk}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_forward_then_backward_end_to_end(dtype):
+    wl, (h, w, y) = _case(200, 136, 3000, dtype, seed=34)
+    _, _, rdh, rdw = flce_forward_backward(h, w, y)
+    hd, wd, yd = h.to(DEV), w.to(DEV), y.to(DEV)
+    _, lse = flce.linear_cross_entropy_forward(hd, wd, yd)
+    go = torch.tensor([-1.5], dtype=torch.float32, device=DEV)
+    dh, dw = flce.linear_cross_entropy_backward(hd, wd, yd, lse, go)
+    torch.cuda.synchronize()
+    _check_grads(to_f64(dh), to_f64(dw), -1.5 * rdh, -1.5 * rdw, wl.torch_dtype, "fwd+bwd")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_autograd_module(dtype):
+    wl, (h, w, y) = _case(150, 128, 2500, dtype, ignore_frac=0.2, seed=35)
+    loss_ref, _, rdh, rdw = flce_forward_backward(h, w, y)
+    hd = h.to(DEV).requires_grad_(True)
+    wd = w.to(DEV).requires_grad_(True)
+    loss = LinearCrossEntropyLoss()(hd, wd, y.to(DEV))
+    assert loss.dim() == 0
+    (2.5 * loss).backward()
+    torch.cuda.synchronize()
+    tol = TOL[wl.torch_dtype]
+    assert abs(float(loss.item()) - loss_ref) <= tol["loss"] * abs(loss_ref)
+    _check_grads(to_f64(hd.grad), to_f64(wd.grad), 2.5 * rdh, 2.5 * rdw, wl.torch_dtype, "autograd")
+
+
+def test_bwd_single_row_and_tiny_vocab():
+    wl, (h, w, y) = _case(1, 16, 5, "bf16", ignore_frac=0.0, seed=36)
+    _, lse64 = flce_forward(h, w, y)
+    lse32 = torch.from_numpy(lse64.astype(np.float32))
+    rdh, rdw = flce_backward_from_lse(h, w, y, lse32.double().numpy())
+    dh, dw = flce.linear_cross_entropy_backward(h.to(DEV), w.to(DEV), y.to(DEV), lse32.to(DEV))
+    torch.cuda.synchronize()
+    _check_grads(to_f64(dh), to_f64(dw), rdh, rdw, torch.bfloat16, "bwd 1x16x5")
