@@ -182,6 +182,38 @@ def main() -> int:
                    "ratio": extra / logits_bytes_avoided(wl.n, wl.v)},
         "plan": plan,
     }
+    # The split path an autograd function uses: flce_fwd (loss, LSE) then flce_bwd
+    # (logits recomputed from the saved LSE), 8 N D V flop per step.
+    dt_code = flce.FLCE_BF16 if wl.dtype == "bf16" else flce.FLCE_F32
+    red_code = flce.FLCE_MEAN if wl.reduction == "mean" else flce.FLCE_SUM
+    loss_s, lse_s, dh_s, dw_s = out
+
+    def split_step():
+        st = flce.flce_fwd(hd, wd, yd, wl.n, wl.d, wl.v, dt_code, -100, red_code, loss_s, lse_s, stream)
+        st = st or flce.flce_bwd(hd, wd, yd, lse_s, None, wl.n, wl.d, wl.v, dt_code, -100, red_code, dh_s, dw_s,
+                                 stream)
+        if st != flce.FLCE_OK:
+            raise flce.FlceError(st, "split step")
+
+    for _ in range(max(1, args.warmup)):
+        split_step()
+    torch.cuda.synchronize()
+    s0 = torch.cuda.Event(enable_timing=True)
+    s1 = torch.cuda.Event(enable_timing=True)
+    s0.record(stream)
+    for _ in range(args.steps):
+        split_step()
+    s1.record(stream)
+    torch.cuda.synchronize()
+    ms_split = s0.elapsed_time(s1) / args.steps
+    log(f"[bench] split fwd + bwd-from-LSE: {ms_split:.3f} ms/step")
+    result["split_fwd_bwd"] = {
+        "ms_per_step": ms_split,
+        "tokens_per_s": wl.n / (ms_split * 1e-3),
+        "tflops_8ndv": 8.0 * wl.n * wl.d * wl.v / (ms_split * 1e-3) / 1e12,
+        "mfma_pct_8ndv": 100.0 * 8.0 * wl.n * wl.d * wl.v / (ms_split * 1e-3) / (peak * 1e12),
+        "path": "flce_fwd then flce_bwd (logits recomputed from the saved LSE)",
+    }
     if not args.no_cpu_baseline:
         log(f"[bench] CPU baseline: oracle on {args.cpu_rows} rows")
         result["cpu_baseline"] = cpu_baseline(wl, h, w, y, args.cpu_rows)
