@@ -23,6 +23,7 @@ METRIC = "fused linear-CE fwd+bwd tokens/s (N=8192,D=4096,V=128256 bf16); MFMA %
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}      # MI355X dense matrix peaks
 GEMM_KINDS = ("logits_lse", "dh_gemm", "dw_gemm")
 COPY_BYTES = 1 << 30
+HBM_PEAK_GBPS = 8000.0                               # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_llama3_8b_head_traffic.txt")
 TRAFFIC_KEYS = {"logits_lse": "logits", "dh_gemm": "dh", "dw_gemm": "dw"}
 ENGINE_SRC = os.path.join(ROOT, "linear_cross_entropy_bwd_amd", "csrc", "engine_mfma.hip")
@@ -66,6 +67,66 @@ def cpu_baseline(wl, h, w, y, rows: int):
     return {"value": rows / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"first {rows} of {wl.n} tokens of {wl.name} (full D={wl.d}, V={wl.v}), fp64 numpy, "
                       f"{dt:.1f} s incl. fp64 conversion"}
+
+
+def ce_logits_measure(flce, torch, hd, wd, yd, wl, args, stream):
+    """Cross-entropy on materialised logits (flce_ce_logits) for this workload's
+    logits Z = H W^T: forward only, forward + gradient into a separate buffer,
+    and the backward from the saved LSE.  HBM-bound; the algorithmic bytes are
+    one read of Z (forward) and one read of Z plus one write of the gradient
+    (gradient modes)."""
+    n, v = wl.n, wl.v
+    z = torch.matmul(hd, wd.t())             # input preparation only, outside the timed region
+    g = torch.empty_like(z)
+    loss = torch.empty(1, dtype=torch.float32, device=hd.device)
+    lse = torch.empty(n, dtype=torch.float32, device=hd.device)
+    dt_code = flce.FLCE_BF16 if wl.dtype == "bf16" else flce.FLCE_F32
+    red_code = flce.FLCE_MEAN if wl.reduction == "mean" else flce.FLCE_SUM
+    elem = z.element_size()
+    modes = {
+        "forward": (lambda: flce.flce_ce_logits(z, yd, n, v, dt_code, -100, red_code, None, None, loss, lse, None,
+                                                stream), n * v * elem),
+        "forward_grad": (lambda: flce.flce_ce_logits(z, yd, n, v, dt_code, -100, red_code, None, None, loss, lse, g,
+                                                     stream), 2 * n * v * elem),
+        "backward_from_lse": (lambda: flce.flce_ce_logits(z, yd, n, v, dt_code, -100, red_code, lse, None, None,
+                                                          None, g, stream), 2 * n * v * elem),
+    }
+    res = {"workload": f"{wl.name} logits [{n}, {v}] {wl.dtype}", "peak_GBps": HBM_PEAK_GBPS}
+    for name, (fn, nbytes) in modes.items():
+        for _ in range(max(1, args.warmup)):
+            if fn() != flce.FLCE_OK:
+                raise RuntimeError(f"flce_ce_logits {name} failed")
+        torch.cuda.synchronize()
+        flce.flce_profile_read()
+        flce.flce_profile_enable(True)
+        for _ in range(args.steps):
+            fn()
+        torch.cuda.synchronize()
+        flce.flce_profile_enable(False)
+        kern = flce.flce_profile_read()
+        launches, ms = kern.get("ce_rows", (0, 0.0))
+        avg = ms / max(launches, 1)
+        res[name] = {"ce_rows_avg_ms": avg, "algorithmic_bytes": nbytes,
+                     "achieved_GBps": nbytes / (avg * 1e-3) / 1e9,
+                     "frac": nbytes / (avg * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                     "ms_per_call": sum(t for _, t in kern.values()) / args.steps}
+        log(f"[bench] ce_logits {name}: {avg:.3f} ms ({res[name]['achieved_GBps']:.0f} GB/s)")
+    # practical ceiling: a device-to-device copy of the same bytes (one read + one write)
+    for _ in range(2):
+        g.copy_(z)
+    torch.cuda.synchronize()
+    c0 = torch.cuda.Event(enable_timing=True)
+    c1 = torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(args.steps):
+        g.copy_(z)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    ms_copy = c0.elapsed_time(c1) / args.steps
+    res["device_copy"] = {"ms": ms_copy, "GBps": 2 * n * v * elem / (ms_copy * 1e-3) / 1e9}
+    log(f"[bench] device copy of the logits: {ms_copy:.3f} ms ({res['device_copy']['GBps']:.0f} GB/s)")
+    del z, g
+    return res
 
 
 def main() -> int:
@@ -214,6 +275,7 @@ def main() -> int:
         "mfma_pct_8ndv": 100.0 * 8.0 * wl.n * wl.d * wl.v / (ms_split * 1e-3) / (peak * 1e12),
         "path": "flce_fwd then flce_bwd (logits recomputed from the saved LSE)",
     }
+    result["ce_logits"] = ce_logits_measure(flce, torch, hd, wd, yd, wl, args, stream)
     if not args.no_cpu_baseline:
         log(f"[bench] CPU baseline: oracle on {args.cpu_rows} rows")
         result["cpu_baseline"] = cpu_baseline(wl, h, w, y, args.cpu_rows)

@@ -142,6 +142,33 @@ int flce_bwd(const void* h, const void* w, const int64_t* labels, const float* l
              void* dh_out, void* dw_out, hipStream_t stream);
 
 /*
+ * Cross-entropy on logits the caller already holds ([n, v], row-major, dtype
+ * bf16 or fp32): the LigerCrossEntropyLoss example of the lecture page "GPU
+ * MODE lecture 028 - Liger Kernel" (logits as a [B*S, vocab] view) -- per-row
+ * log-sum-exp, target logit and loss as in the blog page's
+ * section "1. Fused Linear Cross-Entropy with Online LogSumExp" steps 3-5, and
+ * the gradient softmax - one-hot of its section "2. In-Kernel Gradient
+ * Computation During the Backward Pass", without the GEMM.
+ *
+ *   logits     device, [n, v] in dtype; read only unless grad_out == logits.
+ *   lse_in     device, [n] fp32 or NULL.  NULL: compute the LSE and the loss.
+ *              Non-NULL: the LSE of these logits (a backward from the saved
+ *              LSE); loss_out and lse_out are then not written.
+ *   grad_scale device, one fp32 multiplying the gradient (the upstream
+ *              gradient of the loss), or NULL for 1.
+ *   loss_out   device, one fp32; required when lse_in is NULL.
+ *   lse_out    device, [n] fp32, or NULL.
+ *   grad_out   device, [n, v] in dtype, or NULL for no gradient; may equal
+ *              logits (the gradient then overwrites the logits in place);
+ *              required when lse_in is given.  Ignored rows get zero rows.
+ * Stream-ordered; errors as for flce_fwd_bwd (FLCE_ERR_ALIGNMENT when a
+ * pointer is not aligned to its element size).
+ */
+int flce_ce_logits(const void* logits, const int64_t* labels, int64_t n, int64_t v, flce_dtype dtype,
+                   int64_t ignore_index, flce_reduction reduction, const float* lse_in, const float* grad_scale,
+                   float* loss_out, float* lse_out, void* grad_out, hipStream_t stream);
+
+/*
  * Bytes of device workspace one call allocates (with_bwd = 1 for
  * flce_fwd_bwd and flce_bwd, 0 for flce_fwd); 0 for invalid sizes.  Honours the
  * FLCE_CHUNK_ROWS and FLCE_WORKSPACE_CAP_BYTES environment overrides exactly

@@ -26,6 +26,7 @@ EXPORTED = (
     "flce_fwd_bwd",
     "flce_fwd",
     "flce_bwd",
+    "flce_ce_logits",
     "flce_workspace_bytes",
     "flce_plan_info",
     "flce_strerror",
@@ -77,6 +78,8 @@ def lib() -> ctypes.CDLL:
     L.flce_fwd.restype = i32
     L.flce_bwd.argtypes = [p, p, p, p, p, i64, i64, i64, i32, i64, i32, p, p, p]
     L.flce_bwd.restype = i32
+    L.flce_ce_logits.argtypes = [p, p, i64, i64, i32, i64, i32, p, p, p, p, p, p]
+    L.flce_ce_logits.restype = i32
     L.flce_workspace_bytes.argtypes = [i64, i64, i64, i32, i32]
     L.flce_workspace_bytes.restype = ctypes.c_size_t
     L.flce_plan_info.argtypes = [i64, i64, i64, i32, i32, ctypes.POINTER(PlanInfo)]
@@ -137,6 +140,12 @@ def flce_bwd(h, w, labels, lse, grad_out, n, d, v, dtype, ignore_index, reductio
                           reduction, _ptr(dh_out), _ptr(dw_out), _stream(stream))
 
 
+def flce_ce_logits(logits, labels, n, v, dtype, ignore_index, reduction, lse_in, grad_scale, loss_out, lse_out,
+                   grad_out, stream) -> int:
+    return lib().flce_ce_logits(_ptr(logits), _ptr(labels), n, v, dtype, ignore_index, reduction, _ptr(lse_in),
+                                _ptr(grad_scale), _ptr(loss_out), _ptr(lse_out), _ptr(grad_out), _stream(stream))
+
+
 def flce_workspace_bytes(n, d, v, dtype, with_bwd) -> int:
     return int(lib().flce_workspace_bytes(n, d, v, dtype, int(with_bwd)))
 
@@ -159,7 +168,7 @@ def flce_profile_enable(on: bool) -> int:
 
 def flce_profile_read() -> dict:
     """{kind name: (launches, total ms)} since the previous read."""
-    n = 8
+    n = 16
     launches = (ctypes.c_int64 * n)()
     ms = (ctypes.c_double * n)()
     st = lib().flce_profile_read(n, launches, ms)
@@ -278,3 +287,55 @@ def linear_cross_entropy_backward(h, w, labels, lse, grad_out=None, ignore_index
     if st != FLCE_OK:
         raise FlceError(st, "flce_bwd")
     return dh, dw
+
+
+def _check_logits(logits, labels):
+    import torch
+    if not (logits.is_cuda and labels.is_cuda):
+        raise ValueError("logits and labels must be device tensors")
+    if logits.dim() != 2 or labels.dim() != 1 or labels.shape[0] != logits.shape[0]:
+        raise ValueError("expected logits [n, v] and labels [n]")
+    if labels.dtype != torch.int64:
+        raise TypeError("labels must be int64")
+    if not (logits.is_contiguous() and labels.is_contiguous()):
+        raise ValueError("logits and labels must be contiguous")
+
+
+def cross_entropy(logits, labels, ignore_index: int = -100, reduction: str = "mean", grad: Optional[str] = None):
+    """Cross-entropy on given logits (flce_ce_logits): returns (loss fp32 [1], lse fp32 [n], gradient or None).
+
+    ``grad``: None (no gradient), "separate" (a new [n, v] tensor) or "inplace"
+    (the gradient overwrites ``logits``, which is returned as the gradient).
+    """
+    import torch
+    _check_logits(logits, labels)
+    n, v = logits.shape
+    loss = torch.empty(1, dtype=torch.float32, device=logits.device)
+    lse = torch.empty(n, dtype=torch.float32, device=logits.device)
+    if grad is None:
+        g = None
+    elif grad == "separate":
+        g = torch.empty_like(logits)
+    elif grad == "inplace":
+        g = logits
+    else:
+        raise ValueError(f"unknown grad mode {grad!r}")
+    st = flce_ce_logits(logits, labels, n, v, _dtype_code(logits), ignore_index, _red_code(reduction), None, None,
+                        loss, lse, g, torch.cuda.current_stream(logits.device))
+    if st != FLCE_OK:
+        raise FlceError(st, "flce_ce_logits")
+    return loss, lse, g
+
+
+def cross_entropy_backward(logits, labels, lse, grad_scale=None, ignore_index: int = -100, reduction: str = "mean",
+                           out=None):
+    """Gradient of ``grad_scale * loss`` w.r.t. the logits from the saved LSE (flce_ce_logits with lse_in)."""
+    import torch
+    _check_logits(logits, labels)
+    n, v = logits.shape
+    g = torch.empty_like(logits) if out is None else out
+    st = flce_ce_logits(logits, labels, n, v, _dtype_code(logits), ignore_index, _red_code(reduction), lse,
+                        grad_scale, None, None, g, torch.cuda.current_stream(logits.device))
+    if st != FLCE_OK:
+        raise FlceError(st, "flce_ce_logits")
+    return g

@@ -163,8 +163,8 @@ struct Prof {
 };
 Prof g_prof;
 
-const char* const kKindNames[K_NUM_KINDS] = {"label_scan", "logits_lse", "lse_merge", "grad_inplace",
-                                             "dh_gemm",    "dh_reduce",  "dw_gemm",   "loss_reduce"};
+const char* const kKindNames[K_NUM_KINDS] = {"label_scan", "logits_lse", "lse_merge",   "grad_inplace", "dh_gemm",
+                                             "dh_reduce",  "dw_gemm",    "loss_reduce", "ce_rows"};
 
 template <class F>
 hipError_t timed(int kind, hipStream_t s, F&& launch) {
@@ -350,6 +350,61 @@ int call_bwd(const void* h, const void* w, const int64_t* labels, const float* l
   });
 }
 
+int call_ce_logits(const void* logits, const int64_t* labels, int64_t n, int64_t v, flce_dtype dtype,
+                   int64_t ignore_index, flce_reduction reduction, const float* lse_in, const float* grad_scale,
+                   float* loss_out, float* lse_out, void* grad_out, hipStream_t stream) {
+  if (logits == nullptr || labels == nullptr) return FLCE_ERR_INVALID_ARG;
+  if (n <= 0 || v <= 0 || n > (int64_t(1) << 40) || v > (int64_t(1) << 40) || !mul_ok(n, v))
+    return FLCE_ERR_INVALID_ARG;
+  if (dtype != FLCE_BF16 && dtype != FLCE_F32) return FLCE_ERR_INVALID_ARG;
+  if (reduction != FLCE_MEAN && reduction != FLCE_SUM) return FLCE_ERR_INVALID_ARG;
+  if (lse_in == nullptr && loss_out == nullptr) return FLCE_ERR_INVALID_ARG;   // statistics need a loss output
+  if (lse_in != nullptr && grad_out == nullptr) return FLCE_ERR_INVALID_ARG;   // a backward needs a gradient output
+  const size_t elem = dtype == FLCE_BF16 ? 2 : 4;
+  if (!aligned(logits, elem) || (grad_out != nullptr && !aligned(grad_out, elem)) || !aligned(labels, 8))
+    return FLCE_ERR_ALIGNMENT;
+  for (const void* q : {static_cast<const void*>(lse_in), static_cast<const void*>(grad_scale),
+                        static_cast<const void*>(loss_out), static_cast<const void*>(lse_out)})
+    if (q != nullptr && !aligned(q, 4)) return FLCE_ERR_ALIGNMENT;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FLCE_ERR_HIP;
+  hipMemPool_t pool;
+  if (device_pool(dev, &pool) != hipSuccess) return FLCE_ERR_HIP;
+  // workspace: n_valid, per-row loss, and the LSE when the caller wants none back
+  const size_t off_loss = kAlign;
+  const size_t off_lse = off_loss + ((sizeof(float) * static_cast<size_t>(n) + kAlign - 1) / kAlign) * kAlign;
+  const size_t total = off_lse + sizeof(float) * static_cast<size_t>(n);
+  void* base = nullptr;
+  if (hipMallocFromPoolAsync(&base, total, pool, stream) != hipSuccess || base == nullptr) {
+    (void)hipGetLastError();
+    return FLCE_ERR_OOM;
+  }
+  char* b = static_cast<char*>(base);
+  CeArgs a;
+  a.logits = logits;
+  a.n = n;
+  a.v = v;
+  a.dtype = dtype;
+  a.labels = labels;
+  a.ignore_index = ignore_index;
+  a.reduction = reduction;
+  a.nvalid = reinterpret_cast<int32_t*>(b);
+  a.lse_in = lse_in;
+  a.grad_scale = grad_scale;
+  a.loss_rows = reinterpret_cast<float*>(b + off_loss);
+  a.lse_out = lse_out != nullptr ? lse_out : reinterpret_cast<float*>(b + off_lse);
+  a.grad = grad_out;
+  hipError_t e = timed(K_LABEL_SCAN, stream, [&] {
+    return launch_label_count(labels, n, ignore_index, reinterpret_cast<int32_t*>(b), stream);
+  });
+  if (e == hipSuccess) e = timed(K_CE_ROWS, stream, [&] { return launch_ce_rows(a, stream); });
+  if (e == hipSuccess && lse_in == nullptr)
+    e = timed(K_LOSS, stream, [&] { return launch_loss_sum(a.loss_rows, n, a.nvalid, reduction, loss_out, stream); });
+  hipError_t f = hipFreeAsync(base, stream);
+  if (e != hipSuccess) return FLCE_ERR_HIP;
+  return status_of(f);
+}
+
 }  // namespace
 }  // namespace flce
 
@@ -372,6 +427,13 @@ int flce_bwd(const void* h, const void* w, const int64_t* labels, const float* l
              int64_t d, int64_t v, flce_dtype dtype, int64_t ignore_index, flce_reduction reduction, void* dh_out,
              void* dw_out, hipStream_t stream) {
   return flce::call_bwd(h, w, labels, lse, grad_out, n, d, v, dtype, ignore_index, reduction, dh_out, dw_out, stream);
+}
+
+int flce_ce_logits(const void* logits, const int64_t* labels, int64_t n, int64_t v, flce_dtype dtype,
+                   int64_t ignore_index, flce_reduction reduction, const float* lse_in, const float* grad_scale,
+                   float* loss_out, float* lse_out, void* grad_out, hipStream_t stream) {
+  return flce::call_ce_logits(logits, labels, n, v, dtype, ignore_index, reduction, lse_in, grad_scale, loss_out,
+                              lse_out, grad_out, stream);
 }
 
 size_t flce_workspace_bytes(int64_t n, int64_t d, int64_t v, flce_dtype dtype, int with_bwd) {

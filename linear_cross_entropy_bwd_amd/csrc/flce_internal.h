@@ -66,7 +66,8 @@ enum Kind : int {
   K_DH_REDUCE = 5,
   K_DW = 6,
   K_LOSS = 7,
-  K_NUM_KINDS = 8
+  K_CE_ROWS = 8,
+  K_NUM_KINDS = 9
 };
 
 // What the logits contraction's epilogue produces.
@@ -103,6 +104,26 @@ hipError_t launch_lse_merge(const Plan& p, const Work& w, const ChunkArgs& a, in
 hipError_t launch_grad(const Plan& p, const Work& w, const ChunkArgs& a, hipStream_t s);
 hipError_t launch_loss_reduce(const Plan& p, const Work& w, int32_t reduction, float* loss_out, hipStream_t s);
 hipError_t launch_dh_reduce(const Plan& p, const Work& w, const ChunkArgs& a, hipStream_t s);
+hipError_t launch_label_count(const int64_t* labels, int64_t n, int64_t ignore_index, int32_t* nvalid, hipStream_t s);
+hipError_t launch_loss_sum(const float* loss_rows, int64_t n, const int32_t* nvalid, int32_t reduction,
+                           float* loss_out, hipStream_t s);
+
+// Cross-entropy on given logits (ce_logits.hip).
+struct CeArgs {
+  const void* logits;       // [n, v], dtype
+  int64_t n, v;
+  int32_t dtype;
+  const int64_t* labels;
+  int64_t ignore_index;
+  int32_t reduction;
+  const int32_t* nvalid;
+  const float* lse_in;      // saved LSE (skip the statistics pass) or nullptr
+  const float* grad_scale;  // device scalar or nullptr for 1
+  float* lse_out;           // [n] (statistics pass)
+  float* loss_rows;         // [n] (statistics pass)
+  void* grad;               // [n, v] dtype, may alias logits, or nullptr
+};
+hipError_t launch_ce_rows(const CeArgs& a, hipStream_t s);
 
 // fp32 FMA engine (engine_fma.hip): FLCE_F32 (dw_out itself accumulates).
 hipError_t fma_logits(const Plan& p, const Work& w, const ChunkArgs& a, int mode, hipStream_t s);

@@ -242,3 +242,18 @@ hipError_t launch_loss_reduce(const Plan& p, const Work& w, int32_t reduction, f
 }
 
 }  // namespace flce
+
+namespace flce {
+
+hipError_t launch_label_count(const int64_t* labels, int64_t n, int64_t ignore_index, int32_t* nvalid, hipStream_t s) {
+  label_scan_kernel<<<1, kScanThreads, 0, s>>>(labels, n, ignore_index, nvalid, nullptr, 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_loss_sum(const float* loss_rows, int64_t n, const int32_t* nvalid, int32_t reduction,
+                           float* loss_out, hipStream_t s) {
+  loss_reduce_kernel<<<1, 1024, 0, s>>>(loss_rows, n, nvalid, reduction, loss_out);
+  return hipGetLastError();
+}
+
+}  // namespace flce

@@ -27,9 +27,9 @@ written from the pages:
   logits and forms the softmax from it); the gradient of an upstream scalar
   ``g . loss`` is ``g`` times the loss gradient;
 * cross-entropy on logits that are already materialised (the
-  ``LigerCrossEntropyLoss`` call of the lecture page and the "Chunked
-  CrossEntropy" row of the third page): the same LSE, target and gradient
-  formulas applied to a given ``[N, V]`` logits array;
+  ``LigerCrossEntropyLoss`` example of the lecture page, a drop-in for
+  PyTorch's loss on a ``[B*S, vocab]`` logits view): the same LSE, target and
+  gradient formulas applied to a given ``[N, V]`` logits array;
 * ``reduction="mean"`` as in the loss module call on the lecture page
   ("GPU MODE lecture 028 - Liger Kernel", the LigerCrossEntropyLoss example);
   the mean is taken over the rows whose label is not ``ignore_index``, and a

@@ -134,6 +134,30 @@ def test_bwd_argument_errors_before_any_device_work():
     assert call(d=6) == flce.FLCE_ERR_ALIGNMENT
 
 
+def test_ce_logits_argument_errors_before_any_device_work():
+    A = 1 << 20
+    ok = dict(logits=A, labels=A, n=4, v=16, dtype=flce.FLCE_BF16, ignore_index=-100, reduction=flce.FLCE_MEAN,
+              lse_in=None, grad_scale=None, loss_out=A, lse_out=None, grad_out=None, stream=None)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return flce.flce_ce_logits(**a)
+
+    assert call(logits=None) == flce.FLCE_ERR_INVALID_ARG
+    assert call(labels=None) == flce.FLCE_ERR_INVALID_ARG
+    assert call(n=0) == flce.FLCE_ERR_INVALID_ARG
+    assert call(v=-1) == flce.FLCE_ERR_INVALID_ARG
+    assert call(dtype=3) == flce.FLCE_ERR_INVALID_ARG
+    assert call(loss_out=None) == flce.FLCE_ERR_INVALID_ARG              # statistics without a loss output
+    assert call(lse_in=A, loss_out=None) == flce.FLCE_ERR_INVALID_ARG    # a backward without a gradient output
+    assert call(logits=A + 1) == flce.FLCE_ERR_ALIGNMENT
+    assert call(grad_out=A + 1) == flce.FLCE_ERR_ALIGNMENT
+    assert call(dtype=flce.FLCE_F32, logits=A + 2) == flce.FLCE_ERR_ALIGNMENT
+    assert call(labels=A + 4) == flce.FLCE_ERR_ALIGNMENT
+    assert call(lse_out=A + 2) == flce.FLCE_ERR_ALIGNMENT
+
+
 def test_no_cpu_fallback(monkeypatch, tmp_path):
     """Without the built library the binding raises instead of computing anything."""
     monkeypatch.setattr(flce, "_lib", None)

@@ -66,3 +66,15 @@ def test_block_draw_independent_of_threads():
     a = workloads._normal_rows(5, 9000, 3, 1.0, threads=1)
     b = workloads._normal_rows(5, 9000, 3, 1.0, threads=3)
     assert np.array_equal(a, b)
+
+
+def test_logits_draw_deterministic_and_spread():
+    from workloads import make_logits
+    wl = Workload("z", 300, 4096, 5000, "f32", 0.02, "uniform", 0.1, "mean", seed=7)
+    z1, y1 = make_logits(wl, threads=1)
+    z2, y2 = make_logits(wl, threads=4)
+    assert z1.shape == (300, 5000) and z1.dtype == torch.float32
+    assert torch.equal(z1, z2) and torch.equal(y1, y2)
+    assert torch.equal(y1, torch.from_numpy(make_labels(wl)))
+    # default spread sigma_w * sqrt(d) = 1.28
+    assert abs(float(z1.double().std()) - 1.28) < 0.01

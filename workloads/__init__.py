@@ -133,6 +133,22 @@ def make_inputs(wl: Workload, threads: Optional[int] = None):
     return ht.contiguous(), wt.contiguous(), torch.from_numpy(y)
 
 
+def make_logits(wl: Workload, sigma: Optional[float] = None, threads: Optional[int] = None):
+    """Return (Z [n, v], labels) for cross-entropy on materialised logits.
+
+    Z ~ N(0, sigma^2) in the workload dtype; the default sigma is
+    sigma_w * sqrt(d), the spread of W.h for the workload's own H and W draws
+    (each logit is a sum of d products of N(0, 1) and N(0, sigma_w^2) values).
+    Labels are the workload's labels.  Seeds 4000 + k.
+    """
+    if sigma is None:
+        sigma = wl.sigma_w * float(np.sqrt(wl.d))
+    z = _normal_rows(4000 + wl.seed, wl.n, wl.v, sigma, threads)
+    zt = torch.from_numpy(z).to(wl.torch_dtype)
+    del z
+    return zt.contiguous(), torch.from_numpy(make_labels(wl))
+
+
 def logits_bytes_avoided(n: int, v: int, elem_bytes: int = 4) -> int:
     """Size of the full [n, v] logits tensor that the fused path never allocates.
 
