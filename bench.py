@@ -25,13 +25,15 @@ GEMM_KINDS = ("logits_lse", "dh_gemm", "dw_gemm")
 COPY_BYTES = 1 << 30
 HBM_PEAK_GBPS = 8000.0                               # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_llama3_8b_head_traffic.txt")
-TRAFFIC_KEYS = {"logits_lse": "logits", "dh_gemm": "dh", "dw_gemm": "dw"}
-ENGINE_SRC = os.path.join(ROOT, "linear_cross_entropy_bwd_amd", "csrc", "engine_mfma.hip")
+TRAFFIC_KEYS = {"logits_lse": ("logits", "engine"), "dh_gemm": ("dh", "engine"), "dw_gemm": ("dw", "engine"),
+                "ce_fwd_grad": ("ce_fwd_grad", "ce")}
+KERNEL_SRC = {"engine": os.path.join(ROOT, "linear_cross_entropy_bwd_amd", "csrc", "engine_mfma.hip"),
+              "ce": os.path.join(ROOT, "linear_cross_entropy_bwd_amd", "csrc", "ce_logits.hip")}
 
 
 def measured_traffic(kernel: str):
     """HBM bytes per launch of `kernel` from the committed counter summary, or None when
-    there is none or the engine source changed since the counters were taken."""
+    there is none or the kernel's source changed since the counters were taken."""
     import hashlib
     if not os.path.exists(TRAFFIC_FILE) or kernel not in TRAFFIC_KEYS:
         return None
@@ -40,11 +42,12 @@ def measured_traffic(kernel: str):
         if "=" in line and not line.startswith("#"):
             k, v = line.split("=", 1)
             kv[k.strip()] = v.strip()
-    digest = hashlib.sha256(open(ENGINE_SRC, "rb").read()).hexdigest()
-    if kv.get("engine_sha256") != digest:
+    key, src = TRAFFIC_KEYS[kernel]
+    digest = hashlib.sha256(open(KERNEL_SRC[src], "rb").read()).hexdigest()
+    if kv.get(f"{src}_sha256") != digest:
         return None
     try:
-        return float(kv[f"{TRAFFIC_KEYS[kernel]}_traffic_bytes_per_launch"])
+        return float(kv[f"{key}_traffic_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
 
@@ -107,6 +110,7 @@ def ce_logits_measure(flce, torch, hd, wd, yd, wl, args, stream):
         launches, ms = kern.get("ce_rows", (0, 0.0))
         avg = ms / max(launches, 1)
         res[name] = {"ce_rows_avg_ms": avg, "algorithmic_bytes": nbytes,
+                     "traffic": measured_traffic("ce_fwd_grad") if name == "forward_grad" else None,
                      "achieved_GBps": nbytes / (avg * 1e-3) / 1e9,
                      "frac": nbytes / (avg * 1e-3) / 1e9 / HBM_PEAK_GBPS,
                      "ms_per_call": sum(t for _, t in kern.values()) / args.steps}
@@ -138,8 +142,9 @@ def main() -> int:
     ap.add_argument("--cpu-rows", type=int, default=3072, help="tokens in the oracle's CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic-probe", action="store_true",
-                    help="run a 1 GiB device copy (counter calibration) and one step, print nothing else; "
-                         "meant to run under rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE")
+                    help="run a 1 GiB device copy (counter calibration), one step and one cross-entropy on "
+                         "the workload's logits, print nothing else; meant to run under rocprofv3 --pmc "
+                         "FETCH_SIZE / WRITE_SIZE")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -181,6 +186,18 @@ def main() -> int:
         torch.cuda.synchronize()
         flce.linear_cross_entropy(hd, wd, yd, reduction=wl.reduction, out=out)
         torch.cuda.synchronize()
+        # and one cross-entropy on this workload's logits, forward + gradient into a separate buffer
+        z = torch.matmul(hd, wd.t())
+        g = torch.empty_like(z)
+        loss_z = torch.empty(1, dtype=torch.float32, device=dev)
+        lse_z = torch.empty(wl.n, dtype=torch.float32, device=dev)
+        torch.cuda.synchronize()
+        st = flce.flce_ce_logits(z, yd, wl.n, wl.v, flce.FLCE_BF16 if wl.dtype == "bf16" else flce.FLCE_F32, -100,
+                                 flce.FLCE_MEAN if wl.reduction == "mean" else flce.FLCE_SUM, None, None, loss_z,
+                                 lse_z, g, torch.cuda.current_stream(dev))
+        torch.cuda.synchronize()
+        if st != flce.FLCE_OK:
+            raise flce.FlceError(st, "flce_ce_logits")
         log("[bench] traffic probe done")
         return 0
 
