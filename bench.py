@@ -211,20 +211,23 @@ def main() -> int:
     flce.flce_profile_read()                 # clear
     flce.flce_profile_enable(True)
     torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     wall0 = time.perf_counter()
-    t0.record(stream)
-    for _ in range(args.steps):
+    ev[0].record(stream)
+    for i in range(args.steps):
         flce.linear_cross_entropy(hd, wd, yd, reduction=wl.reduction, out=out)
-    t1.record(stream)
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     flce.flce_profile_enable(False)
     kern = flce.flce_profile_read()
-    ms_total = t0.elapsed_time(t1)
+    ms_total = ev[0].elapsed_time(ev[-1])
     ms_step = ms_total / args.steps
-    log(f"[bench] {args.steps} steps: {ms_step:.3f} ms/step (wall {wall:.2f} s); kernels {kern}")
+    per_step = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
+    ms_median = per_step[len(per_step) // 2] if len(per_step) % 2 else 0.5 * (
+        per_step[len(per_step) // 2 - 1] + per_step[len(per_step) // 2])
+    log(f"[bench] {args.steps} steps: {ms_step:.3f} ms/step (median {ms_median:.3f}, min {per_step[0]:.3f}; "
+        f"wall {wall:.2f} s); kernels {kern}")
 
     flops_step = 6.0 * wl.n * wl.d * wl.v
     peak = PEAK_TFLOPS[wl.dtype]
@@ -243,6 +246,8 @@ def main() -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_step,
+        "ms_per_step_median": ms_median,
+        "ms_per_step_min": per_step[0],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -291,6 +296,29 @@ def main() -> int:
         "tflops_8ndv": 8.0 * wl.n * wl.d * wl.v / (ms_split * 1e-3) / 1e12,
         "mfma_pct_8ndv": 100.0 * 8.0 * wl.n * wl.d * wl.v / (ms_split * 1e-3) / (peak * 1e12),
         "path": "flce_fwd then flce_bwd (logits recomputed from the saved LSE)",
+    }
+    # the forward alone (loss and LSE), 2 N D V flop
+    def fwd_only():
+        st = flce.flce_fwd(hd, wd, yd, wl.n, wl.d, wl.v, dt_code, -100, red_code, loss_s, lse_s, stream)
+        if st != flce.FLCE_OK:
+            raise flce.FlceError(st, "flce_fwd")
+
+    for _ in range(max(1, args.warmup)):
+        fwd_only()
+    torch.cuda.synchronize()
+    s0.record(stream)
+    for _ in range(args.steps):
+        fwd_only()
+    s1.record(stream)
+    torch.cuda.synchronize()
+    ms_fwd = s0.elapsed_time(s1) / args.steps
+    log(f"[bench] forward only: {ms_fwd:.3f} ms/call")
+    result["forward_only"] = {
+        "ms_per_call": ms_fwd,
+        "tokens_per_s": wl.n / (ms_fwd * 1e-3),
+        "tflops_2ndv": 2.0 * wl.n * wl.d * wl.v / (ms_fwd * 1e-3) / 1e12,
+        "mfma_pct_2ndv": 100.0 * 2.0 * wl.n * wl.d * wl.v / (ms_fwd * 1e-3) / (peak * 1e12),
+        "path": "flce_fwd (loss and LSE; logits statistics only)",
     }
     result["ce_logits"] = ce_logits_measure(flce, torch, hd, wd, yd, wl, args, stream)
     if not args.no_cpu_baseline:
