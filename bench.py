@@ -320,6 +320,30 @@ def main() -> int:
         "mfma_pct_2ndv": 100.0 * 2.0 * wl.n * wl.d * wl.v / (ms_fwd * 1e-3) / (peak * 1e12),
         "path": "flce_fwd (loss and LSE; logits statistics only)",
     }
+    # vocabulary split in eight shards (the shard shape of an eight-way vocabulary-parallel
+    # head): per shard the partial forward, the merge, per shard the backward from the merged
+    # LSE, the sum of the dH terms; 8 N D V flop
+    def split8():
+        flce.linear_cross_entropy_vocab_split(hd, wd, yd, num_shards=8, reduction=wl.reduction)
+
+    for _ in range(max(1, args.warmup)):
+        split8()
+    torch.cuda.synchronize()
+    s0.record(stream)
+    for _ in range(args.steps):
+        split8()
+    s1.record(stream)
+    torch.cuda.synchronize()
+    ms_vs = s0.elapsed_time(s1) / args.steps
+    log(f"[bench] vocabulary split, 8 shards: {ms_vs:.3f} ms/step")
+    result["vocab_split_8"] = {
+        "ms_per_step": ms_vs,
+        "tokens_per_s": wl.n / (ms_vs * 1e-3),
+        "tflops_8ndv": 8.0 * wl.n * wl.d * wl.v / (ms_vs * 1e-3) / 1e12,
+        "mfma_pct_8ndv": 100.0 * 8.0 * wl.n * wl.d * wl.v / (ms_vs * 1e-3) / (peak * 1e12),
+        "shards": flce.vocab_shard_bounds(wl.v, 8),
+        "path": "flce_fwd_shard x8, flce_merge_shards, flce_bwd_shard x8, flce_sum_parts",
+    }
     result["ce_logits"] = ce_logits_measure(flce, torch, hd, wd, yd, wl, args, stream)
     if not args.no_cpu_baseline:
         log(f"[bench] CPU baseline: oracle on {args.cpu_rows} rows")

@@ -169,6 +169,70 @@ int flce_ce_logits(const void* logits, const int64_t* labels, int64_t n, int64_t
                    float* loss_out, float* lse_out, void* grad_out, hipStream_t stream);
 
 /*
+ * Vocabulary shards.  The vocabulary rows of W are split into contiguous
+ * shards [v_first, v_first + v_shard); each shard's partial statistics are
+ * computed on its own and merged exactly, because the log-sum-exp of a row is
+ * the log-sum-exp of its shards' log-sum-exps.  This is the vocabulary split
+ * the lecture page "GPU MODE lecture 028 - Liger Kernel" leaves open for
+ * vocabularies of a million ids and more (its open questions), built from the
+ * online-LSE merge of the blog page's section "1. Fused Linear Cross-Entropy
+ * with Online LogSumExp" (step 3), and the per-GPU half of a vocabulary-
+ * parallel loss: one GPU per shard, the partials exchanged in between.
+ * On one GPU a caller loops over the shards: flce_fwd_shard for each, then
+ * flce_merge_shards, then flce_bwd_shard for each with the merged LSE, then
+ * flce_sum_parts over the dH partials.
+ *
+ * Labels are the full-vocabulary ids (ignore_index or [0, V)); a shard sees
+ * the labels outside it as "no target in this shard".
+ */
+
+/*
+ * Partial forward of one shard.
+ *   w_shard       device, [v_shard, d] in dtype: rows v_first .. v_first + v_shard - 1 of W.
+ *   v_first       first vocabulary id of the shard (>= 0).
+ *   lse_part_out  device, fp32 [n]: log sum over the shard's columns of exp(z_ij), every row.
+ *   zy_part_out   device, fp32 [n]: z_{i, y_i} when y_i lies in the shard, else 0 (0 for ignored rows).
+ * h, labels, n, d, dtype, ignore_index, layouts and errors as for flce_fwd_bwd.
+ */
+int flce_fwd_shard(const void* h, const void* w_shard, const int64_t* labels, int64_t n, int64_t d, int64_t v_shard,
+                   int64_t v_first, flce_dtype dtype, int64_t ignore_index, float* lse_part_out, float* zy_part_out,
+                   hipStream_t stream);
+
+/*
+ * Merge num_shards partials into the loss and the per-row LSE.
+ *   lse_parts, zy_parts  device, fp32 [num_shards][n] (shard q's flce_fwd_shard outputs at offset q * n).
+ *   loss_out             device, one fp32; the loss of flce_fwd_bwd over the whole vocabulary.
+ *   lse_out              device, fp32 [n] or NULL; the whole-vocabulary LSE (flce_bwd_shard's lse).
+ * Stream-ordered; errors as for flce_fwd_bwd.
+ */
+int flce_merge_shards(const float* lse_parts, const float* zy_parts, int64_t num_shards, const int64_t* labels,
+                      int64_t n, int64_t ignore_index, flce_reduction reduction, float* loss_out, float* lse_out,
+                      hipStream_t stream);
+
+/*
+ * Backward of one shard from the whole-vocabulary LSE (logits recomputed, as
+ * flce_bwd): the shard's columns of G = (softmax - onehot) * scale * grad_out.
+ *   lse           device, fp32 [n]: the merged LSE from flce_merge_shards.
+ *   grad_out      device, one fp32 upstream gradient, or NULL for 1.
+ *   dh_part_out   device, fp32 [n, d] (whatever dtype is): this shard's term G_q . W_q of dH;
+ *                 dH is the sum over the shards (flce_sum_parts).  16-byte aligned.
+ *   dw_shard_out  device, [v_shard, d] in dtype: rows v_first .. v_first + v_shard - 1 of dW.
+ * Other arguments as for flce_fwd_shard and flce_bwd.
+ */
+int flce_bwd_shard(const void* h, const void* w_shard, const int64_t* labels, const float* lse, const float* grad_out,
+                   int64_t n, int64_t d, int64_t v_shard, int64_t v_first, flce_dtype dtype, int64_t ignore_index,
+                   flce_reduction reduction, float* dh_part_out, void* dw_shard_out, hipStream_t stream);
+
+/*
+ * out[i] = sum_q parts[q * count + i] for i < count, accumulated in fp32 in
+ * shard order and rounded to dtype (round-to-nearest-even for bf16): the dH
+ * of a vocabulary-split backward from its shards' partials.
+ *   parts  device, fp32 [num_parts][count];  out  device, [count] in dtype.
+ */
+int flce_sum_parts(const float* parts, int64_t num_parts, int64_t count, flce_dtype dtype, void* out,
+                   hipStream_t stream);
+
+/*
  * Bytes of device workspace one call allocates (with_bwd = 1 for
  * flce_fwd_bwd and flce_bwd, 0 for flce_fwd); 0 for invalid sizes.  Honours the
  * FLCE_CHUNK_ROWS and FLCE_WORKSPACE_CAP_BYTES environment overrides exactly

@@ -27,6 +27,10 @@ EXPORTED = (
     "flce_fwd",
     "flce_bwd",
     "flce_ce_logits",
+    "flce_fwd_shard",
+    "flce_merge_shards",
+    "flce_bwd_shard",
+    "flce_sum_parts",
     "flce_workspace_bytes",
     "flce_plan_info",
     "flce_strerror",
@@ -80,6 +84,14 @@ def lib() -> ctypes.CDLL:
     L.flce_bwd.restype = i32
     L.flce_ce_logits.argtypes = [p, p, i64, i64, i32, i64, i32, p, p, p, p, p, p]
     L.flce_ce_logits.restype = i32
+    L.flce_fwd_shard.argtypes = [p, p, p, i64, i64, i64, i64, i32, i64, p, p, p]
+    L.flce_fwd_shard.restype = i32
+    L.flce_merge_shards.argtypes = [p, p, i64, p, i64, i64, i32, p, p, p]
+    L.flce_merge_shards.restype = i32
+    L.flce_bwd_shard.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i32, i64, i32, p, p, p]
+    L.flce_bwd_shard.restype = i32
+    L.flce_sum_parts.argtypes = [p, i64, i64, i32, p, p]
+    L.flce_sum_parts.restype = i32
     L.flce_workspace_bytes.argtypes = [i64, i64, i64, i32, i32]
     L.flce_workspace_bytes.restype = ctypes.c_size_t
     L.flce_plan_info.argtypes = [i64, i64, i64, i32, i32, ctypes.POINTER(PlanInfo)]
@@ -144,6 +156,29 @@ def flce_ce_logits(logits, labels, n, v, dtype, ignore_index, reduction, lse_in,
                    grad_out, stream) -> int:
     return lib().flce_ce_logits(_ptr(logits), _ptr(labels), n, v, dtype, ignore_index, reduction, _ptr(lse_in),
                                 _ptr(grad_scale), _ptr(loss_out), _ptr(lse_out), _ptr(grad_out), _stream(stream))
+
+
+def flce_fwd_shard(h, w_shard, labels, n, d, v_shard, v_first, dtype, ignore_index, lse_part_out, zy_part_out,
+                   stream) -> int:
+    return lib().flce_fwd_shard(_ptr(h), _ptr(w_shard), _ptr(labels), n, d, v_shard, v_first, dtype, ignore_index,
+                                _ptr(lse_part_out), _ptr(zy_part_out), _stream(stream))
+
+
+def flce_merge_shards(lse_parts, zy_parts, num_shards, labels, n, ignore_index, reduction, loss_out, lse_out,
+                      stream) -> int:
+    return lib().flce_merge_shards(_ptr(lse_parts), _ptr(zy_parts), num_shards, _ptr(labels), n, ignore_index,
+                                   reduction, _ptr(loss_out), _ptr(lse_out), _stream(stream))
+
+
+def flce_bwd_shard(h, w_shard, labels, lse, grad_out, n, d, v_shard, v_first, dtype, ignore_index, reduction,
+                   dh_part_out, dw_shard_out, stream) -> int:
+    return lib().flce_bwd_shard(_ptr(h), _ptr(w_shard), _ptr(labels), _ptr(lse), _ptr(grad_out), n, d, v_shard,
+                                v_first, dtype, ignore_index, reduction, _ptr(dh_part_out), _ptr(dw_shard_out),
+                                _stream(stream))
+
+
+def flce_sum_parts(parts, num_parts, count, dtype, out, stream) -> int:
+    return lib().flce_sum_parts(_ptr(parts), num_parts, count, dtype, _ptr(out), _stream(stream))
 
 
 def flce_workspace_bytes(n, d, v, dtype, with_bwd) -> int:
@@ -339,3 +374,66 @@ def cross_entropy_backward(logits, labels, lse, grad_scale=None, ignore_index: i
     if st != FLCE_OK:
         raise FlceError(st, "flce_ce_logits")
     return g
+
+
+def vocab_shard_bounds(v: int, num_shards: int):
+    """Contiguous shards [a, b) covering [0, v): sizes differ by at most 256 (whole 256-row blocks)."""
+    if num_shards < 1 or num_shards > v:
+        raise ValueError("need 1 <= num_shards <= v")
+    blocks = (v + 255) // 256
+    if num_shards > blocks:
+        cuts = [v * q // num_shards for q in range(num_shards + 1)]
+    else:
+        cuts = [min(v, (blocks * q // num_shards) * 256) for q in range(num_shards + 1)]
+    return list(zip(cuts[:-1], cuts[1:]))
+
+
+def linear_cross_entropy_vocab_split(h, w, labels, num_shards: int = 2, ignore_index: int = -100,
+                                     reduction: str = "mean", grad_out=None, shards=None):
+    """Fused linear cross-entropy with W's vocabulary rows split into shards, on one GPU.
+
+    Per shard the partial forward (flce_fwd_shard), then the exact merge
+    (flce_merge_shards), then per shard the backward from the merged LSE
+    (flce_bwd_shard, fp32 dH terms) and the sum of the dH terms
+    (flce_sum_parts).  Returns (loss fp32 [1], lse fp32 [n], dh, dw) as
+    flce_fwd_bwd does; the logits of each shard are recomputed in its backward.
+    ``shards`` may give explicit [a, b) bounds instead of ``num_shards``.
+    """
+    import torch
+    _check_inputs(h, w, labels)
+    n, d = h.shape
+    v = w.shape[0]
+    bounds = list(shards) if shards is not None else vocab_shard_bounds(v, num_shards)
+    if bounds[0][0] != 0 or bounds[-1][1] != v or any(a >= b for a, b in bounds) or any(
+            bounds[q][1] != bounds[q + 1][0] for q in range(len(bounds) - 1)):
+        raise ValueError("shards must be contiguous, non-empty and cover [0, v)")
+    if grad_out is not None and (grad_out.dtype != torch.float32 or grad_out.numel() != 1 or not grad_out.is_cuda):
+        raise ValueError("grad_out must be a one-element fp32 device tensor")
+    q_n = len(bounds)
+    dev = h.device
+    stream = torch.cuda.current_stream(dev)
+    dt, red = _dtype_code(h), _red_code(reduction)
+    lse_parts = torch.empty(q_n, n, dtype=torch.float32, device=dev)
+    zy_parts = torch.empty(q_n, n, dtype=torch.float32, device=dev)
+    for q, (a, b) in enumerate(bounds):
+        st = flce_fwd_shard(h, w[a:b], labels, n, d, b - a, a, dt, ignore_index, lse_parts[q], zy_parts[q], stream)
+        if st != FLCE_OK:
+            raise FlceError(st, "flce_fwd_shard")
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    lse = torch.empty(n, dtype=torch.float32, device=dev)
+    st = flce_merge_shards(lse_parts, zy_parts, q_n, labels, n, ignore_index, red, loss, lse, stream)
+    if st != FLCE_OK:
+        raise FlceError(st, "flce_merge_shards")
+    dh_parts = torch.empty(q_n, n, d, dtype=torch.float32, device=dev)
+    dw = torch.empty_like(w)
+    for q, (a, b) in enumerate(bounds):
+        st = flce_bwd_shard(h, w[a:b], labels, lse, grad_out, n, d, b - a, a, dt, ignore_index, red, dh_parts[q],
+                            dw[a:b], stream)
+        if st != FLCE_OK:
+            raise FlceError(st, "flce_bwd_shard")
+    dh = torch.empty_like(h)
+    st = flce_sum_parts(dh_parts, q_n, n * d, dt, dh, stream)
+    if st != FLCE_OK:
+        raise FlceError(st, "flce_sum_parts")
+    return loss, lse, dh, dw
+

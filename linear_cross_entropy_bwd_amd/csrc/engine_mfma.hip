@@ -890,7 +890,7 @@ hipError_t mfma_dh(const Plan& p, const Work& w, const ChunkArgs& c, hipStream_t
   a.out_f32 = nullptr;
   if (p.dh_splits > 1)
     a.out_f32 = w.dhpart;
-  else if (p.dtype == FLCE_BF16)
+  else if (p.dtype == FLCE_BF16 && !c.dh_f32)
     a.out_bf16 = static_cast<bf16_t*>(c.dh);
   else
     a.out_f32 = static_cast<float*>(c.dh);

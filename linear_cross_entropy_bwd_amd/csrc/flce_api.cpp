@@ -3,6 +3,7 @@
 // and the timing instrumentation.
 #include <hip/hip_runtime.h>
 
+#include <climits>
 #include <mutex>
 #include <stdint.h>
 #include <stdlib.h>
@@ -198,6 +199,7 @@ int check_common(const void* h, const void* w, const int64_t* labels, int64_t n,
 
 Work carve(const Plan& p, char* base) {
   Work w;
+  w.base = base;
   w.nvalid = reinterpret_cast<int32_t*>(base + p.off_nvalid);
   w.zy = reinterpret_cast<float*>(base + p.off_zy);
   w.gy = reinterpret_cast<float*>(base + p.off_gy);
@@ -212,9 +214,11 @@ Work carve(const Plan& p, char* base) {
 }
 
 // The kernel sequence of one call; workspace already allocated.
+// zy_out (optional): the per-row target logit (0 for ignored rows and for
+// labels outside [0, v)); loss_out may be null when zy_out is given.
 hipError_t run(const Plan& p, const Work& wk, const void* h, const void* w, const int64_t* labels,
                int64_t ignore_index, int32_t reduction, float* loss_out, float* lse_out, void* dh_out, void* dw_out,
-               hipStream_t s) {
+               hipStream_t s, float* zy_out = nullptr) {
   const int64_t elem = p.dtype == FLCE_BF16 ? 2 : 4;
   hipError_t e = timed(K_LABEL_SCAN, s, [&] { return launch_label_scan(p, wk, labels, ignore_index, s); });
   if (e != hipSuccess) return e;
@@ -234,6 +238,8 @@ hipError_t run(const Plan& p, const Work& wk, const void* h, const void* w, cons
     a.dw_mode = p.nchunks == 1 ? DW_SINGLE : (c == 0 ? DW_FIRST : (c == p.nchunks - 1 ? DW_LAST : DW_MID));
     a.lse_in = nullptr;
     a.grad_out = nullptr;
+    a.zy_rows = zy_out != nullptr ? zy_out + a.row0 : nullptr;
+    a.dh_f32 = 0;
 
     const int mode = p.with_bwd ? LOGITS_PROB : LOGITS_STATS;
     e = timed(K_LOGITS, s, [&] {
@@ -254,15 +260,18 @@ hipError_t run(const Plan& p, const Work& wk, const void* h, const void* w, cons
     e = timed(K_DW, s, [&] { return p.engine == ENGINE_MFMA ? mfma_dw(p, wk, a, s) : fma_dw(p, wk, a, s); });
     if (e != hipSuccess) return e;
   }
+  if (loss_out == nullptr) return hipSuccess;
   return timed(K_LOSS, s, [&] { return launch_loss_reduce(p, wk, reduction, loss_out, s); });
 }
 
 // The backward from the saved LSE (recompute): per chunk the logits are
 // recomputed and their epilogue writes G directly; then dH and dW as above.
+// dh_f32: dh_out is an fp32 array whatever the dtype (a vocabulary shard's dH partial).
 hipError_t run_bwd(const Plan& p, const Work& wk, const void* h, const void* w, const int64_t* labels,
                    const float* lse, const float* grad_out, int64_t ignore_index, int32_t reduction, void* dh_out,
-                   void* dw_out, hipStream_t s) {
+                   void* dw_out, hipStream_t s, int dh_f32 = 0) {
   const int64_t elem = p.dtype == FLCE_BF16 ? 2 : 4;
+  const int64_t dh_elem = dh_f32 ? 4 : elem;
   hipError_t e = timed(K_LABEL_SCAN, s, [&] { return launch_label_scan(p, wk, labels, ignore_index, s); });
   if (e != hipSuccess) return e;
   for (int64_t c = 0; c < p.nchunks; ++c) {
@@ -275,11 +284,13 @@ hipError_t run_bwd(const Plan& p, const Work& wk, const void* h, const void* w, 
     a.ignore_index = ignore_index;
     a.reduction = reduction;
     a.lse_rows = nullptr;
-    a.dh = static_cast<char*>(dh_out) + a.row0 * p.d * elem;
+    a.dh = static_cast<char*>(dh_out) + a.row0 * p.d * dh_elem;
     a.dw = dw_out;
     a.dw_mode = p.nchunks == 1 ? DW_SINGLE : (c == 0 ? DW_FIRST : (c == p.nchunks - 1 ? DW_LAST : DW_MID));
     a.lse_in = lse + a.row0;
     a.grad_out = grad_out;
+    a.zy_rows = nullptr;
+    a.dh_f32 = dh_f32;
     e = timed(K_LOGITS, s, [&] {
       return p.engine == ENGINE_MFMA ? mfma_logits(p, wk, a, LOGITS_GRAD_FROM_LSE, s)
                                      : fma_logits(p, wk, a, LOGITS_GRAD_FROM_LSE, s);
@@ -405,6 +416,111 @@ int call_ce_logits(const void* logits, const int64_t* labels, int64_t n, int64_t
   return status_of(f);
 }
 
+// ---- vocabulary shards ---------------------------------------------------------
+
+// A shard's plan plus room for its shifted labels (int64 [n]) after the plan's workspace.
+int shard_plan(int64_t n, int64_t d, int64_t v_shard, int64_t v_first, flce_dtype dtype, int64_t ignore_index,
+               int with_bwd, Plan* p, size_t* off_labels) {
+  if (v_first < 0 || v_first > (int64_t(1) << 40)) return FLCE_ERR_INVALID_ARG;
+  // the shifted ignore value must not wrap
+  if (ignore_index < INT64_MIN + v_first) return FLCE_ERR_INVALID_ARG;
+  const int st = make_plan(n, d, v_shard, dtype, with_bwd, p);
+  if (st != FLCE_OK) return st;
+  *off_labels = p->total;
+  p->total += align_up(sizeof(int64_t) * static_cast<size_t>(n));
+  return FLCE_OK;
+}
+
+int call_fwd_shard(const void* h, const void* w_shard, const int64_t* labels, int64_t n, int64_t d, int64_t v_shard,
+                   int64_t v_first, flce_dtype dtype, int64_t ignore_index, float* lse_part_out, float* zy_part_out,
+                   hipStream_t stream) {
+  if (lse_part_out == nullptr || zy_part_out == nullptr) return FLCE_ERR_INVALID_ARG;
+  int st = check_common(h, w_shard, labels, n, d, v_shard, dtype, FLCE_SUM, lse_part_out, zy_part_out);
+  if (st != FLCE_OK) return st;
+  Plan p;
+  size_t off_labels = 0;
+  st = shard_plan(n, d, v_shard, v_first, dtype, ignore_index, 0, &p, &off_labels);
+  if (st != FLCE_OK) return st;
+  const int64_t* base_labels = labels;
+  return with_workspace(p, stream, [&](const Work& wk) {
+    int64_t* shifted = reinterpret_cast<int64_t*>(wk.base + off_labels);
+    hipError_t e = launch_shift_labels(base_labels, n, v_first, shifted, stream);
+    if (e != hipSuccess) return e;
+    return run(p, wk, h, w_shard, shifted, ignore_index - v_first, FLCE_SUM, nullptr, lse_part_out, nullptr,
+               nullptr, stream, zy_part_out);
+  });
+}
+
+int call_merge_shards(const float* lse_parts, const float* zy_parts, int64_t num_shards, const int64_t* labels,
+                      int64_t n, int64_t ignore_index, flce_reduction reduction, float* loss_out, float* lse_out,
+                      hipStream_t stream) {
+  if (lse_parts == nullptr || zy_parts == nullptr || labels == nullptr || loss_out == nullptr)
+    return FLCE_ERR_INVALID_ARG;
+  if (n <= 0 || num_shards <= 0 || num_shards > (int64_t(1) << 20) || !mul_ok(n, num_shards))
+    return FLCE_ERR_INVALID_ARG;
+  if (reduction != FLCE_MEAN && reduction != FLCE_SUM) return FLCE_ERR_INVALID_ARG;
+  if (!aligned(lse_parts, 4) || !aligned(zy_parts, 4) || !aligned(labels, 8) || !aligned(loss_out, 4) ||
+      (lse_out != nullptr && !aligned(lse_out, 4)))
+    return FLCE_ERR_ALIGNMENT;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FLCE_ERR_HIP;
+  hipMemPool_t pool;
+  if (device_pool(dev, &pool) != hipSuccess) return FLCE_ERR_HIP;
+  // workspace: n_valid, per-row loss, and the LSE when the caller wants none back
+  const size_t off_loss = kAlign;
+  const size_t off_lse = off_loss + align_up(sizeof(float) * static_cast<size_t>(n));
+  const size_t total = off_lse + sizeof(float) * static_cast<size_t>(n);
+  void* base = nullptr;
+  if (hipMallocFromPoolAsync(&base, total, pool, stream) != hipSuccess || base == nullptr) {
+    (void)hipGetLastError();
+    return FLCE_ERR_OOM;
+  }
+  char* b = static_cast<char*>(base);
+  int32_t* nvalid = reinterpret_cast<int32_t*>(b);
+  float* loss_rows = reinterpret_cast<float*>(b + off_loss);
+  float* lse = lse_out != nullptr ? lse_out : reinterpret_cast<float*>(b + off_lse);
+  hipError_t e = timed(K_LABEL_SCAN, stream, [&] { return launch_label_count(labels, n, ignore_index, nvalid, stream); });
+  if (e == hipSuccess)
+    e = timed(K_LSE_MERGE, stream, [&] {
+      return launch_shard_merge(lse_parts, zy_parts, num_shards, n, labels, ignore_index, lse, loss_rows, stream);
+    });
+  if (e == hipSuccess)
+    e = timed(K_LOSS, stream, [&] { return launch_loss_sum(loss_rows, n, nvalid, reduction, loss_out, stream); });
+  hipError_t f = hipFreeAsync(base, stream);
+  if (e != hipSuccess) return FLCE_ERR_HIP;
+  return status_of(f);
+}
+
+int call_bwd_shard(const void* h, const void* w_shard, const int64_t* labels, const float* lse, const float* grad_out,
+                   int64_t n, int64_t d, int64_t v_shard, int64_t v_first, flce_dtype dtype, int64_t ignore_index,
+                   flce_reduction reduction, float* dh_part_out, void* dw_shard_out, hipStream_t stream) {
+  if (lse == nullptr || dh_part_out == nullptr || dw_shard_out == nullptr) return FLCE_ERR_INVALID_ARG;
+  int st = check_common(h, w_shard, labels, n, d, v_shard, dtype, reduction, lse, nullptr);
+  if (st != FLCE_OK) return st;
+  if (!aligned(dh_part_out, 16) || !aligned(dw_shard_out, 16) || (grad_out != nullptr && !aligned(grad_out, 4)))
+    return FLCE_ERR_ALIGNMENT;
+  Plan p;
+  size_t off_labels = 0;
+  st = shard_plan(n, d, v_shard, v_first, dtype, ignore_index, 1, &p, &off_labels);
+  if (st != FLCE_OK) return st;
+  return with_workspace(p, stream, [&](const Work& wk) {
+    int64_t* shifted = reinterpret_cast<int64_t*>(wk.base + off_labels);
+    hipError_t e = launch_shift_labels(labels, n, v_first, shifted, stream);
+    if (e != hipSuccess) return e;
+    return run_bwd(p, wk, h, w_shard, shifted, lse, grad_out, ignore_index - v_first, reduction, dh_part_out,
+                   dw_shard_out, stream, 1);
+  });
+}
+
+int call_sum_parts(const float* parts, int64_t num_parts, int64_t count, flce_dtype dtype, void* out,
+                   hipStream_t stream) {
+  if (parts == nullptr || out == nullptr || num_parts <= 0 || count <= 0 || !mul_ok(num_parts, count))
+    return FLCE_ERR_INVALID_ARG;
+  if (dtype != FLCE_BF16 && dtype != FLCE_F32) return FLCE_ERR_INVALID_ARG;
+  if (!aligned(parts, 4) || !aligned(out, dtype == FLCE_BF16 ? 2 : 4)) return FLCE_ERR_ALIGNMENT;
+  return status_of(timed(K_DH_REDUCE, stream, [&] { return launch_sum_parts(parts, num_parts, count, dtype, out, stream); }));
+}
+
 }  // namespace
 }  // namespace flce
 
@@ -434,6 +550,32 @@ int flce_ce_logits(const void* logits, const int64_t* labels, int64_t n, int64_t
                    float* loss_out, float* lse_out, void* grad_out, hipStream_t stream) {
   return flce::call_ce_logits(logits, labels, n, v, dtype, ignore_index, reduction, lse_in, grad_scale, loss_out,
                               lse_out, grad_out, stream);
+}
+
+int flce_fwd_shard(const void* h, const void* w_shard, const int64_t* labels, int64_t n, int64_t d, int64_t v_shard,
+                   int64_t v_first, flce_dtype dtype, int64_t ignore_index, float* lse_part_out, float* zy_part_out,
+                   hipStream_t stream) {
+  return flce::call_fwd_shard(h, w_shard, labels, n, d, v_shard, v_first, dtype, ignore_index, lse_part_out,
+                              zy_part_out, stream);
+}
+
+int flce_merge_shards(const float* lse_parts, const float* zy_parts, int64_t num_shards, const int64_t* labels,
+                      int64_t n, int64_t ignore_index, flce_reduction reduction, float* loss_out, float* lse_out,
+                      hipStream_t stream) {
+  return flce::call_merge_shards(lse_parts, zy_parts, num_shards, labels, n, ignore_index, reduction, loss_out,
+                                 lse_out, stream);
+}
+
+int flce_bwd_shard(const void* h, const void* w_shard, const int64_t* labels, const float* lse, const float* grad_out,
+                   int64_t n, int64_t d, int64_t v_shard, int64_t v_first, flce_dtype dtype, int64_t ignore_index,
+                   flce_reduction reduction, float* dh_part_out, void* dw_shard_out, hipStream_t stream) {
+  return flce::call_bwd_shard(h, w_shard, labels, lse, grad_out, n, d, v_shard, v_first, dtype, ignore_index,
+                              reduction, dh_part_out, dw_shard_out, stream);
+}
+
+int flce_sum_parts(const float* parts, int64_t num_parts, int64_t count, flce_dtype dtype, void* out,
+                   hipStream_t stream) {
+  return flce::call_sum_parts(parts, num_parts, count, dtype, out, stream);
 }
 
 size_t flce_workspace_bytes(int64_t n, int64_t d, int64_t v, flce_dtype dtype, int with_bwd) {

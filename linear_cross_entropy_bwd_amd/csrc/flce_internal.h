@@ -44,6 +44,7 @@ int make_plan(int64_t n, int64_t d, int64_t v, int32_t dtype, int32_t with_bwd, 
 
 // Pointers into the workspace for one call.
 struct Work {
+  char* base;        // the call's whole workspace
   int32_t* nvalid;   // [1]
   float* zy;         // [C]   target logit of each chunk row (0 until found)
   float* gy;         // [C]   gradient value at the target column
@@ -93,6 +94,8 @@ struct ChunkArgs {
   int32_t dw_mode;
   const float* lse_in;      // chunk's slice of the saved LSE (recompute backward), else nullptr
   const float* grad_out;    // upstream gradient of the loss (device scalar) or nullptr for 1
+  float* zy_rows;           // chunk's slice of a per-row target-logit output, or nullptr
+  int32_t dh_f32;           // 1: dh is an fp32 array whatever the dtype (a shard's dH partial)
 };
 
 // --- launchers (each returns the launch status) ---------------------------------
@@ -107,6 +110,13 @@ hipError_t launch_dh_reduce(const Plan& p, const Work& w, const ChunkArgs& a, hi
 hipError_t launch_label_count(const int64_t* labels, int64_t n, int64_t ignore_index, int32_t* nvalid, hipStream_t s);
 hipError_t launch_loss_sum(const float* loss_rows, int64_t n, const int32_t* nvalid, int32_t reduction,
                            float* loss_out, hipStream_t s);
+// Vocabulary shards.
+hipError_t launch_shift_labels(const int64_t* labels, int64_t n, int64_t first, int64_t* out, hipStream_t s);
+hipError_t launch_shard_merge(const float* lse_parts, const float* zy_parts, int64_t shards, int64_t n,
+                              const int64_t* labels, int64_t ignore_index, float* lse_out, float* loss_rows,
+                              hipStream_t s);
+hipError_t launch_sum_parts(const float* parts, int64_t num_parts, int64_t count, int32_t dtype, void* out,
+                            hipStream_t s);
 
 // Cross-entropy on given logits (ce_logits.hip).
 struct CeArgs {

@@ -52,7 +52,7 @@ __global__ __launch_bounds__(kMergeRows* kMergeSlices) void lse_merge_kernel(
     float* __restrict__ pm, const float* __restrict__ ps, int64_t C, int64_t G, int64_t rows,
     const int64_t* __restrict__ labels, int64_t ignore_index, int64_t v, const int32_t* __restrict__ nvalid,
     int32_t reduction, float* __restrict__ zy, float* __restrict__ gy, float* __restrict__ lse_rows,
-    float* __restrict__ loss_rows, int with_grad) {
+    float* __restrict__ loss_rows, float* __restrict__ zy_rows, int with_grad) {
   __shared__ float red[kMergeSlices][kMergeRows];
   __shared__ float row_lse[kMergeRows];
   const int r = threadIdx.x % kMergeRows;
@@ -89,6 +89,7 @@ __global__ __launch_bounds__(kMergeRows* kMergeSlices) void lse_merge_kernel(
       zy[t] = 0.0f;  // ready for the next chunk
       lse_rows[t] = l;
       loss_rows[t] = valid ? l - z : 0.0f;
+      if (zy_rows != nullptr) zy_rows[t] = valid ? z : 0.0f;
       if (with_grad) {
         const float sc = valid ? row_scale(*nvalid, reduction) : 0.0f;
         const bool hit = valid && y >= 0 && y < v;
@@ -177,6 +178,37 @@ __global__ __launch_bounds__(256) void dh_reduce_kernel(const float* __restrict_
   Elem<TO>::st(out, i, acc);
 }
 
+// Labels of a vocabulary shard: id - first (wrapping), so that a label in the
+// shard becomes its row in the shard's W and every other label falls outside
+// [0, v_shard); the ignore value is shifted alike by the caller.
+__global__ __launch_bounds__(256) void shift_labels_kernel(const int64_t* __restrict__ labels, int64_t n,
+                                                           int64_t first, int64_t* __restrict__ out) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i < n) out[i] = static_cast<int64_t>(static_cast<uint64_t>(labels[i]) - static_cast<uint64_t>(first));
+}
+
+// Merge the per-shard partials of each row: lse = log sum_p exp(lse_p) (max
+// first), the target logit is the one shard's value that holds the label (the
+// others hold 0), and the row's NLL lse - z_y.
+__global__ __launch_bounds__(256) void shard_merge_kernel(const float* __restrict__ lse_parts,
+                                                          const float* __restrict__ zy_parts, int64_t shards,
+                                                          int64_t n, const int64_t* __restrict__ labels,
+                                                          int64_t ignore_index, float* __restrict__ lse_out,
+                                                          float* __restrict__ loss_rows) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= n) return;
+  float m = -INFINITY;
+  for (int64_t q = 0; q < shards; ++q) m = fmaxf(m, lse_parts[q * n + i]);
+  float sum = 0.0f, zy = 0.0f;
+  for (int64_t q = 0; q < shards; ++q) {
+    sum += m == -INFINITY ? 0.0f : fast_exp(lse_parts[q * n + i] - m);
+    zy += zy_parts[q * n + i];
+  }
+  const float l = m + logf(sum);
+  lse_out[i] = l;
+  loss_rows[i] = labels[i] != ignore_index ? l - zy : 0.0f;
+}
+
 // loss = scale * sum_i loss_rows[i], summed in fp64 in a fixed order.
 __global__ __launch_bounds__(1024) void loss_reduce_kernel(const float* __restrict__ loss_rows, int64_t n,
                                                            const int32_t* __restrict__ nvalid, int32_t reduction,
@@ -209,7 +241,7 @@ hipError_t launch_lse_merge(const Plan& p, const Work& w, const ChunkArgs& a, in
   const int64_t blocks = (a.rows + kMergeRows - 1) / kMergeRows;
   lse_merge_kernel<<<static_cast<unsigned>(blocks), kMergeRows * kMergeSlices, 0, s>>>(
       w.pm, w.ps, p.chunk, p.ngroups, a.rows, a.labels, a.ignore_index, p.v, w.nvalid, a.reduction, w.zy, w.gy,
-      a.lse_rows, w.loss_rows + a.row0, with_grad);
+      a.lse_rows, w.loss_rows + a.row0, a.zy_rows, with_grad);
   return hipGetLastError();
 }
 
@@ -227,7 +259,7 @@ hipError_t launch_grad(const Plan& p, const Work& w, const ChunkArgs& a, hipStre
 hipError_t launch_dh_reduce(const Plan& p, const Work& w, const ChunkArgs& a, hipStream_t s) {
   const int64_t count = a.rows * p.d;
   const unsigned blocks = static_cast<unsigned>((count + 255) / 256);
-  if (p.dtype == FLCE_BF16)
+  if (p.dtype == FLCE_BF16 && !a.dh_f32)
     dh_reduce_kernel<bf16_t><<<blocks, 256, 0, s>>>(w.dhpart, p.dh_splits, p.chunk * p.d, count,
                                                     static_cast<bf16_t*>(a.dh));
   else
@@ -253,6 +285,29 @@ hipError_t launch_label_count(const int64_t* labels, int64_t n, int64_t ignore_i
 hipError_t launch_loss_sum(const float* loss_rows, int64_t n, const int32_t* nvalid, int32_t reduction,
                            float* loss_out, hipStream_t s) {
   loss_reduce_kernel<<<1, 1024, 0, s>>>(loss_rows, n, nvalid, reduction, loss_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_shift_labels(const int64_t* labels, int64_t n, int64_t first, int64_t* out, hipStream_t s) {
+  shift_labels_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(labels, n, first, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_shard_merge(const float* lse_parts, const float* zy_parts, int64_t shards, int64_t n,
+                              const int64_t* labels, int64_t ignore_index, float* lse_out, float* loss_rows,
+                              hipStream_t s) {
+  shard_merge_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(lse_parts, zy_parts, shards, n, labels,
+                                                                             ignore_index, lse_out, loss_rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_sum_parts(const float* parts, int64_t num_parts, int64_t count, int32_t dtype, void* out,
+                            hipStream_t s) {
+  const unsigned blocks = static_cast<unsigned>((count + 255) / 256);
+  if (dtype == FLCE_BF16)
+    dh_reduce_kernel<bf16_t><<<blocks, 256, 0, s>>>(parts, num_parts, count, count, static_cast<bf16_t*>(out));
+  else
+    dh_reduce_kernel<float><<<blocks, 256, 0, s>>>(parts, num_parts, count, count, static_cast<float*>(out));
   return hipGetLastError();
 }
 

@@ -8,6 +8,9 @@ from .flce_oracle import (  # noqa: F401
     flce_dw_rows,
     flce_rows,
     log_sum_exp,
+    merge_vocab_shards,
     reduction_scale,
     valid_rows,
+    vocab_shard_backward,
+    vocab_shard_partials,
 )

@@ -30,6 +30,14 @@ written from the pages:
   ``LigerCrossEntropyLoss`` example of the lecture page, a drop-in for
   PyTorch's loss on a ``[B*S, vocab]`` logits view): the same LSE, target and
   gradient formulas applied to a given ``[N, V]`` logits array;
+* the vocabulary split the lecture page leaves open for vocabularies of a
+  million ids ("GPU MODE lecture 028 - Liger Kernel", open questions): each
+  contiguous shard of W's rows yields a per-row partial LSE and, where the
+  label falls in it, the target logit; the whole-vocabulary LSE is the LSE of
+  the partial LSEs (the merge of the blog page's section "1. Fused Linear
+  Cross-Entropy with Online LogSumExp", step 3, taken over shards instead of
+  tiles), and a shard's gradient is the softmax-minus-one-hot formula on its
+  own columns with the merged LSE;
 * ``reduction="mean"`` as in the loss module call on the lecture page
   ("GPU MODE lecture 028 - Liger Kernel", the LigerCrossEntropyLoss example);
   the mean is taken over the rows whose label is not ``ignore_index``, and a
@@ -268,3 +276,67 @@ def ce_on_logits(z, labels, ignore_index: int = IGNORE_INDEX, reduction: str = "
     g[~valid] = 0.0
     g *= scale
     return loss, lse, g
+
+
+def vocab_shard_partials(h, w_shard, labels, v_first: int, ignore_index: int = IGNORE_INDEX,
+                         v_total: int | None = None):
+    """One vocabulary shard's partials: (lse_part[N], zy_part[N]) float64.
+
+    ``w_shard`` holds the rows ``v_first .. v_first + v_shard - 1`` of W.
+    lse_part is the log-sum-exp of the row's logits over the shard's columns;
+    zy_part is the target logit when the row's label lies in the shard, else
+    0 (also 0 for ignored rows).  Labels are whole-vocabulary ids, checked
+    against ``v_total`` when given.
+    """
+    hd, wd, y = _as_f64(h), _as_f64(w_shard), _as_labels(labels)
+    v_shard = wd.shape[0]
+    valid = valid_rows(y, v_total, ignore_index) if v_total is not None else y != ignore_index
+    z = hd @ wd.T                                   # the shard's logits, all rows
+    lse_part = log_sum_exp(z)
+    local = y - int(v_first)
+    here = np.flatnonzero(valid & (local >= 0) & (local < v_shard))
+    zy_part = np.zeros(y.shape[0], dtype=np.float64)
+    zy_part[here] = z[here, local[here]]
+    return lse_part, zy_part
+
+
+def merge_vocab_shards(lse_parts, zy_parts, labels, ignore_index: int = IGNORE_INDEX, reduction: str = "mean"):
+    """(loss, lse[N]) float64 from the shards' partials ([shards, N] each).
+
+    lse = log sum_q exp(lse_q) (largest partial factored out first); the
+    target logit is the one shard's nonzero entry, i.e. the sum over shards;
+    the loss reduces lse - z_y over the valid rows.
+    """
+    lp = np.asarray(lse_parts, dtype=np.float64)
+    zp = np.asarray(zy_parts, dtype=np.float64)
+    y = _as_labels(labels)
+    valid = y != ignore_index
+    scale = reduction_scale(int(valid.sum()), reduction)
+    m = lp.max(axis=0)
+    lse = m + np.log(np.exp(lp - m[None, :]).sum(axis=0))
+    zy = zp.sum(axis=0)
+    loss = scale * float(np.sum(lse[valid] - zy[valid]))
+    return loss, lse
+
+
+def vocab_shard_backward(h, w_shard, labels, lse, v_first: int, grad_out: float = 1.0,
+                         ignore_index: int = IGNORE_INDEX, reduction: str = "mean"):
+    """(dH_part[N, D], dW_shard[v_shard, D]) float64 of ``grad_out * loss`` for one shard.
+
+    G_q = (exp(z_q - lse) - onehot) * scale * grad_out over the shard's columns
+    only, with the whole-vocabulary LSE; dH = sum over shards of G_q W_q and
+    dW's rows of the shard are G_q^T H.
+    """
+    hd, wd, y = _as_f64(h), _as_f64(w_shard), _as_labels(labels)
+    v_shard = wd.shape[0]
+    lse = np.asarray(lse, dtype=np.float64)
+    valid = y != ignore_index
+    scale = float(grad_out) * reduction_scale(int(valid.sum()), reduction)
+    g = np.exp(hd @ wd.T - lse[:, None])
+    local = y - int(v_first)
+    here = np.flatnonzero(valid & (local >= 0) & (local < v_shard))
+    g[here, local[here]] -= 1.0
+    g[~valid] = 0.0
+    g *= scale
+    return g @ wd, g.T @ hd
+

@@ -158,6 +158,66 @@ def test_ce_logits_argument_errors_before_any_device_work():
     assert call(lse_out=A + 2) == flce.FLCE_ERR_ALIGNMENT
 
 
+def test_shard_argument_errors_before_any_device_work():
+    A = 1 << 20
+    fw = dict(h=A, w_shard=A, labels=A, n=4, d=64, v_shard=300, v_first=1000, dtype=flce.FLCE_BF16,
+              ignore_index=-100, lse_part_out=A, zy_part_out=A, stream=None)
+
+    def fwd(**kw):
+        a = dict(fw)
+        a.update(kw)
+        return flce.flce_fwd_shard(**a)
+
+    assert fwd(lse_part_out=None) == flce.FLCE_ERR_INVALID_ARG
+    assert fwd(zy_part_out=None) == flce.FLCE_ERR_INVALID_ARG
+    assert fwd(v_first=-1) == flce.FLCE_ERR_INVALID_ARG
+    assert fwd(v_shard=0) == flce.FLCE_ERR_INVALID_ARG
+    assert fwd(ignore_index=-(1 << 63)) == flce.FLCE_ERR_INVALID_ARG     # shifted ignore value would wrap
+    assert fwd(w_shard=A + 8) == flce.FLCE_ERR_ALIGNMENT
+    assert fwd(zy_part_out=A + 2) == flce.FLCE_ERR_ALIGNMENT
+
+    mg = dict(lse_parts=A, zy_parts=A, num_shards=3, labels=A, n=4, ignore_index=-100, reduction=flce.FLCE_MEAN,
+              loss_out=A, lse_out=None, stream=None)
+
+    def merge(**kw):
+        a = dict(mg)
+        a.update(kw)
+        return flce.flce_merge_shards(**a)
+
+    assert merge(num_shards=0) == flce.FLCE_ERR_INVALID_ARG
+    assert merge(loss_out=None) == flce.FLCE_ERR_INVALID_ARG
+    assert merge(reduction=5) == flce.FLCE_ERR_INVALID_ARG
+    assert merge(labels=A + 4) == flce.FLCE_ERR_ALIGNMENT
+
+    bw = dict(h=A, w_shard=A, labels=A, lse=A, grad_out=None, n=4, d=64, v_shard=300, v_first=0,
+              dtype=flce.FLCE_BF16, ignore_index=-100, reduction=flce.FLCE_SUM, dh_part_out=A, dw_shard_out=A,
+              stream=None)
+
+    def bwd(**kw):
+        a = dict(bw)
+        a.update(kw)
+        return flce.flce_bwd_shard(**a)
+
+    assert bwd(lse=None) == flce.FLCE_ERR_INVALID_ARG
+    assert bwd(dh_part_out=None) == flce.FLCE_ERR_INVALID_ARG
+    assert bwd(v_first=-5) == flce.FLCE_ERR_INVALID_ARG
+    assert bwd(dh_part_out=A + 4) == flce.FLCE_ERR_ALIGNMENT
+    assert bwd(grad_out=A + 2) == flce.FLCE_ERR_ALIGNMENT
+
+    assert flce.flce_sum_parts(A, 0, 10, flce.FLCE_BF16, A, None) == flce.FLCE_ERR_INVALID_ARG
+    assert flce.flce_sum_parts(None, 2, 10, flce.FLCE_BF16, A, None) == flce.FLCE_ERR_INVALID_ARG
+    assert flce.flce_sum_parts(A, 2, 10, 7, A, None) == flce.FLCE_ERR_INVALID_ARG
+    assert flce.flce_sum_parts(A, 2, 10, flce.FLCE_F32, A + 2, None) == flce.FLCE_ERR_ALIGNMENT
+
+
+def test_vocab_shard_bounds():
+    assert flce.vocab_shard_bounds(128256, 8)[0] == (0, 15872)
+    for v, q in [(128256, 8), (1000, 3), (5, 5), (1 << 20, 7), (300, 2)]:
+        b = flce.vocab_shard_bounds(v, q)
+        assert len(b) == q and b[0][0] == 0 and b[-1][1] == v
+        assert all(x < y for x, y in b) and all(b[i][1] == b[i + 1][0] for i in range(q - 1))
+
+
 def test_no_cpu_fallback(monkeypatch, tmp_path):
     """Without the built library the binding raises instead of computing anything."""
     monkeypatch.setattr(flce, "_lib", None)

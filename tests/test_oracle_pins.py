@@ -18,7 +18,7 @@ import pytest
 import torch
 
 from oracle import (ce_on_logits, flce_backward_from_lse, flce_dw_rows, flce_forward, flce_forward_backward, flce_rows,
-                    log_sum_exp)
+                    log_sum_exp, merge_vocab_shards, vocab_shard_backward, vocab_shard_partials)
 
 RTOL = 1e-12
 
@@ -442,3 +442,72 @@ def test_ce_on_logits_uniform_closed_form():
     ref[[0, 1, 3, 4], [0, 3, 7, 7]] -= 1.0
     ref[2] = 0.0
     _close(grad, ref / 4.0)
+
+
+# --- vocabulary shards ------------------------------------------------------------
+
+SHARD_CUTS = [
+    (0, 64),                 # one shard: the unsharded problem
+    (0, 20, 41, 64),         # uneven shards
+    (0, 1, 2, 63, 64),       # one-column shards at both ends
+]
+
+
+def _shards(h, w, y, cuts, reduction="mean"):
+    parts = [vocab_shard_partials(h, w[a:b], y, a, v_total=w.shape[0]) for a, b in zip(cuts[:-1], cuts[1:])]
+    loss, lse = merge_vocab_shards([p[0] for p in parts], [p[1] for p in parts], y, reduction=reduction)
+    return parts, loss, lse
+
+
+@pytest.mark.parametrize("cuts", SHARD_CUTS)
+@pytest.mark.parametrize("reduction", ["mean", "sum"])
+def test_vocab_shards_forward_torch(cuts, reduction):
+    """Library routine: the merged shards give torch's float64 cross-entropy and logsumexp
+    over the whole vocabulary, and each partial is torch's logsumexp over its columns."""
+    n, d, v = 19, 6, 64
+    h, w, y = _rand(50, n, d, v, sigma_w=0.8, ignore=(2, 11))
+    y[[0, 1]] = [0, v - 1]                      # labels at both vocabulary ends
+    parts, loss, lse = _shards(h, w, y, cuts, reduction)
+    zt = torch.tensor(h) @ torch.tensor(w).T
+    ref = torch.nn.functional.cross_entropy(zt, torch.tensor(y), ignore_index=-100, reduction=reduction)
+    assert loss == pytest.approx(ref.item(), rel=1e-12)
+    _close(lse, torch.logsumexp(zt, dim=1).numpy())
+    for (a, b), (lp, zp) in zip(zip(cuts[:-1], cuts[1:]), parts):
+        _close(lp, torch.logsumexp(zt[:, a:b], dim=1).numpy())
+        inside = (y >= a) & (y < b)
+        assert np.all(zp[~inside] == 0.0)
+
+
+@pytest.mark.parametrize("cuts", SHARD_CUTS[1:])
+def test_vocab_shards_backward_torch_autograd(cuts):
+    """Library routine: torch autograd of grad_out * cross-entropy (float64): the shards'
+    dH terms sum to dH and their dW blocks are dW's rows."""
+    n, d, v = 17, 5, 64
+    h, w, y = _rand(51, n, d, v, sigma_w=0.6, ignore=(4,))
+    _, _, lse = _shards(h, w, y, cuts)
+    g_up = 1.7
+    outs = [vocab_shard_backward(h, w[a:b], y, lse, a, grad_out=g_up) for a, b in zip(cuts[:-1], cuts[1:])]
+    ht = torch.tensor(h, requires_grad=True)
+    wt = torch.tensor(w, requires_grad=True)
+    lt = torch.nn.functional.cross_entropy(ht @ wt.T, torch.tensor(y), ignore_index=-100)
+    lt.backward(torch.tensor(g_up, dtype=torch.float64))
+    _close(sum(o[0] for o in outs), ht.grad.numpy())
+    _close(np.concatenate([o[1] for o in outs]), wt.grad.numpy())
+
+
+def test_vocab_shards_label_free_shard_and_ignored_rows():
+    """Closed form: a shard that holds no label has zy_part = 0 and, with every row
+    ignored, no gradient; a shard's dW block without labels is sum_i P_ij H_i * scale."""
+    n, d, v = 8, 3, 12
+    h, w, y = _rand(52, n, d, v)
+    y[:] = 1                                     # every label in the first shard
+    lse_full = log_sum_exp(h @ w.T)
+    lp, zp = vocab_shard_partials(h, w[6:], y, 6)
+    assert np.all(zp == 0.0)
+    _, dw_q = vocab_shard_backward(h, w[6:], y, lse_full, 6)
+    p = np.exp(h @ w[6:].T - lse_full[:, None])
+    _close(dw_q, p.T @ h / n)
+    y_ign = np.full(n, -100)
+    dh0, dw0 = vocab_shard_backward(h, w[6:], y_ign, lse_full, 6)
+    assert np.all(dh0 == 0.0) and np.all(dw0 == 0.0)
+
