@@ -269,6 +269,13 @@ __device__ __forceinline__ void wait_stages(int n) {
   }
 }
 
+// s_waitcnt vmcnt(N) for a compile-time N < 64, lgkmcnt and expcnt left alone.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
 // Workgroup barrier without the memory fence of __syncthreads(): the direct
 // loads are waited for explicitly.  The wave's own LDS reads complete first,
 // so that a slot the barrier frees is no longer being read by anyone.  The
@@ -726,26 +733,44 @@ __device__ __forceinline__ void dw_epilogue_tiled(const DwArgs& a, Acc& acc, int
   constexpr bool keep_split = MODE == DW_FIRST || MODE == DW_MID;
   // block b = (i, p) = (b / 2, b % 2) starts at row 32 i, column 64 p of the wave's quadrant
   auto block_off = [&](int b) { return (32 * (b >> 1)) * row_bytes + 128 * (b & 1); };
-  uint4 buf[2][2][4];
-  auto fetch = [&](int b, uint4 (&dst)[2][4]) {
+  // The stored sums of the next kAhead blocks are in flight while a block is
+  // finished.  They travel by direct loads into this wave's 32 KB of the idle
+  // operand ring (slot 1 + wave: four 8 KB block buffers of eight 1 KB pieces,
+  // lane L's 16 bytes at L * 16), so they hold no registers: register-held
+  // prefetches were waited for one load at a time once the accumulators had
+  // taken the register file.
+  constexpr int kAhead = 3;
+  constexpr int kStoresPerBlock = keep_split ? 8 : 4;
+  char* fold_lds = reinterpret_cast<char*>(ring()[1 + wave]);
+  auto fetch = [&](auto b) {
     char* hb = hi_base + block_off(b);
     char* lb = lo_base + block_off(b);
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      dst[u][0] = *dw_piece(hb, row_bytes, u, 0, lane_off);
-      dst[u][1] = *dw_piece(hb, row_bytes, u, 1, lane_off);
-      dst[u][2] = *dw_piece(lb, row_bytes, u, 0, lane_off);
-      dst[u][3] = *dw_piece(lb, row_bytes, u, 1, lane_off);
-    }
+    char* dst = fold_lds + (b % (kAhead + 1)) * 8192;
+    static_for<2>([&](auto u) {
+      __builtin_amdgcn_global_load_lds(dw_piece(hb, row_bytes, u, 0, lane_off), FLCE_LDS(dst + (4 * u + 0) * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(dw_piece(hb, row_bytes, u, 1, lane_off), FLCE_LDS(dst + (4 * u + 1) * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(dw_piece(lb, row_bytes, u, 0, lane_off), FLCE_LDS(dst + (4 * u + 2) * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(dw_piece(lb, row_bytes, u, 1, lane_off), FLCE_LDS(dst + (4 * u + 3) * 1024), 16, 0, 0);
+    });
   };
-  if constexpr (fold) fetch(0, buf[0]);
+  if constexpr (fold) {
+    // every wave has waited for its own loads into the ring and finished reading it
+    __builtin_amdgcn_s_barrier();
+    static_for<kAhead>([&](auto B) { fetch(B); });
+  }
   static_for<8>([&](auto B) {
     constexpr int I = B / 2, P = B % 2;
     if constexpr (fold) {
-      // the next block's stored sum is in flight while this one is finished
-      if constexpr (B < 7) fetch(B + 1, buf[(B + 1) & 1]);
+      if constexpr (B + kAhead < 8) fetch(std::integral_constant<int, B + kAhead>{});
+      // Memory operations issued after block B's eight loads: the loads of the
+      // blocks ahead of it and the result stores of the blocks finished since.
+      constexpr int ahead = (B + kAhead < 8 ? B + kAhead : 7) - B;
+      constexpr int done = B < kAhead ? B : kAhead;
+      wait_vm<8 * ahead + kStoresPerBlock * done>();
+      const char* src = fold_lds + (B % (kAhead + 1)) * 8192 + lane * 16;
       static_for<2>([&](auto U) {
-        add_pair(acc.c[I][2 * P + U], buf[B & 1][U][0], buf[B & 1][U][1], buf[B & 1][U][2], buf[B & 1][U][3]);
+        const uint4* q = reinterpret_cast<const uint4*>(src + 4 * U * 1024);
+        add_pair(acc.c[I][2 * P + U], q[0], q[64], q[128], q[192]);
       });
     }
     if constexpr (keep_split) {
@@ -779,12 +804,30 @@ __device__ __forceinline__ void dw_epilogue_tiled(const DwArgs& a, Acc& acc, int
         });
       });
       __builtin_amdgcn_wave_barrier();
+      // The four row reads are asm so that the compiler does not wait for the
+      // direct loads still filling the fold buffers, which it cannot tell apart
+      // from this scratch; the asm waits for its own reads only.
+      const int c = lane & 7;
+      uint32_t ra[4];
       static_for<4>([&](auto Rr) {
-        const int rb = 8 * Rr + (lane >> 3), c = lane & 7;
-        const uint4 v = *reinterpret_cast<const uint4*>(blk + rb * 128 + ((c ^ (rb & 7)) * 16));
+        const int rb = 8 * Rr + (lane >> 3);
+        ra[Rr] = lds_addr(blk + rb * 128 + ((c ^ (rb & 7)) * 16));
+      });
+      uint4 v[4];
+      asm volatile(
+          "ds_read_b128 %0, %4\n\t"
+          "ds_read_b128 %1, %5\n\t"
+          "ds_read_b128 %2, %6\n\t"
+          "ds_read_b128 %3, %7\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+          : "v"(ra[0]), "v"(ra[1]), "v"(ra[2]), "v"(ra[3])
+          : "memory");
+      static_for<4>([&](auto Rr) {
+        const int rb = 8 * Rr + (lane >> 3);
         const int64_t row = m0 + wm * 128 + I * 32 + rb;
         const int64_t col = n0 + wn * 128 + 64 * P + 8 * c;
-        *reinterpret_cast<uint4*>(a.out + row * a.d + col) = v;
+        *reinterpret_cast<uint4*>(a.out + row * a.d + col) = v[Rr];
       });
     }
   });
