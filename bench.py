@@ -20,7 +20,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "fused linear-CE fwd+bwd tokens/s (N=8192,D=4096,V=128256 bf16); MFMA %"
-PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}      # MI355X dense matrix peaks
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3, "fp8": 5000.0}      # MI355X dense matrix peaks
 GEMM_KINDS = ("logits_lse", "dh_gemm", "dw_gemm")
 COPY_BYTES = 1 << 30
 HBM_PEAK_GBPS = 8000.0                               # MI355X HBM3E
@@ -70,6 +70,44 @@ def cpu_baseline(wl, h, w, y, rows: int):
     return {"value": rows / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"first {rows} of {wl.n} tokens of {wl.name} (full D={wl.d}, V={wl.v}), fp64 numpy, "
                       f"{dt:.1f} s incl. fp64 conversion"}
+
+
+def fp8_forward_measure(flce, torch, wl, args, stream):
+    """flce_fwd_fp8 on this workload's H and W quantised row by row to e4m3:
+    2 N D V flop against the fp8 matrix peak."""
+    from workloads import make_inputs_fp8
+    hq, hs, wq, ws, y = make_inputs_fp8(wl)
+    dev = torch.device("cuda:0")
+    hq, hs, wq, ws, y = hq.to(dev), hs.to(dev), wq.to(dev), ws.to(dev), y.to(dev)
+    for _ in range(max(1, args.warmup)):
+        flce.linear_cross_entropy_forward_fp8(hq, hs, wq, ws, y, reduction=wl.reduction)
+    torch.cuda.synchronize()
+    flce.flce_profile_read()
+    flce.flce_profile_enable(True)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        flce.linear_cross_entropy_forward_fp8(hq, hs, wq, ws, y, reduction=wl.reduction)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    flce.flce_profile_enable(False)
+    kern = flce.flce_profile_read()
+    ms = e0.elapsed_time(e1) / args.steps
+    flop = 2.0 * wl.n * wl.d * wl.v
+    launches, lg_ms = kern.get("logits_lse", (0, 0.0))
+    lg_avg = lg_ms / max(launches, 1)
+    flop_launch = flop / max(launches // args.steps, 1)
+    log(f"[bench] fp8 forward: {ms:.3f} ms/call, logits launch {lg_avg:.3f} ms")
+    return {
+        "ms_per_call": ms,
+        "tflops_2ndv": flop / (ms * 1e-3) / 1e12,
+        "peak_tflops": PEAK_TFLOPS["fp8"],
+        "mfma_pct_2ndv": 100.0 * flop / (ms * 1e-3) / (PEAK_TFLOPS["fp8"] * 1e12),
+        "logits_launch_ms": lg_avg,
+        "logits_frac": flop_launch / (lg_avg * 1e-3) / (PEAK_TFLOPS["fp8"] * 1e12),
+        "inputs": "H and W quantised per row to e4m3 (scale max|row|/448)",
+    }
 
 
 def ce_logits_measure(flce, torch, hd, wd, yd, wl, args, stream):
@@ -344,6 +382,7 @@ def main() -> int:
         "shards": flce.vocab_shard_bounds(wl.v, 8),
         "path": "flce_fwd_shard x8, flce_merge_shards, flce_bwd_shard x8, flce_sum_parts",
     }
+    result["forward_fp8"] = fp8_forward_measure(flce, torch, wl, args, stream)
     result["ce_logits"] = ce_logits_measure(flce, torch, hd, wd, yd, wl, args, stream)
     if not args.no_cpu_baseline:
         log(f"[bench] CPU baseline: oracle on {args.cpu_rows} rows")

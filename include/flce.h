@@ -169,6 +169,27 @@ int flce_ce_logits(const void* logits, const int64_t* labels, int64_t n, int64_t
                    float* loss_out, float* lse_out, void* grad_out, hipStream_t stream);
 
 /*
+ * Forward (loss and per-row LSE) from FP8 inputs: H and W as OCP e4m3 bytes
+ * (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; 0x7f/0xff are NaN),
+ * each row with an fp32 scale, so that
+ *   z_ij = h_scale[i] * w_scale[j] * sum_k e4m3(h_q[i, k]) * e4m3(w_q[j, k]).
+ * The pages raise FP8 only as an open question of the lecture page "GPU MODE
+ * lecture 028 - Liger Kernel" (FP8 training on newer GPUs) and give no method;
+ * this call takes quantised inputs and computes exactly the loss of
+ * flce_fwd on the dequantised H and W: the products are exact and accumulate
+ * in fp32 on the matrix cores' fp8 instructions; the online LSE, target
+ * extraction and loss are those of flce_fwd.
+ *
+ *   h_q      device, [n, d] e4m3 bytes, 16-byte aligned;  h_scale  device, fp32 [n].
+ *   w_q      device, [v, d] e4m3 bytes, 16-byte aligned;  w_scale  device, fp32 [v], 16-byte aligned.
+ *   d        a multiple of 16 (FLCE_ERR_ALIGNMENT otherwise).
+ * labels, ignore_index, reduction, loss_out, lse_out, stream and errors as for flce_fwd.
+ */
+int flce_fwd_fp8(const void* h_q, const float* h_scale, const void* w_q, const float* w_scale, const int64_t* labels,
+                 int64_t n, int64_t d, int64_t v, int64_t ignore_index, flce_reduction reduction, float* loss_out,
+                 float* lse_out, hipStream_t stream);
+
+/*
  * Vocabulary shards.  The vocabulary rows of W are split into contiguous
  * shards [v_first, v_first + v_shard); each shard's partial statistics are
  * computed on its own and merged exactly, because the log-sum-exp of a row is

@@ -27,6 +27,7 @@ EXPORTED = (
     "flce_fwd",
     "flce_bwd",
     "flce_ce_logits",
+    "flce_fwd_fp8",
     "flce_fwd_shard",
     "flce_merge_shards",
     "flce_bwd_shard",
@@ -84,6 +85,8 @@ def lib() -> ctypes.CDLL:
     L.flce_bwd.restype = i32
     L.flce_ce_logits.argtypes = [p, p, i64, i64, i32, i64, i32, p, p, p, p, p, p]
     L.flce_ce_logits.restype = i32
+    L.flce_fwd_fp8.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i32, p, p, p]
+    L.flce_fwd_fp8.restype = i32
     L.flce_fwd_shard.argtypes = [p, p, p, i64, i64, i64, i64, i32, i64, p, p, p]
     L.flce_fwd_shard.restype = i32
     L.flce_merge_shards.argtypes = [p, p, i64, p, i64, i64, i32, p, p, p]
@@ -156,6 +159,12 @@ def flce_ce_logits(logits, labels, n, v, dtype, ignore_index, reduction, lse_in,
                    grad_out, stream) -> int:
     return lib().flce_ce_logits(_ptr(logits), _ptr(labels), n, v, dtype, ignore_index, reduction, _ptr(lse_in),
                                 _ptr(grad_scale), _ptr(loss_out), _ptr(lse_out), _ptr(grad_out), _stream(stream))
+
+
+def flce_fwd_fp8(h_q, h_scale, w_q, w_scale, labels, n, d, v, ignore_index, reduction, loss_out, lse_out,
+                 stream) -> int:
+    return lib().flce_fwd_fp8(_ptr(h_q), _ptr(h_scale), _ptr(w_q), _ptr(w_scale), _ptr(labels), n, d, v,
+                              ignore_index, reduction, _ptr(loss_out), _ptr(lse_out), _stream(stream))
 
 
 def flce_fwd_shard(h, w_shard, labels, n, d, v_shard, v_first, dtype, ignore_index, lse_part_out, zy_part_out,
@@ -436,4 +445,28 @@ def linear_cross_entropy_vocab_split(h, w, labels, num_shards: int = 2, ignore_i
     if st != FLCE_OK:
         raise FlceError(st, "flce_sum_parts")
     return loss, lse, dh, dw
+
+
+def linear_cross_entropy_forward_fp8(h_q, h_scale, w_q, w_scale, labels, ignore_index: int = -100,
+                                     reduction: str = "mean"):
+    """Loss and LSE (flce_fwd_fp8) from e4m3 H [n, d] and W [v, d] (uint8 or float8_e4m3fn
+    device tensors) with fp32 per-row scales [n] and [v]."""
+    import torch
+    for t, name in ((h_q, "h_q"), (w_q, "w_q")):
+        if not t.is_cuda or t.dim() != 2 or t.element_size() != 1 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous 2-D one-byte device tensor")
+    for t, name in ((h_scale, "h_scale"), (w_scale, "w_scale")):
+        if not t.is_cuda or t.dtype != torch.float32 or t.dim() != 1 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous fp32 1-D device tensor")
+    n, d = h_q.shape
+    v = w_q.shape[0]
+    if w_q.shape[1] != d or h_scale.shape[0] != n or w_scale.shape[0] != v or labels.shape != (n,):
+        raise ValueError("shape mismatch")
+    loss = torch.empty(1, dtype=torch.float32, device=h_q.device)
+    lse = torch.empty(n, dtype=torch.float32, device=h_q.device)
+    st = flce_fwd_fp8(h_q, h_scale, w_q, w_scale, labels, n, d, v, ignore_index, _red_code(reduction), loss, lse,
+                      torch.cuda.current_stream(h_q.device))
+    if st != FLCE_OK:
+        raise FlceError(st, "flce_fwd_fp8")
+    return loss, lse
 

@@ -48,6 +48,8 @@ constexpr int kThreads = 256;
 constexpr int kStageElems = TM * TK;  // one operand, one stage: 32 KB
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef int v4i32 __attribute__((ext_vector_type(4)));
+typedef int v8i32 __attribute__((ext_vector_type(8)));
 #define FLCE_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 
 // Source of every out-of-range 16-byte load.
@@ -329,9 +331,19 @@ __device__ __forceinline__ void interleave_hint() {
 // So A is fetched two stages and B one stage ahead of its use.  Stages past
 // the end load zeros and are never consumed, so every iteration issues the
 // same loads and the waits are constants.
-template <bool A_KMAJ, bool B_KMAJ>
+//
+// FP8 (both operands k-major, e4m3 bytes viewed as 16-bit pairs, so that
+// loads, slots and offsets are those of bf16): a stage holds 128 fp8 values
+// of k and runs as two 64-deep k-steps of v_mfma_f32_32x32x64_f8f6f4.  A
+// lane's fp8 operand for k-step q is its bf16-layout fragments of k-steps 2q
+// and 2q+1 side by side; the k order inside an MFMA does not matter as long
+// as both operands share it, and each lane half still covers disjoint k.
+//   k-step 0: MFMAs of k-step 1 of stage j-1 | reads of 0, 1 | B_{j+1} loads
+//   k-step 1: MFMAs of k-step 0              | reads of 2, 3 | A_{j+2} loads
+template <bool A_KMAJ, bool B_KMAJ, bool FP8 = false>
 __device__ __forceinline__ void tile_loop(const Operand& A, const Operand& B, int64_t m0, int64_t n0, int64_t k_lo,
                                           int64_t k_hi, Acc& acc) {
+  static_assert(!FP8 || (A_KMAJ && B_KMAJ), "the fp8 loop takes k-major operands");
   bf16_t (*lds)[kStageElems] = ring();
   constexpr int kReads = (A_KMAJ ? 4 : 8) + (B_KMAJ ? 4 : 8);  // LDS reads per k-step
   const int wave = threadIdx.x >> 6;
@@ -366,6 +378,19 @@ __device__ __forceinline__ void tile_loop(const Operand& A, const Operand& B, in
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         acc.c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc.c[i][j], 0, 0, 0);
+  };
+  auto mma8 = [&](const Frags& lo, const Frags& hi) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const v4i32 al = __builtin_bit_cast(v4i32, lo.a[i]), ah = __builtin_bit_cast(v4i32, hi.a[i]);
+        const v4i32 bl = __builtin_bit_cast(v4i32, lo.b[j]), bh = __builtin_bit_cast(v4i32, hi.b[j]);
+        const v8i32 a8 = __builtin_shufflevector(al, ah, 0, 1, 2, 3, 4, 5, 6, 7);
+        const v8i32 b8 = __builtin_shufflevector(bl, bh, 0, 1, 2, 3, 4, 5, 6, 7);
+        // formats 0, 0: both operands e4m3; no block scales
+        acc.c[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, acc.c[i][j], 0, 0, 0, 0, 0, 0);
+      }
   };
   auto next = [](int s, int d) { return s + d >= kSlots ? s + d - kSlots : s + d; };
 
@@ -435,13 +460,57 @@ __device__ __forceinline__ void tile_loop(const Operand& A, const Operand& B, in
   };
   const int64_t ia = inside(A, m0), ib = inside(B, n0);
   const int64_t fast_end = ib - 1 < ia - 2 ? ib - 1 : ia - 2;
-  if (nk > 0) body(0, std::true_type{}, std::false_type{});
-  int64_t j = 1;
-  for (; j < fast_end; ++j) body(j, std::false_type{}, std::true_type{});
-  for (; j < nk; ++j) body(j, std::false_type{}, std::false_type{});
-  if (nk > 0) {  // k-step 3 of the last stage
-    wait_frags<A_KMAJ, B_KMAJ>(f1);
-    mma(f1);
+  if constexpr (!FP8) {
+    if (nk > 0) body(0, std::true_type{}, std::false_type{});
+    int64_t j = 1;
+    for (; j < fast_end; ++j) body(j, std::false_type{}, std::true_type{});
+    for (; j < nk; ++j) body(j, std::false_type{}, std::false_type{});
+    if (nk > 0) {  // k-step 3 of the last stage
+      wait_frags<A_KMAJ, B_KMAJ>(f1);
+      mma(f1);
+    }
+  } else {
+    Frags g0h, g1h;  // second halves of the two fp8 k-steps' operands (f0, f1 hold the first)
+    auto body8 = [&](int64_t j, auto first, auto fast) {
+      constexpr bool kFirst = decltype(first)::value;
+      constexpr bool kFast = decltype(fast)::value;
+      bf16_t* slot_b = lds[next(sb, 2)];
+      bf16_t* slot_a = lds[next(sa, 4)];
+      const int64_t kb = k_of(j + 1), ka = k_of(j + 2);
+      auto load_b = [&](auto i0) {
+        if constexpr (kFast)
+          load_stage_fast<decltype(i0)::value, 4, B_KMAJ>(B, n0, kb, slot_b, offb);
+        else
+          load_stage<decltype(i0)::value, 4, B_KMAJ>(B, n0, kb, slot_b, offb);
+      };
+      auto load_a = [&](auto i0) {
+        if constexpr (kFast)
+          load_stage_fast<decltype(i0)::value, 4, A_KMAJ>(A, m0, ka, slot_a, offa);
+        else
+          load_stage<decltype(i0)::value, 4, A_KMAJ>(A, m0, ka, slot_a, offa);
+      };
+      read(sa, sb, std::integral_constant<int, 0>{}, f0);
+      read(sa, sb, std::integral_constant<int, 1>{}, g0h);
+      if constexpr (!kFirst) mma8(f1, g1h);
+      load_b(std::integral_constant<int, 0>{});
+      load_b(std::integral_constant<int, 4>{});
+      interleave_hint<kFirst ? 0 : 16, 16>();
+      read(sa, sb, std::integral_constant<int, 2>{}, f1);
+      read(sa, sb, std::integral_constant<int, 3>{}, g1h);
+      mma8(f0, g0h);
+      load_a(std::integral_constant<int, 0>{});
+      load_a(std::integral_constant<int, 4>{});
+      interleave_hint<16, 16>();
+      wait_stages(1);
+      stage_barrier();
+      sa = next(sa, 2);
+      sb = next(sb, 2);
+    };
+    if (nk > 0) body8(0, std::true_type{}, std::false_type{});
+    int64_t j = 1;
+    for (; j < fast_end; ++j) body8(j, std::false_type{}, std::true_type{});
+    for (; j < nk; ++j) body8(j, std::false_type{}, std::false_type{});
+    if (nk > 0) mma8(f1, g1h);  // k-step 1 of the last stage
   }
   wait_stages(0);  // no direct load may still target this workgroup's LDS when it exits
 }
@@ -467,6 +536,9 @@ struct LogitsArgs {
   const int32_t* nvalid;
   int32_t reduction;
   int64_t ignore_index;
+  // fp8 operands: z = h_scale[token] * w_scale[vocabulary row] * (q_h . q_w)
+  const float* h_scale;
+  const float* w_scale;
 };
 
 // Recompute-mode epilogue of one wave's 128 vocabulary rows x 128 tokens:
@@ -530,21 +602,50 @@ __device__ __forceinline__ void logits_grad_epilogue(const LogitsArgs& a, Acc& a
   });
 }
 
-template <bool RECOMP>
+template <bool RECOMP, bool FP8 = false>
 __global__ __launch_bounds__(kThreads) void mfma_logits_kernel(LogitsArgs a) {
+  static_assert(!(RECOMP && FP8), "the fp8 logits serve the forward statistics only");
   const int64_t nb = a.tiles_m * a.tiles_n;
   const int64_t t = xcd_remap(blockIdx.x, nb);
   int64_t tm, tn;
   tile_coords(t, a.tiles_m, a.tiles_n, a.group_m, tm, tn);
   const int64_t m0 = tm * TM, n0 = tn * TN;
   Acc acc;
-  tile_loop<true, true>(a.w, a.h, m0, n0, 0, a.w.k_bound, acc);
+  tile_loop<true, true, FP8>(a.w, a.h, m0, n0, 0, a.w.k_bound, acc);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int half = lane >> 5;
   const int64_t vbase = m0 + wm * 128;  // this wave's 128-wide vocabulary group
   const int64_t g = vbase / 128;
+  if constexpr (FP8) {
+    // dequantise: row (I, 4Q + U) of the accumulators is vocabulary row
+    // vbase + 32 I + 8 Q + 4 half + U, column J is token n0 + 128 wn + 32 J + lane % 32
+    float sh[4];
+    static_for<4>([&](auto J) {
+      const int64_t tok = n0 + wn * 128 + J * 32 + (lane & 31);
+      sh[J] = tok < a.rows ? a.h_scale[tok] : 0.0f;
+    });
+    static_for<4>([&](auto I) {
+      static_for<4>([&](auto Q) {
+        const int64_t r0 = vbase + I * 32 + 8 * Q + 4 * half;
+        float sw[4];
+        if (r0 + 4 <= a.v) {
+          const float4 q4 = *reinterpret_cast<const float4*>(a.w_scale + r0);
+          sw[0] = q4.x;
+          sw[1] = q4.y;
+          sw[2] = q4.z;
+          sw[3] = q4.w;
+        } else {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) sw[u] = r0 + u < a.v ? a.w_scale[r0 + u] : 0.0f;
+        }
+        static_for<4>([&](auto J) {
+          static_for<4>([&](auto U) { acc.c[I][J][Q * 4 + U] *= sw[U] * sh[J]; });
+        });
+      });
+    });
+  }
   if constexpr (RECOMP) {
     if (vbase + 128 <= a.v)
       logits_grad_epilogue<true>(a, acc, n0, vbase, wn, wave, lane);
@@ -909,11 +1010,17 @@ hipError_t mfma_logits(const Plan& p, const Work& w, const ChunkArgs& c, int mod
   a.nvalid = w.nvalid;
   a.reduction = c.reduction;
   a.ignore_index = c.ignore_index;
+  a.h_scale = c.h_scale;
+  a.w_scale = c.w_scale;
   const dim3 grid(static_cast<unsigned>(a.tiles_m * a.tiles_n));
-  if (mode == LOGITS_GRAD_FROM_LSE)
+  if (c.fp8) {
+    if (mode != LOGITS_STATS) return hipErrorInvalidValue;
+    mfma_logits_kernel<false, true><<<grid, kThreads, 0, s>>>(a);
+  } else if (mode == LOGITS_GRAD_FROM_LSE) {
     mfma_logits_kernel<true><<<grid, kThreads, 0, s>>>(a);
-  else
+  } else {
     mfma_logits_kernel<false><<<grid, kThreads, 0, s>>>(a);
+  }
   return hipGetLastError();
 }
 

@@ -216,9 +216,12 @@ Work carve(const Plan& p, char* base) {
 // The kernel sequence of one call; workspace already allocated.
 // zy_out (optional): the per-row target logit (0 for ignored rows and for
 // labels outside [0, v)); loss_out may be null when zy_out is given.
+// h_scale / w_scale (optional, forward only): h and w hold e4m3 bytes, the
+// plan's d counting byte pairs, and each row carries its own scale.
 hipError_t run(const Plan& p, const Work& wk, const void* h, const void* w, const int64_t* labels,
                int64_t ignore_index, int32_t reduction, float* loss_out, float* lse_out, void* dh_out, void* dw_out,
-               hipStream_t s, float* zy_out = nullptr) {
+               hipStream_t s, float* zy_out = nullptr, const float* h_scale = nullptr,
+               const float* w_scale = nullptr) {
   const int64_t elem = p.dtype == FLCE_BF16 ? 2 : 4;
   hipError_t e = timed(K_LABEL_SCAN, s, [&] { return launch_label_scan(p, wk, labels, ignore_index, s); });
   if (e != hipSuccess) return e;
@@ -240,6 +243,9 @@ hipError_t run(const Plan& p, const Work& wk, const void* h, const void* w, cons
     a.grad_out = nullptr;
     a.zy_rows = zy_out != nullptr ? zy_out + a.row0 : nullptr;
     a.dh_f32 = 0;
+    a.fp8 = h_scale != nullptr ? 1 : 0;
+    a.h_scale = h_scale != nullptr ? h_scale + a.row0 : nullptr;
+    a.w_scale = w_scale;
 
     const int mode = p.with_bwd ? LOGITS_PROB : LOGITS_STATS;
     e = timed(K_LOGITS, s, [&] {
@@ -291,6 +297,9 @@ hipError_t run_bwd(const Plan& p, const Work& wk, const void* h, const void* w, 
     a.grad_out = grad_out;
     a.zy_rows = nullptr;
     a.dh_f32 = dh_f32;
+    a.fp8 = 0;
+    a.h_scale = nullptr;
+    a.w_scale = nullptr;
     e = timed(K_LOGITS, s, [&] {
       return p.engine == ENGINE_MFMA ? mfma_logits(p, wk, a, LOGITS_GRAD_FROM_LSE, s)
                                      : fma_logits(p, wk, a, LOGITS_GRAD_FROM_LSE, s);
@@ -414,6 +423,29 @@ int call_ce_logits(const void* logits, const int64_t* labels, int64_t n, int64_t
   hipError_t f = hipFreeAsync(base, stream);
   if (e != hipSuccess) return FLCE_ERR_HIP;
   return status_of(f);
+}
+
+// ---- fp8 forward -------------------------------------------------------------------
+
+int call_fwd_fp8(const void* h_q, const float* h_scale, const void* w_q, const float* w_scale, const int64_t* labels,
+                 int64_t n, int64_t d, int64_t v, int64_t ignore_index, flce_reduction reduction, float* loss_out,
+                 float* lse_out, hipStream_t stream) {
+  if (h_q == nullptr || w_q == nullptr || h_scale == nullptr || w_scale == nullptr || labels == nullptr ||
+      loss_out == nullptr)
+    return FLCE_ERR_INVALID_ARG;
+  if (n <= 0 || d <= 0 || v <= 0) return FLCE_ERR_INVALID_ARG;
+  if (reduction != FLCE_MEAN && reduction != FLCE_SUM) return FLCE_ERR_INVALID_ARG;
+  if (d % 16 != 0 || !aligned(h_q, 16) || !aligned(w_q, 16) || !aligned(w_scale, 16) || !aligned(h_scale, 4) ||
+      !aligned(labels, 8) || !aligned(loss_out, 4) || (lse_out != nullptr && !aligned(lse_out, 4)))
+    return FLCE_ERR_ALIGNMENT;
+  Plan p;
+  // the matrix engine sees each row of e4m3 bytes as d / 2 sixteen-bit units
+  int st = make_plan(n, d / 2, v, FLCE_BF16, 0, &p);
+  if (st != FLCE_OK) return st;
+  return with_workspace(p, stream, [&](const Work& wk) {
+    return run(p, wk, h_q, w_q, labels, ignore_index, reduction, loss_out, lse_out, nullptr, nullptr, stream, nullptr,
+               h_scale, w_scale);
+  });
 }
 
 // ---- vocabulary shards ---------------------------------------------------------
@@ -550,6 +582,13 @@ int flce_ce_logits(const void* logits, const int64_t* labels, int64_t n, int64_t
                    float* loss_out, float* lse_out, void* grad_out, hipStream_t stream) {
   return flce::call_ce_logits(logits, labels, n, v, dtype, ignore_index, reduction, lse_in, grad_scale, loss_out,
                               lse_out, grad_out, stream);
+}
+
+int flce_fwd_fp8(const void* h_q, const float* h_scale, const void* w_q, const float* w_scale, const int64_t* labels,
+                 int64_t n, int64_t d, int64_t v, int64_t ignore_index, flce_reduction reduction, float* loss_out,
+                 float* lse_out, hipStream_t stream) {
+  return flce::call_fwd_fp8(h_q, h_scale, w_q, w_scale, labels, n, d, v, ignore_index, reduction, loss_out, lse_out,
+                            stream);
 }
 
 int flce_fwd_shard(const void* h, const void* w_shard, const int64_t* labels, int64_t n, int64_t d, int64_t v_shard,

@@ -96,6 +96,9 @@ struct ChunkArgs {
   const float* grad_out;    // upstream gradient of the loss (device scalar) or nullptr for 1
   float* zy_rows;           // chunk's slice of a per-row target-logit output, or nullptr
   int32_t dh_f32;           // 1: dh is an fp32 array whatever the dtype (a shard's dH partial)
+  int32_t fp8;              // 1: h and w hold e4m3 bytes (d counts byte pairs), scaled per row
+  const float* h_scale;     // fp8: chunk's first token scale
+  const float* w_scale;     // fp8: vocabulary row scales
 };
 
 // --- launchers (each returns the launch status) ---------------------------------

@@ -2,8 +2,10 @@
 from .flce_oracle import (  # noqa: F401
     IGNORE_INDEX,
     ce_on_logits,
+    decode_e4m3,
     flce_backward_from_lse,
     flce_forward,
+    flce_forward_fp8,
     flce_forward_backward,
     flce_dw_rows,
     flce_rows,

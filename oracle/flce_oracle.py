@@ -38,6 +38,12 @@ written from the pages:
   Cross-Entropy with Online LogSumExp", step 3, taken over shards instead of
   tiles), and a shard's gradient is the softmax-minus-one-hot formula on its
   own columns with the merged LSE;
+* FP8 inputs, which the lecture page raises only as an open question (FP8
+  training on newer GPUs) without a method: the forward of e4m3-quantised H
+  and W with one scale per row is the forward of the dequantised matrices,
+  ``z_ij = s_h[i] s_w[j] sum_k q_h[i, k] q_w[j, k]``; e4m3 is the OCP 8-bit
+  float with 1 sign bit, 4 exponent bits (bias 7) and 3 mantissa bits,
+  subnormals at exponent 0 and no infinities (S.1111.111 is NaN);
 * ``reduction="mean"`` as in the loss module call on the lecture page
   ("GPU MODE lecture 028 - Liger Kernel", the LigerCrossEntropyLoss example);
   the mean is taken over the rows whose label is not ``ignore_index``, and a
@@ -339,4 +345,34 @@ def vocab_shard_backward(h, w_shard, labels, lse, v_first: int, grad_out: float 
     g[~valid] = 0.0
     g *= scale
     return g @ wd, g.T @ hd
+
+
+def decode_e4m3(codes) -> np.ndarray:
+    """float64 values of OCP e4m3 bytes (any shape), from the format definition.
+
+    Exponent field e, mantissa field m: e = 0 is subnormal, m/8 * 2^-6; else
+    (1 + m/8) * 2^(e - 7); the code with e = 15 and m = 7 is NaN.
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    out = sign * mag
+    out[(e == 15) & ((c & 0x7) == 7)] = np.nan
+    return out
+
+
+def flce_forward_fp8(h_q, h_scale, w_q, w_scale, labels, ignore_index: int = IGNORE_INDEX, reduction: str = "mean",
+                     block_rows: int = 1024, workers: int = 1):
+    """Loss and LSE[N] (float64) of the forward on e4m3 H and W with one fp32 scale per row."""
+    def codes(x):
+        if hasattr(x, "detach"):
+            import torch
+            x = x.detach().to("cpu").contiguous().view(torch.uint8).numpy()
+        return np.asarray(x, dtype=np.uint8)
+    h = decode_e4m3(codes(h_q)) * _as_f64(h_scale)[:, None]
+    w = decode_e4m3(codes(w_q)) * _as_f64(w_scale)[:, None]
+    return flce_forward(h, w, labels, ignore_index=ignore_index, reduction=reduction, block_rows=block_rows,
+                        workers=workers)
 

@@ -210,6 +210,27 @@ def test_shard_argument_errors_before_any_device_work():
     assert flce.flce_sum_parts(A, 2, 10, flce.FLCE_F32, A + 2, None) == flce.FLCE_ERR_ALIGNMENT
 
 
+def test_fp8_argument_errors_before_any_device_work():
+    A = 1 << 20
+    ok = dict(h_q=A, h_scale=A, w_q=A, w_scale=A, labels=A, n=4, d=64, v=300, ignore_index=-100,
+              reduction=flce.FLCE_MEAN, loss_out=A, lse_out=None, stream=None)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return flce.flce_fwd_fp8(**a)
+
+    for k in ("h_q", "h_scale", "w_q", "w_scale", "labels", "loss_out"):
+        assert call(**{k: None}) == flce.FLCE_ERR_INVALID_ARG, k
+    assert call(n=0) == flce.FLCE_ERR_INVALID_ARG
+    assert call(reduction=9) == flce.FLCE_ERR_INVALID_ARG
+    assert call(d=72) == flce.FLCE_ERR_ALIGNMENT            # rows must be whole 16-byte vectors
+    assert call(h_q=A + 8) == flce.FLCE_ERR_ALIGNMENT
+    assert call(w_scale=A + 4) == flce.FLCE_ERR_ALIGNMENT
+    assert call(h_scale=A + 2) == flce.FLCE_ERR_ALIGNMENT
+    assert call(d=(1 << 25) + 32) == flce.FLCE_ERR_INVALID_ARG   # beyond the engine's row length
+
+
 def test_vocab_shard_bounds():
     assert flce.vocab_shard_bounds(128256, 8)[0] == (0, 15872)
     for v, q in [(128256, 8), (1000, 3), (5, 5), (1 << 20, 7), (300, 2)]:

@@ -17,8 +17,9 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import (ce_on_logits, flce_backward_from_lse, flce_dw_rows, flce_forward, flce_forward_backward, flce_rows,
-                    log_sum_exp, merge_vocab_shards, vocab_shard_backward, vocab_shard_partials)
+from oracle import (ce_on_logits, decode_e4m3, flce_backward_from_lse, flce_dw_rows, flce_forward, flce_forward_backward,
+                    flce_forward_fp8, flce_rows, log_sum_exp, merge_vocab_shards, vocab_shard_backward,
+                    vocab_shard_partials)
 
 RTOL = 1e-12
 
@@ -510,4 +511,49 @@ def test_vocab_shards_label_free_shard_and_ignored_rows():
     y_ign = np.full(n, -100)
     dh0, dw0 = vocab_shard_backward(h, w[6:], y_ign, lse_full, 6)
     assert np.all(dh0 == 0.0) and np.all(dw0 == 0.0)
+
+
+# --- FP8 inputs -------------------------------------------------------------------
+
+def test_e4m3_decoder_against_torch_and_format_values():
+    """Library routine: torch's float8_e4m3fn for all 256 codes; and values fixed by the
+    format: 0x38 = 1, 0x7e = 448 (largest), 0x08 = 2^-6 (smallest normal), 0x01 = 2^-9
+    (smallest subnormal), 0x80 = -0, 0x7f and 0xff NaN."""
+    c = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(c).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    d = decode_e4m3(c)
+    assert np.array_equal(np.isnan(d), np.isnan(ref)) and np.isnan(d[[0x7f, 0xff]]).all()
+    ok = ~np.isnan(ref)
+    assert np.array_equal(d[ok], ref[ok])
+    assert list(decode_e4m3([0x38, 0x7e, 0x08, 0x01, 0xb8])) == [1.0, 448.0, 2.0 ** -6, 2.0 ** -9, -1.0]
+    assert decode_e4m3([0x80])[0] == 0.0 and math.copysign(1.0, decode_e4m3([0x80])[0]) == -1.0
+
+
+def test_fp8_forward_torch_cross_entropy():
+    """Library routine: torch float64 cross-entropy on the logits of the dequantised
+    matrices (torch's own e4m3 decoding), per-row scales of both operands."""
+    g = np.random.default_rng(60)
+    n, d, v = 23, 32, 50
+    hq = torch.from_numpy(g.standard_normal((n, d)).astype(np.float32) * 40).to(torch.float8_e4m3fn)
+    wq = torch.from_numpy(g.standard_normal((v, d)).astype(np.float32) * 40).to(torch.float8_e4m3fn)
+    hs = torch.from_numpy(g.uniform(0.001, 0.01, n).astype(np.float32))
+    ws = torch.from_numpy(g.uniform(0.001, 0.01, v).astype(np.float32))
+    y = g.integers(0, v, n).astype(np.int64)
+    y[4] = -100
+    loss, lse = flce_forward_fp8(hq.view(torch.uint8), hs, wq.view(torch.uint8), ws, y)
+    h64 = hq.to(torch.float64) * hs.double()[:, None]
+    w64 = wq.to(torch.float64) * ws.double()[:, None]
+    z = h64 @ w64.T
+    ref = torch.nn.functional.cross_entropy(z, torch.from_numpy(y), ignore_index=-100)
+    assert loss == pytest.approx(ref.item(), rel=1e-12)
+    _close(lse, torch.logsumexp(z, dim=1).numpy())
+
+
+def test_fp8_forward_zero_weight_codes():
+    """Closed form: W codes all zero give lse = ln V and loss ln V whatever H and scales."""
+    n, d, v = 5, 16, 24
+    hq = np.random.default_rng(61).integers(0, 0x7e, (n, d)).astype(np.uint8)
+    loss, lse = flce_forward_fp8(hq, np.full(n, 3.0), np.zeros((v, d), np.uint8), np.full(v, 2.0), np.arange(n))
+    assert loss == pytest.approx(math.log(v), rel=1e-14)
+    _close(lse, np.full(n, math.log(v)))
 

@@ -149,6 +149,29 @@ def make_logits(wl: Workload, sigma: Optional[float] = None, threads: Optional[i
     return zt.contiguous(), torch.from_numpy(make_labels(wl))
 
 
+def quantize_rows_e4m3(x: torch.Tensor):
+    """(codes uint8 [rows, cols], scales fp32 [rows]) of a float tensor: each row
+    divided by max|row| / 448 (the largest e4m3 value; 1 for an all-zero row) and
+    rounded to e4m3 by torch's round-to-nearest-even conversion."""
+    x = x.float()
+    amax = x.abs().amax(dim=1)
+    scale = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+    q = (x / scale[:, None]).to(torch.float8_e4m3fn)
+    return q.view(torch.uint8).contiguous(), scale.contiguous()
+
+
+def make_inputs_fp8(wl: Workload, threads: Optional[int] = None):
+    """(H codes, H scales, W codes, W scales, labels): the workload's H and W
+    (float32 draws, seeds as make_inputs) quantised row by row to e4m3."""
+    h = torch.from_numpy(_normal_rows(1000 + wl.seed, wl.n, wl.d, 1.0, threads))
+    hq, hs = quantize_rows_e4m3(h)
+    del h
+    w = torch.from_numpy(_normal_rows(2000 + wl.seed, wl.v, wl.d, wl.sigma_w, threads))
+    wq, ws = quantize_rows_e4m3(w)
+    del w
+    return hq, hs, wq, ws, torch.from_numpy(make_labels(wl))
+
+
 def logits_bytes_avoided(n: int, v: int, elem_bytes: int = 4) -> int:
     """Size of the full [n, v] logits tensor that the fused path never allocates.
 
