@@ -556,14 +556,30 @@ __device__ __forceinline__ void logits_grad_epilogue(const LogitsArgs& a, Acc& a
   const int32_t nv = *a.nvalid;
   const float red = a.reduction == FLCE_SUM ? 1.0f : (nv > 0 ? 1.0f / static_cast<float>(nv) : 0.0f);
   auto in_vocab = [&](int r_row) { return FULL || vbase + r_row < a.v; };
+  // The four token columns' labels and LSEs are read before any store: a load
+  // issued after a column's stores would wait for them (vmcnt is in order).
+  // The loads are unconditional (a row past the end reads the last row and is
+  // masked): behind a per-lane branch each would be waited for at its join.
+  int64_t labs[4];
+  float lses[4];
+  static_for<4>([&](auto J) {
+    const int64_t tok = n0 + wn * 128 + J * 32 + (lane & 31);
+    const int64_t tc = tok < a.rows ? tok : a.rows - 1;
+    labs[J] = a.labels[tc];
+    lses[J] = a.lse_in[tc];
+  });
+  static_for<4>([&](auto J) {
+    const int64_t tok = n0 + wn * 128 + J * 32 + (lane & 31);
+    if (tok >= a.rows) labs[J] = a.ignore_index;
+  });
   static_for<4>([&](auto J) {
     const int64_t tok = n0 + wn * 128 + J * 32 + (lane & 31);
     const bool live = tok < a.rows;
     char* stage = reinterpret_cast<char*>(ring()[J]) + kWaveScratchBytes * wave;
-    const int64_t lab = live ? a.labels[tok] : a.ignore_index;
+    const int64_t lab = labs[J];
     const bool valid = live && lab != a.ignore_index;
     const float sc = valid ? go * red : 0.0f;
-    const float l2 = live ? a.lse_in[tok] * kLog2e : 0.0f;
+    const float l2 = live ? lses[J] * kLog2e : 0.0f;
     const int t = lane & 31;
     static_for<4>([&](auto I) {
       static_for<4>([&](auto Q) {
@@ -621,25 +637,36 @@ __global__ __launch_bounds__(kThreads) void mfma_logits_kernel(LogitsArgs a) {
   if constexpr (FP8) {
     // dequantise: row (I, 4Q + U) of the accumulators is vocabulary row
     // vbase + 32 I + 8 Q + 4 half + U, column J is token n0 + 128 wn + 32 J + lane % 32
+    // The group's 128 row scales go through this wave's 8 KB of ring slot 4
+    // (the statistics staging below uses slots 0-3): one load per lane, all
+    // issued together with the token scales, so nothing waits on them one by
+    // one, and the scaling reads them back from LDS without holding registers.
     float sh[4];
     static_for<4>([&](auto J) {
       const int64_t tok = n0 + wn * 128 + J * 32 + (lane & 31);
-      sh[J] = tok < a.rows ? a.h_scale[tok] : 0.0f;
+      sh[J] = a.h_scale[tok < a.rows ? tok : a.rows - 1];
     });
+    float* sws = reinterpret_cast<float*>(reinterpret_cast<char*>(ring()[4]) + kWaveScratchBytes * wave);
+    {
+      const int64_t r = vbase + 2 * lane;  // rows r, r + 1 of the group
+      float2 v2;
+      if (r + 2 <= a.v) {
+        v2 = *reinterpret_cast<const float2*>(a.w_scale + r);
+      } else {
+        v2.x = r < a.v ? a.w_scale[r < a.v ? r : a.v - 1] : 0.0f;
+        v2.y = r + 1 < a.v ? a.w_scale[r + 1 < a.v ? r + 1 : a.v - 1] : 0.0f;
+      }
+      *reinterpret_cast<float2*>(sws + 2 * lane) = v2;
+    }
+    static_for<4>([&](auto J) {
+      const int64_t tok = n0 + wn * 128 + J * 32 + (lane & 31);
+      if (tok >= a.rows) sh[J] = 0.0f;
+    });
+    __builtin_amdgcn_wave_barrier();
     static_for<4>([&](auto I) {
       static_for<4>([&](auto Q) {
-        const int64_t r0 = vbase + I * 32 + 8 * Q + 4 * half;
-        float sw[4];
-        if (r0 + 4 <= a.v) {
-          const float4 q4 = *reinterpret_cast<const float4*>(a.w_scale + r0);
-          sw[0] = q4.x;
-          sw[1] = q4.y;
-          sw[2] = q4.z;
-          sw[3] = q4.w;
-        } else {
-#pragma unroll
-          for (int u = 0; u < 4; ++u) sw[u] = r0 + u < a.v ? a.w_scale[r0 + u] : 0.0f;
-        }
+        const float4 q4 = *reinterpret_cast<const float4*>(sws + I * 32 + 8 * Q + 4 * half);
+        const float sw[4] = {q4.x, q4.y, q4.z, q4.w};
         static_for<4>([&](auto J) {
           static_for<4>([&](auto U) { acc.c[I][J][Q * 4 + U] *= sw[U] * sh[J]; });
         });
@@ -656,6 +683,14 @@ __global__ __launch_bounds__(kThreads) void mfma_logits_kernel(LogitsArgs a) {
   // FULL: every vocabulary row of the group exists (no per-element masks).
   auto epilogue = [&](auto FULL) {
     auto in_vocab = [&](int r_row) { return FULL || vbase + r_row < a.v; };
+    // The four token columns' labels are read before any store: a load issued
+    // after a column's P stores would wait for them (vmcnt is in order).
+    // (unconditional, from a clamped row, so that no branch makes them wait one by one)
+    int64_t labs[4];
+    static_for<4>([&](auto J) {
+      const int64_t tok = n0 + wn * 128 + J * 32 + (lane & 31);
+      labs[J] = a.labels[tok < a.rows ? tok : a.rows - 1];
+    });
     static_for<4>([&](auto J) {
       const int64_t tok = n0 + wn * 128 + J * 32 + (lane & 31);
       const bool live = tok < a.rows;
@@ -705,7 +740,7 @@ __global__ __launch_bounds__(kThreads) void mfma_logits_kernel(LogitsArgs a) {
           a.pm[g * a.C + tok] = mx;
           a.ps[g * a.C + tok] = s;
         }
-        const int64_t q = a.labels[tok] - vbase;
+        const int64_t q = labs[J] - vbase;
         const int o = static_cast<int>(q & 31);
         if (q >= 0 && q < 128 && ((o >> 2) & 1) == half) {
           const int it = static_cast<int>(q >> 5);
