@@ -72,6 +72,43 @@ def cpu_baseline(wl, h, w, y, rows: int):
                       f"{dt:.1f} s incl. fp64 conversion"}
 
 
+def all_configs_measure(flce, torch, args, stream):
+    """flce_fwd_bwd on every workload: median step time, tokens/s, MFMA % (6 N D V against
+    the workload dtype's matrix peak) and the extra device memory against the N V 4 bytes
+    of logits it avoids."""
+    from workloads import CONFIGS, logits_bytes_avoided, make_inputs
+    out = {}
+    for name, wl in CONFIGS.items():
+        h, w, y = make_inputs(wl)
+        dev = torch.device("cuda:0")
+        hd, wd, yd = h.to(dev), w.to(dev), y.to(dev)
+        del h, w
+        o = (torch.empty(1, dtype=torch.float32, device=dev), torch.empty(wl.n, dtype=torch.float32, device=dev),
+             torch.empty_like(hd), torch.empty_like(wd))
+        for _ in range(max(1, args.warmup)):
+            flce.linear_cross_entropy(hd, wd, yd, reduction=wl.reduction, out=o)
+        torch.cuda.synchronize()
+        flce.flce_memory_high_water(reset=True)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        ev[0].record(stream)
+        for i in range(args.steps):
+            flce.linear_cross_entropy(hd, wd, yd, reduction=wl.reduction, out=o)
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        extra = flce.flce_memory_high_water()
+        t = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
+        med = t[len(t) // 2] if len(t) % 2 else 0.5 * (t[len(t) // 2 - 1] + t[len(t) // 2])
+        flop = 6.0 * wl.n * wl.d * wl.v
+        out[name] = {"n": wl.n, "d": wl.d, "v": wl.v, "dtype": wl.dtype, "ms_median": med, "ms_min": t[0],
+                     "tokens_per_s": wl.n / (med * 1e-3),
+                     "mfma_pct": 100.0 * flop / (med * 1e-3) / (PEAK_TFLOPS[wl.dtype] * 1e12),
+                     "extra_device_bytes": extra, "logits_bytes_avoided": logits_bytes_avoided(wl.n, wl.v)}
+        log(f"[bench] {name}: {med:.3f} ms median, {out[name]['mfma_pct']:.1f}% of the {wl.dtype} peak")
+        del hd, wd, yd, o
+        torch.cuda.empty_cache()
+    return out
+
+
 def fp8_forward_measure(flce, torch, wl, args, stream):
     """flce_fwd_fp8 on this workload's H and W quantised row by row to e4m3:
     2 N D V flop against the fp8 matrix peak."""
@@ -179,6 +216,8 @@ def main() -> int:
     ap.add_argument("--config", default="llama3_8b_head")
     ap.add_argument("--cpu-rows", type=int, default=3072, help="tokens in the oracle's CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--all-configs", action="store_true",
+                    help="also time flce_fwd_bwd on every workload (inputs drawn per workload) and report each")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run a 1 GiB device copy (counter calibration), one step and one cross-entropy on "
                          "the workload's logits, print nothing else; meant to run under rocprofv3 --pmc "
@@ -384,6 +423,8 @@ def main() -> int:
     }
     result["forward_fp8"] = fp8_forward_measure(flce, torch, wl, args, stream)
     result["ce_logits"] = ce_logits_measure(flce, torch, hd, wd, yd, wl, args, stream)
+    if args.all_configs:
+        result["per_config"] = all_configs_measure(flce, torch, args, stream)
     if not args.no_cpu_baseline:
         log(f"[bench] CPU baseline: oracle on {args.cpu_rows} rows")
         result["cpu_baseline"] = cpu_baseline(wl, h, w, y, args.cpu_rows)

@@ -162,12 +162,19 @@ __global__ __launch_bounds__(256) void fma_logits_kernel(const T* __restrict__ H
 
 // dH[t, :] (or a split partial) = G[t, :] . W
 template <typename T>
+// blockIdx.z = vocabulary split: columns [z k_split, (z+1) k_split) of G and
+// rows of W; with several splits `out` is split z's fp32 partial (part_stride apart).
 __global__ __launch_bounds__(256) void fma_dh_kernel(const float* __restrict__ G, int64_t vp, const T* __restrict__ W,
-                                                     int64_t rows, int64_t d, int64_t v, T* __restrict__ out) {
+                                                     int64_t rows, int64_t d, int64_t v, int64_t k_split,
+                                                     int64_t part_stride, T* __restrict__ out) {
   const int64_t m0 = static_cast<int64_t>(blockIdx.x) * BM;
   const int64_t n0 = static_cast<int64_t>(blockIdx.y) * BN;
+  const int64_t k_lo = static_cast<int64_t>(blockIdx.z) * k_split;
+  const int64_t k_hi = k_lo + k_split < v ? k_lo + k_split : v;
+  out += static_cast<int64_t>(blockIdx.z) * part_stride;
   float acc[4][4];
-  TileLoop<float, T, true, false>::run(G, vp, W, d, rows, d, v, m0, n0, acc);
+  TileLoop<float, T, true, false>::run(G + k_lo, vp, W + k_lo * d, d, rows, d, k_hi > k_lo ? k_hi - k_lo : 0, m0, n0,
+                                       acc);
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -225,9 +232,12 @@ hipError_t fma_logits(const Plan& p, const Work& w, const ChunkArgs& a, int mode
 
 hipError_t fma_dh(const Plan& p, const Work& w, const ChunkArgs& a, hipStream_t s) {
   if (p.dtype != FLCE_F32) return hipErrorInvalidValue;
-  fma_dh_kernel<float><<<grid2(a.rows, p.d), 256, 0, s>>>(static_cast<const float*>(w.prob), p.vp,
-                                                         static_cast<const float*>(a.w), a.rows, p.d, p.v,
-                                                         static_cast<float*>(a.dh));
+  dim3 grid = grid2(a.rows, p.d);
+  grid.z = static_cast<unsigned>(p.dh_splits);
+  const int64_t k_split = (p.v + p.dh_splits - 1) / p.dh_splits;
+  float* out = p.dh_splits > 1 ? w.dhpart : static_cast<float*>(a.dh);
+  fma_dh_kernel<float><<<grid, 256, 0, s>>>(static_cast<const float*>(w.prob), p.vp, static_cast<const float*>(a.w),
+                                            a.rows, p.d, p.v, k_split, p.chunk * p.d, out);
   return hipGetLastError();
 }
 

@@ -38,6 +38,22 @@ bool mul_ok(int64_t a, int64_t b) { return a > 0 && b > 0 && a <= (int64_t(1) <<
 
 }  // namespace
 
+// The split count s in [1, smax] of a reduction over `tiles` output tiles that
+// minimises ceil(tiles * s / slots) / s, the waves of `slots` concurrent
+// workgroups per unit of reduction length; the smallest such s.
+static int64_t best_splits(int64_t tiles, int64_t slots, int64_t smax) {
+  int64_t best = 1;
+  int64_t best_waves = (tiles + slots - 1) / slots;  // compare waves_s / s as waves_s * best <  best_waves * s
+  for (int64_t s = 2; s <= smax; ++s) {
+    const int64_t waves = (tiles * s + slots - 1) / slots;
+    if (waves * best < best_waves * s) {
+      best = s;
+      best_waves = waves;
+    }
+  }
+  return best;
+}
+
 // Chunk rows C: as many rows as the probability-buffer budget allows (a
 // multiple of 256 rows once that many fit), never more than half of the rows
 // (rounded up to 16) so that the buffer stays well below the [n, v] logits it
@@ -73,18 +89,20 @@ int make_plan(int64_t n, int64_t d, int64_t v, int32_t dtype, int32_t with_bwd, 
   if (c > n) c = n;
   q.chunk = c;
   q.nchunks = (n + c - 1) / c;
-  // dH = G.W has only ceil(C/256) x ceil(d/256) output tiles; split its
-  // vocabulary reduction until there is about one workgroup per CU (256 on
-  // MI355X; each needs a whole CU's LDS), keeping at least 4096 vocabulary
-  // columns per split.  Unsplit is best once the tiles alone fill the chip:
-  // splits add fp32 partials and a reduction pass.
+  // dH = G.W has few output tiles (ceil(C/256) x ceil(d/256) on the matrix
+  // engine, 64 x 64 tiles on the FMA engine); its vocabulary reduction is split
+  // in s parts, s chosen by best_splits: the fewest waves of one workgroup per
+  // CU (256 on MI355X) per unit of work.  Each split keeps at least 4096
+  // (matrix engine) or 256 (FMA engine) vocabulary columns; splits cost fp32
+  // partials and a reduction pass, so unsplit wins once the tiles fill the chip.
   q.dh_splits = 1;
-  if (q.engine == ENGINE_MFMA && with_bwd) {
-    const int64_t tiles = ((q.chunk + 255) / 256) * ((d + 255) / 256);
-    int64_t s = (kCus + tiles - 1) / tiles;
-    const int64_t smax = q.vp / 4096;
-    if (s > smax) s = smax;
-    if (s > 8) s = 8;
+  if (with_bwd) {
+    const bool mfma = q.engine == ENGINE_MFMA;
+    const int64_t tm = mfma ? 256 : 64;
+    const int64_t tiles = ((q.chunk + tm - 1) / tm) * ((d + tm - 1) / tm);
+    int64_t smax = q.vp / (mfma ? 4096 : 256);
+    if (smax > (mfma ? 8 : 16)) smax = mfma ? 8 : 16;
+    int64_t s = best_splits(tiles, kCus, smax);
     s = env_i64("FLCE_DH_SPLITS", s);
     if (s > q.vp / 64) s = q.vp / 64;  // every split keeps at least one 64-column stage
     q.dh_splits = s < 1 ? 1 : s;
