@@ -183,7 +183,8 @@ int flce_ce_logits(const void* logits, const int64_t* labels, int64_t n, int64_t
  *   h_q      device, [n, d] e4m3 bytes, 16-byte aligned;  h_scale  device, fp32 [n].
  *   w_q      device, [v, d] e4m3 bytes, 16-byte aligned;  w_scale  device, fp32 [v], 16-byte aligned.
  *   d        a multiple of 16 (FLCE_ERR_ALIGNMENT otherwise).
- * labels, ignore_index, reduction, loss_out, lse_out, stream and errors as for flce_fwd.
+ * labels, ignore_index, reduction, loss_out, lse_out, stream and errors as for flce_fwd;
+ * the workspace is flce_workspace_bytes(n, d / 2, v, FLCE_BF16, 0).
  */
 int flce_fwd_fp8(const void* h_q, const float* h_scale, const void* w_q, const float* w_scale, const int64_t* labels,
                  int64_t n, int64_t d, int64_t v, int64_t ignore_index, flce_reduction reduction, float* loss_out,
@@ -204,7 +205,9 @@ int flce_fwd_fp8(const void* h_q, const float* h_scale, const void* w_q, const f
  * flce_sum_parts over the dH partials.
  *
  * Labels are the full-vocabulary ids (ignore_index or [0, V)); a shard sees
- * the labels outside it as "no target in this shard".
+ * the labels outside it as "no target in this shard".  A shard call's
+ * workspace is flce_workspace_bytes(n, d, v_shard, dtype, with_bwd) plus
+ * 8 n bytes (the shard's shifted labels).
  */
 
 /*

@@ -161,3 +161,16 @@ def _loss_all_rows(z, y, nvalid):
         l, _, _ = ce_on_logits(z[lo:lo + 512], y[lo:lo + 512], reduction="sum")
         total += l
     return total / nvalid
+
+
+def test_ce_more_rows_than_one_grid():
+    # 65537 rows: the row kernels' grid stops at 65536 workgroups and loops for the rest.
+    wl, z, y = _case(65537, 64, "bf16", seed=13)
+    say("[ce] 65537 rows")
+    ref = ce_on_logits(z, y)
+    loss, lse, g = flce.cross_entropy(z.to(DEV), y.to(DEV), grad="separate")
+    torch.cuda.synchronize()
+    _check(float(loss.item()), to_f64(lse), to_f64(g), ref, wl.torch_dtype, "ce 65537 rows")
+    loss_f, lse_f, _ = flce.cross_entropy(z.to(DEV), y.to(DEV), grad=None)
+    torch.cuda.synchronize()
+    _check(float(loss_f.item()), to_f64(lse_f), None, ref, wl.torch_dtype, "ce 65537 rows, forward")

@@ -177,3 +177,22 @@ def test_mfma_tails_bf16(shape):
     n, d, v = shape
     wl, inp = _case(n, d, v, "bf16", sigma_w=0.1, seed=24)
     _parity(wl, inp, f"tails {shape}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_vocabulary_of_one(dtype):
+    """Degenerate vocabulary V = 1: the softmax is identically 1, so every valid
+    row's loss is 0, its LSE is its single logit, and both gradients vanish, up
+    to the fp32 rounding of exp(z - max) (the matrix engine forms the exponent as
+    z log2(e) minus its rounded max, a residual of order 1e-8)."""
+    n, d, v = 5, 16, 1
+    wl = Workload("v1", n, d, v, dtype, 0.3, "uniform", 0.0, "mean", seed=25)
+    h, w, y = make_inputs(wl, threads=1)
+    y[3] = -100
+    say(f"[parity] vocabulary of one {dtype}")
+    loss, lse, dh, dw = run_lib(h, w, y)
+    z = to_f64(h) @ to_f64(w).T
+    assert abs(loss) <= 1e-6
+    assert np.max(np.abs(lse - z[:, 0])) <= TOL[wl.torch_dtype]["loss"] * max(1.0, float(np.max(np.abs(z))))
+    assert np.max(np.abs(dh)) <= 1e-6 * max(1.0, float(np.max(np.abs(to_f64(w)))))
+    assert np.max(np.abs(dw)) <= 1e-6 * max(1.0, float(np.max(np.abs(to_f64(h)))))
