@@ -97,7 +97,7 @@ __global__ __launch_bounds__(kCeThreads) void ce_rows_kernel(
     int32_t reduction, const int32_t* __restrict__ nvalid, const float* __restrict__ lse_in,
     const float* __restrict__ grad_scale, float* __restrict__ lse_out, float* __restrict__ loss_rows, T* grad) {
   constexpr int kN = Vec<T>::kN;
-  constexpr int kUnroll = 4;
+  constexpr int kUnroll = 8;
   constexpr int64_t kStep = static_cast<int64_t>(kCeThreads) * kN;  // columns between a thread's vectors
   constexpr int64_t kSweep = kStep * kUnroll;
   __shared__ MaxSum red[kCeThreads / 64];

@@ -45,7 +45,7 @@ __device__ __forceinline__ float row_scale(int32_t nvalid, int32_t reduction) {
 // row's NLL lse - z_y.  With the gradient, each partial max is replaced by
 // the factor scale_i * exp(m_g - lse) that turns the stored exp(z - m_g) into
 // the scaled softmax, and the value the target column takes is precomputed.
-constexpr int kMergeRows = 16;
+constexpr int kMergeRows = 64;
 constexpr int kMergeSlices = 16;
 
 __global__ __launch_bounds__(kMergeRows* kMergeSlices) void lse_merge_kernel(
