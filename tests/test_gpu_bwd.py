@@ -108,3 +108,35 @@ def test_bwd_single_row_and_tiny_vocab():
     dh, dw = flce.linear_cross_entropy_backward(h.to(DEV), w.to(DEV), y.to(DEV), lse32.to(DEV))
     torch.cuda.synchronize()
     _check_grads(to_f64(dh), to_f64(dw), rdh, rdw, torch.bfloat16, "bwd 1x16x5")
+
+
+@pytest.mark.slow
+def test_bwd_llama3_8b_head_full_size():
+    """flce_bwd at the Llama-3 head's size from the oracle's full-forward LSE (fp64,
+    rounded to fp32), upstream gradient 0.5: dH on sampled token rows and dW on
+    sampled vocabulary rows against the oracle, which uses the same LSE."""
+    import os
+    from oracle import flce_dw_rows, flce_rows
+    from workloads import CONFIGS
+    wl = CONFIGS["llama3_8b_head"]
+    say(f"[bwd] llama3 8b head full size n={wl.n} d={wl.d} v={wl.v}")
+    h, w, y = make_inputs(wl)
+    w64 = to_f64(w)
+    workers = min(16, len(os.sched_getaffinity(0)))
+    _, lse64 = flce_forward(h, w64, y, reduction=wl.reduction, workers=workers)
+    lse32 = lse64.astype(np.float32)
+    g_up = 0.5
+    go = torch.tensor([g_up], dtype=torch.float32, device=DEV)
+    dh, dw = flce.linear_cross_entropy_backward(h.to(DEV), w.to(DEV), y.to(DEV), torch.from_numpy(lse32).to(DEV), go,
+                                                reduction=wl.reduction)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(91)
+    rows = sorted({0, 4095, 4096, wl.n - 1, *(int(r) for r in rng.choice(wl.n, 12, replace=False))})
+    _, rdh = flce_rows(h, w64, y, rows, reduction=wl.reduction)
+    cols = sorted({0, wl.v - 1, *(int(c) for c in rng.choice(wl.v, 10, replace=False))})
+    rdw = flce_dw_rows(h, w64, y, lse32.astype(np.float64), cols, reduction=wl.reduction)
+    e_dh = rel_max(to_f64(dh[torch.tensor(rows, device=DEV)]), g_up * rdh)
+    e_dw = rel_max(to_f64(dw[torch.tensor(cols, device=DEV)]), g_up * rdw)
+    say(f"  sampled dH rel {e_dh:.2e}, dW rel {e_dw:.2e}")
+    tol = TOL[torch.bfloat16]["grad"]
+    assert e_dh <= tol and e_dw <= tol
