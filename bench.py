@@ -136,7 +136,7 @@ def fp8_forward_measure(flce, torch, wl, args, stream):
     lg_avg = lg_ms / max(launches, 1)
     flop_launch = flop / max(launches // args.steps, 1)
     log(f"[bench] fp8 forward: {ms:.3f} ms/call, logits launch {lg_avg:.3f} ms")
-    return {
+    out = {
         "ms_per_call": ms,
         "tflops_2ndv": flop / (ms * 1e-3) / 1e12,
         "peak_tflops": PEAK_TFLOPS["fp8"],
@@ -145,6 +145,38 @@ def fp8_forward_measure(flce, torch, wl, args, stream):
         "logits_frac": flop_launch / (lg_avg * 1e-3) / (PEAK_TFLOPS["fp8"] * 1e12),
         "inputs": "H and W quantised per row to e4m3 (scale max|row|/448)",
     }
+    out["backward"] = fp8_backward_measure(flce, torch, wl, args, stream, (hq, hs, wq, ws, y))
+    return out
+
+
+def fp8_backward_measure(flce, torch, wl, args, stream, inputs):
+    """flce_bwd_fp8 from the forward's LSE: the fp8 logits recompute (2 N D V flop at the
+    fp8 peak) plus dH and dW on the dequantised bf16 copies (4 N D V at the bf16 peak).
+    `ideal_ms` is the time of that work at the two peaks; `frac` = ideal / measured."""
+    hq, hs, wq, ws, y = inputs
+    _, lse = flce.linear_cross_entropy_forward_fp8(hq, hs, wq, ws, y, reduction=wl.reduction)
+    go = torch.ones(1, dtype=torch.float32, device=hq.device)
+    for _ in range(max(1, args.warmup)):
+        flce.linear_cross_entropy_backward_fp8(hq, hs, wq, ws, y, lse, go, reduction=wl.reduction)
+    torch.cuda.synchronize()
+    flce.flce_profile_read()
+    flce.flce_profile_enable(True)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        flce.linear_cross_entropy_backward_fp8(hq, hs, wq, ws, y, lse, go, reduction=wl.reduction)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    flce.flce_profile_enable(False)
+    kern = flce.flce_profile_read()
+    ms = e0.elapsed_time(e1) / args.steps
+    ndv = float(wl.n) * wl.d * wl.v
+    ideal = (2.0 * ndv / (PEAK_TFLOPS["fp8"] * 1e12) + 4.0 * ndv / (PEAK_TFLOPS["bf16"] * 1e12)) * 1e3
+    per_call = {k: ms_k / args.steps for k, (cnt, ms_k) in kern.items() if cnt}
+    log(f"[bench] fp8 backward: {ms:.3f} ms/call ({100.0 * ideal / ms:.1f}% of the mixed peak), kernels {per_call}")
+    return {"ms_per_call": ms, "ideal_ms": ideal, "frac": ideal / ms, "kernel_ms_per_call": per_call,
+            "flop": "2NDV fp8 (logits recompute) + 4NDV bf16 (dH, dW)"}
 
 
 def ce_logits_measure(flce, torch, hd, wd, yd, wl, args, stream):

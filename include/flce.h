@@ -191,6 +191,23 @@ int flce_fwd_fp8(const void* h_q, const float* h_scale, const void* w_q, const f
                  float* lse_out, hipStream_t stream);
 
 /*
+ * Backward from the saved LSE for the FP8 inputs of flce_fwd_fp8: dH and dW of
+ * grad_out * loss with respect to the dequantised H and W (what a caller that
+ * keeps fp8 copies of bf16 weights updates them with).  The logits are
+ * recomputed from the e4m3 operands exactly as flce_fwd_fp8 formed them and
+ * turned into G = softmax - onehot (scaled) as in flce_bwd; the two
+ * contractions run on bf16 copies of the dequantised H and W (rounded to
+ * nearest even), which the call keeps in its workspace (2 (n + v) d bytes more
+ * than flce_bwd's).
+ *   lse, grad_out   as for flce_bwd (lse from flce_fwd_fp8 on the same inputs).
+ *   dh_out, dw_out  device, bf16 [n, d] and [v, d], 16-byte aligned; overwritten.
+ * Other arguments and errors as for flce_fwd_fp8.
+ */
+int flce_bwd_fp8(const void* h_q, const float* h_scale, const void* w_q, const float* w_scale, const int64_t* labels,
+                 const float* lse, const float* grad_out, int64_t n, int64_t d, int64_t v, int64_t ignore_index,
+                 flce_reduction reduction, void* dh_out, void* dw_out, hipStream_t stream);
+
+/*
  * Vocabulary shards.  The vocabulary rows of W are split into contiguous
  * shards [v_first, v_first + v_shard); each shard's partial statistics are
  * computed on its own and merged exactly, because the log-sum-exp of a row is

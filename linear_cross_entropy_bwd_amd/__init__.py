@@ -28,6 +28,7 @@ EXPORTED = (
     "flce_bwd",
     "flce_ce_logits",
     "flce_fwd_fp8",
+    "flce_bwd_fp8",
     "flce_fwd_shard",
     "flce_merge_shards",
     "flce_bwd_shard",
@@ -87,6 +88,8 @@ def lib() -> ctypes.CDLL:
     L.flce_ce_logits.restype = i32
     L.flce_fwd_fp8.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i32, p, p, p]
     L.flce_fwd_fp8.restype = i32
+    L.flce_bwd_fp8.argtypes = [p, p, p, p, p, p, p, i64, i64, i64, i64, i32, p, p, p]
+    L.flce_bwd_fp8.restype = i32
     L.flce_fwd_shard.argtypes = [p, p, p, i64, i64, i64, i64, i32, i64, p, p, p]
     L.flce_fwd_shard.restype = i32
     L.flce_merge_shards.argtypes = [p, p, i64, p, i64, i64, i32, p, p, p]
@@ -165,6 +168,13 @@ def flce_fwd_fp8(h_q, h_scale, w_q, w_scale, labels, n, d, v, ignore_index, redu
                  stream) -> int:
     return lib().flce_fwd_fp8(_ptr(h_q), _ptr(h_scale), _ptr(w_q), _ptr(w_scale), _ptr(labels), n, d, v,
                               ignore_index, reduction, _ptr(loss_out), _ptr(lse_out), _stream(stream))
+
+
+def flce_bwd_fp8(h_q, h_scale, w_q, w_scale, labels, lse, grad_out, n, d, v, ignore_index, reduction, dh_out, dw_out,
+                 stream) -> int:
+    return lib().flce_bwd_fp8(_ptr(h_q), _ptr(h_scale), _ptr(w_q), _ptr(w_scale), _ptr(labels), _ptr(lse),
+                              _ptr(grad_out), n, d, v, ignore_index, reduction, _ptr(dh_out), _ptr(dw_out),
+                              _stream(stream))
 
 
 def flce_fwd_shard(h, w_shard, labels, n, d, v_shard, v_first, dtype, ignore_index, lse_part_out, zy_part_out,
@@ -469,4 +479,24 @@ def linear_cross_entropy_forward_fp8(h_q, h_scale, w_q, w_scale, labels, ignore_
     if st != FLCE_OK:
         raise FlceError(st, "flce_fwd_fp8")
     return loss, lse
+
+
+def linear_cross_entropy_backward_fp8(h_q, h_scale, w_q, w_scale, labels, lse, grad_out=None,
+                                      ignore_index: int = -100, reduction: str = "mean"):
+    """dH and dW (bf16) of ``grad_out * loss`` with respect to the dequantised H and W,
+    from the LSE flce_fwd_fp8 returned (flce_bwd_fp8)."""
+    import torch
+    n, d = h_q.shape
+    v = w_q.shape[0]
+    if lse.dtype != torch.float32 or lse.shape != (n,) or not lse.is_contiguous() or not lse.is_cuda:
+        raise ValueError("lse must be a contiguous fp32 [n] device tensor")
+    if grad_out is not None and (grad_out.dtype != torch.float32 or grad_out.numel() != 1 or not grad_out.is_cuda):
+        raise ValueError("grad_out must be a one-element fp32 device tensor")
+    dh = torch.empty(n, d, dtype=torch.bfloat16, device=h_q.device)
+    dw = torch.empty(v, d, dtype=torch.bfloat16, device=h_q.device)
+    st = flce_bwd_fp8(h_q, h_scale, w_q, w_scale, labels, lse, grad_out, n, d, v, ignore_index, _red_code(reduction), dh,
+                      dw, torch.cuda.current_stream(h_q.device))
+    if st != FLCE_OK:
+        raise FlceError(st, "flce_bwd_fp8")
+    return dh, dw
 

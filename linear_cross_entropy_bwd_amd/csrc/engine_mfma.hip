@@ -620,7 +620,6 @@ __device__ __forceinline__ void logits_grad_epilogue(const LogitsArgs& a, Acc& a
 
 template <bool RECOMP, bool FP8 = false>
 __global__ __launch_bounds__(kThreads) void mfma_logits_kernel(LogitsArgs a) {
-  static_assert(!(RECOMP && FP8), "the fp8 logits serve the forward statistics only");
   const int64_t nb = a.tiles_m * a.tiles_n;
   const int64_t t = xcd_remap(blockIdx.x, nb);
   int64_t tm, tn;
@@ -1049,8 +1048,11 @@ hipError_t mfma_logits(const Plan& p, const Work& w, const ChunkArgs& c, int mod
   a.w_scale = c.w_scale;
   const dim3 grid(static_cast<unsigned>(a.tiles_m * a.tiles_n));
   if (c.fp8) {
-    if (mode != LOGITS_STATS) return hipErrorInvalidValue;
-    mfma_logits_kernel<false, true><<<grid, kThreads, 0, s>>>(a);
+    if (mode == LOGITS_PROB) return hipErrorInvalidValue;  // the fp8 path has no one-pass backward
+    if (mode == LOGITS_GRAD_FROM_LSE)
+      mfma_logits_kernel<true, true><<<grid, kThreads, 0, s>>>(a);
+    else
+      mfma_logits_kernel<false, true><<<grid, kThreads, 0, s>>>(a);
   } else if (mode == LOGITS_GRAD_FROM_LSE) {
     mfma_logits_kernel<true><<<grid, kThreads, 0, s>>>(a);
   } else {

@@ -183,7 +183,7 @@ struct Prof {
 Prof g_prof;
 
 const char* const kKindNames[K_NUM_KINDS] = {"label_scan", "logits_lse", "lse_merge",   "grad_inplace", "dh_gemm",
-                                             "dh_reduce",  "dw_gemm",    "loss_reduce", "ce_rows"};
+                                             "dh_reduce",  "dw_gemm",    "loss_reduce", "ce_rows",      "dequant_e4m3"};
 
 template <class F>
 hipError_t timed(int kind, hipStream_t s, F&& launch) {
@@ -466,6 +466,84 @@ int call_fwd_fp8(const void* h_q, const float* h_scale, const void* w_q, const f
   });
 }
 
+// The backward from the saved LSE for e4m3 inputs: H and W are dequantised to
+// bf16 in the workspace; per chunk the fp8 logits are recomputed (the forward's
+// exact logits) and their epilogue writes G, then dH and dW run on the bf16
+// copies.  `p` is the bf16 plan over d; `p8` the fp8 plan over d / 2 units,
+// whose chunk rows and vocabulary pitch are the same.
+int call_bwd_fp8(const void* h_q, const float* h_scale, const void* w_q, const float* w_scale, const int64_t* labels,
+                 const float* lse, const float* grad_out, int64_t n, int64_t d, int64_t v, int64_t ignore_index,
+                 flce_reduction reduction, void* dh_out, void* dw_out, hipStream_t stream) {
+  if (h_q == nullptr || w_q == nullptr || h_scale == nullptr || w_scale == nullptr || labels == nullptr ||
+      lse == nullptr || dh_out == nullptr || dw_out == nullptr)
+    return FLCE_ERR_INVALID_ARG;
+  if (n <= 0 || d <= 0 || v <= 0) return FLCE_ERR_INVALID_ARG;
+  if (reduction != FLCE_MEAN && reduction != FLCE_SUM) return FLCE_ERR_INVALID_ARG;
+  if (d % 16 != 0 || !aligned(h_q, 16) || !aligned(w_q, 16) || !aligned(w_scale, 16) || !aligned(h_scale, 4) ||
+      !aligned(labels, 8) || !aligned(lse, 4) || !aligned(dh_out, 16) || !aligned(dw_out, 16) ||
+      (grad_out != nullptr && !aligned(grad_out, 4)))
+    return FLCE_ERR_ALIGNMENT;
+  Plan p, p8;
+  int st = make_plan(n, d, v, FLCE_BF16, 1, &p);
+  if (st != FLCE_OK) return st;
+  st = make_plan(n, d / 2, v, FLCE_BF16, 0, &p8);
+  if (st != FLCE_OK) return st;
+  if (p8.chunk != p.chunk || p8.vp != p.vp || !mul_ok(v, d)) return FLCE_ERR_INVALID_ARG;
+  const size_t off_w16 = p.total;
+  const size_t off_h16 = off_w16 + align_up(sizeof(uint16_t) * static_cast<size_t>(v) * static_cast<size_t>(d));
+  p.total = off_h16 + align_up(sizeof(uint16_t) * static_cast<size_t>(n) * static_cast<size_t>(d));
+  return with_workspace(p, stream, [&](const Work& wk) {
+    uint16_t* w16 = reinterpret_cast<uint16_t*>(wk.base + off_w16);
+    uint16_t* h16 = reinterpret_cast<uint16_t*>(wk.base + off_h16);
+    hipError_t e = timed(K_DEQUANT, stream, [&] { return launch_dequant_e4m3(w_q, w_scale, v, d, w16, stream); });
+    if (e == hipSuccess)
+      e = timed(K_DEQUANT, stream, [&] { return launch_dequant_e4m3(h_q, h_scale, n, d, h16, stream); });
+    if (e == hipSuccess) e = timed(K_LABEL_SCAN, stream, [&] { return launch_label_scan(p, wk, labels, ignore_index, stream); });
+    if (e != hipSuccess) return e;
+    for (int64_t c = 0; c < p.nchunks; ++c) {
+      ChunkArgs a;
+      a.row0 = c * p.chunk;
+      a.rows = p.n - a.row0 < p.chunk ? p.n - a.row0 : p.chunk;
+      a.labels = labels + a.row0;
+      a.ignore_index = ignore_index;
+      a.reduction = reduction;
+      a.lse_rows = nullptr;
+      a.lse_in = lse + a.row0;
+      a.grad_out = grad_out;
+      a.zy_rows = nullptr;
+      a.dh_f32 = 0;
+      a.dw_mode = p.nchunks == 1 ? DW_SINGLE : (c == 0 ? DW_FIRST : (c == p.nchunks - 1 ? DW_LAST : DW_MID));
+      // recompute: fp8 operands, G into the chunk buffer
+      a.fp8 = 1;
+      a.h = static_cast<const char*>(h_q) + a.row0 * d;
+      a.w = w_q;
+      a.h_scale = h_scale + a.row0;
+      a.w_scale = w_scale;
+      a.dh = nullptr;
+      a.dw = nullptr;
+      e = timed(K_LOGITS, stream, [&] { return mfma_logits(p8, wk, a, LOGITS_GRAD_FROM_LSE, stream); });
+      if (e != hipSuccess) return e;
+      // the contractions: bf16 copies
+      a.fp8 = 0;
+      a.h_scale = nullptr;
+      a.w_scale = nullptr;
+      a.h = h16 + a.row0 * d;
+      a.w = w16;
+      a.dh = static_cast<char*>(dh_out) + a.row0 * d * 2;
+      a.dw = dw_out;
+      e = timed(K_DH, stream, [&] { return mfma_dh(p, wk, a, stream); });
+      if (e != hipSuccess) return e;
+      if (p.dh_splits > 1) {
+        e = timed(K_DH_REDUCE, stream, [&] { return launch_dh_reduce(p, wk, a, stream); });
+        if (e != hipSuccess) return e;
+      }
+      e = timed(K_DW, stream, [&] { return mfma_dw(p, wk, a, stream); });
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  });
+}
+
 // ---- vocabulary shards ---------------------------------------------------------
 
 // A shard's plan plus room for its shifted labels (int64 [n]) after the plan's workspace.
@@ -607,6 +685,13 @@ int flce_fwd_fp8(const void* h_q, const float* h_scale, const void* w_q, const f
                  float* lse_out, hipStream_t stream) {
   return flce::call_fwd_fp8(h_q, h_scale, w_q, w_scale, labels, n, d, v, ignore_index, reduction, loss_out, lse_out,
                             stream);
+}
+
+int flce_bwd_fp8(const void* h_q, const float* h_scale, const void* w_q, const float* w_scale, const int64_t* labels,
+                 const float* lse, const float* grad_out, int64_t n, int64_t d, int64_t v, int64_t ignore_index,
+                 flce_reduction reduction, void* dh_out, void* dw_out, hipStream_t stream) {
+  return flce::call_bwd_fp8(h_q, h_scale, w_q, w_scale, labels, lse, grad_out, n, d, v, ignore_index, reduction,
+                            dh_out, dw_out, stream);
 }
 
 int flce_fwd_shard(const void* h, const void* w_shard, const int64_t* labels, int64_t n, int64_t d, int64_t v_shard,

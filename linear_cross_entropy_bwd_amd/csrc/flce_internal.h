@@ -68,7 +68,8 @@ enum Kind : int {
   K_DW = 6,
   K_LOSS = 7,
   K_CE_ROWS = 8,
-  K_NUM_KINDS = 9
+  K_DEQUANT = 9,
+  K_NUM_KINDS = 10
 };
 
 // What the logits contraction's epilogue produces.
@@ -113,6 +114,8 @@ hipError_t launch_dh_reduce(const Plan& p, const Work& w, const ChunkArgs& a, hi
 hipError_t launch_label_count(const int64_t* labels, int64_t n, int64_t ignore_index, int32_t* nvalid, hipStream_t s);
 hipError_t launch_loss_sum(const float* loss_rows, int64_t n, const int32_t* nvalid, int32_t reduction,
                            float* loss_out, hipStream_t s);
+// e4m3 rows with one scale per row -> bf16 (d a multiple of 16).
+hipError_t launch_dequant_e4m3(const void* q, const float* scale, int64_t rows, int64_t d, void* out, hipStream_t s);
 // Vocabulary shards.
 hipError_t launch_shift_labels(const int64_t* labels, int64_t n, int64_t first, int64_t* out, hipStream_t s);
 hipError_t launch_shard_merge(const float* lse_parts, const float* zy_parts, int64_t shards, int64_t n,

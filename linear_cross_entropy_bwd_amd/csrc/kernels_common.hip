@@ -209,6 +209,38 @@ __global__ __launch_bounds__(256) void shard_merge_kernel(const float* __restric
   loss_rows[i] = labels[i] != ignore_index ? l - zy : 0.0f;
 }
 
+// out[r, k] = bf16(e4m3(q[r, k]) * scale[r]), rounded to nearest even.  e4m3
+// (OCP): sign, 4 exponent bits with bias 7, 3 mantissa bits; exponent 0 is
+// subnormal (m / 8 * 2^-6), S.1111.111 is NaN.  Each thread converts 16 bytes.
+__global__ __launch_bounds__(256) void dequant_e4m3_kernel(const uint8_t* __restrict__ q,
+                                                           const float* __restrict__ scale, int64_t rows,
+                                                           int64_t d, bf16_t* __restrict__ out) {
+  const int64_t vecs_per_row = d / 16;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= rows * vecs_per_row) return;
+  const int64_t r = i / vecs_per_row;
+  const float s = scale[r];
+  const uint4 u = *reinterpret_cast<const uint4*>(q + i * 16);
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+  uint32_t o[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    float f[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t c = (w[j >> 1] >> (8 * (2 * (j & 1) + h))) & 0xffu;
+      const uint32_t e = (c >> 3) & 0xfu, m = c & 0x7u;
+      float v = e == 0 ? static_cast<float>(m) * 0.001953125f : __uint_as_float(((e + 120u) << 23) | (m << 20));
+      if (e == 15 && m == 7) v = __uint_as_float(0x7fc00000u);
+      f[h] = ((c & 0x80u) ? -v : v) * s;
+    }
+    o[j] = pack_bf16x2(f[0], f[1]);
+  }
+  uint4* dst = reinterpret_cast<uint4*>(out + i * 16);
+  dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+  dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+}
+
 // loss = scale * sum_i loss_rows[i], summed in fp64 in a fixed order.
 __global__ __launch_bounds__(1024) void loss_reduce_kernel(const float* __restrict__ loss_rows, int64_t n,
                                                            const int32_t* __restrict__ nvalid, int32_t reduction,
@@ -308,6 +340,13 @@ hipError_t launch_sum_parts(const float* parts, int64_t num_parts, int64_t count
     dh_reduce_kernel<bf16_t><<<blocks, 256, 0, s>>>(parts, num_parts, count, count, static_cast<bf16_t*>(out));
   else
     dh_reduce_kernel<float><<<blocks, 256, 0, s>>>(parts, num_parts, count, count, static_cast<float*>(out));
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant_e4m3(const void* q, const float* scale, int64_t rows, int64_t d, void* out, hipStream_t s) {
+  const int64_t n = rows * (d / 16);
+  dequant_e4m3_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(
+      static_cast<const uint8_t*>(q), scale, rows, d, static_cast<bf16_t*>(out));
   return hipGetLastError();
 }
 

@@ -3,6 +3,7 @@ from .flce_oracle import (  # noqa: F401
     IGNORE_INDEX,
     ce_on_logits,
     decode_e4m3,
+    flce_backward_fp8,
     flce_backward_from_lse,
     flce_forward,
     flce_forward_fp8,

@@ -376,3 +376,18 @@ def flce_forward_fp8(h_q, h_scale, w_q, w_scale, labels, ignore_index: int = IGN
     return flce_forward(h, w, labels, ignore_index=ignore_index, reduction=reduction, block_rows=block_rows,
                         workers=workers)
 
+
+def flce_backward_fp8(h_q, h_scale, w_q, w_scale, labels, lse, grad_out: float = 1.0,
+                      ignore_index: int = IGNORE_INDEX, reduction: str = "mean"):
+    """(dH, dW) float64 of ``grad_out * loss`` with respect to the dequantised H and W
+    of e4m3 inputs with per-row scales, from the saved per-row LSE."""
+    def codes(x):
+        if hasattr(x, "detach"):
+            import torch
+            x = x.detach().to("cpu").contiguous().view(torch.uint8).numpy()
+        return np.asarray(x, dtype=np.uint8)
+    h = decode_e4m3(codes(h_q)) * _as_f64(h_scale)[:, None]
+    w = decode_e4m3(codes(w_q)) * _as_f64(w_scale)[:, None]
+    return flce_backward_from_lse(h, w, labels, lse, grad_out=grad_out, ignore_index=ignore_index,
+                                  reduction=reduction)
+

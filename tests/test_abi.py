@@ -231,6 +231,24 @@ def test_fp8_argument_errors_before_any_device_work():
     assert call(d=(1 << 25) + 32) == flce.FLCE_ERR_INVALID_ARG   # beyond the engine's row length
 
 
+def test_fp8_backward_argument_errors_before_any_device_work():
+    A = 1 << 20
+    ok = dict(h_q=A, h_scale=A, w_q=A, w_scale=A, labels=A, lse=A, grad_out=None, n=4, d=64, v=300,
+              ignore_index=-100, reduction=flce.FLCE_MEAN, dh_out=A, dw_out=A, stream=None)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return flce.flce_bwd_fp8(**a)
+
+    for k in ("h_q", "h_scale", "w_q", "w_scale", "labels", "lse", "dh_out", "dw_out"):
+        assert call(**{k: None}) == flce.FLCE_ERR_INVALID_ARG, k
+    assert call(v=0) == flce.FLCE_ERR_INVALID_ARG
+    assert call(d=40) == flce.FLCE_ERR_ALIGNMENT
+    assert call(dw_out=A + 8) == flce.FLCE_ERR_ALIGNMENT
+    assert call(grad_out=A + 2) == flce.FLCE_ERR_ALIGNMENT
+
+
 def test_vocab_shard_bounds():
     assert flce.vocab_shard_bounds(128256, 8)[0] == (0, 15872)
     for v, q in [(128256, 8), (1000, 3), (5, 5), (1 << 20, 7), (300, 2)]:

@@ -76,3 +76,75 @@ def test_fp8_llama3_8b_head_full_size():
     torch.cuda.synchronize()
     rloss, rlse = flce_forward_fp8(hq, hs, wq, ws, y, reduction=wl.reduction, workers=WORKERS)
     _check(float(loss.item()), to_f64(lse), rloss, rlse, "fp8 llama head")
+
+
+# --- backward from the saved LSE --------------------------------------------------
+
+def _deq(q, s):
+    from oracle import decode_e4m3
+    return decode_e4m3(q.numpy()) * s.double().numpy()[:, None]
+
+
+@pytest.mark.parametrize("shape,reduction", CASES[:3])
+def test_fp8_backward_from_oracle_lse(shape, reduction):
+    """flce_bwd_fp8 from the oracle's LSE (rounded to fp32), upstream gradient 0.5: dH
+    and dW against the oracle's backward on the dequantised matrices (the kernels
+    round the dequantised H and W to bf16 for the two contractions)."""
+    from oracle import flce_backward_fp8
+    n, d, v = shape
+    wl = Workload(f"fp8b_{n}_{d}_{v}", n, d, v, "bf16", 0.1, "uniform", 0.1, reduction, seed=80 + n)
+    hq, hs, wq, ws, y = make_inputs_fp8(wl, threads=4)
+    say(f"[fp8] backward n={n} d={d} v={v} {reduction}")
+    _, rlse = flce_forward_fp8(hq, hs, wq, ws, y, reduction=reduction)
+    lse32 = rlse.astype(np.float32)
+    rdh, rdw = flce_backward_fp8(hq, hs, wq, ws, y, lse32.astype(np.float64), grad_out=0.5, reduction=reduction)
+    go = torch.tensor([0.5], dtype=torch.float32, device=DEV)
+    dh, dw = flce.linear_cross_entropy_backward_fp8(hq.to(DEV), hs.to(DEV), wq.to(DEV), ws.to(DEV), y.to(DEV),
+                                                    torch.from_numpy(lse32).to(DEV), go, reduction=reduction)
+    torch.cuda.synchronize()
+    from gpu_helpers import rel_max
+    e = dict(dh=rel_max(to_f64(dh), rdh), dw=rel_max(to_f64(dw), rdw))
+    say(f"  errors {e}")
+    tol = TOL[torch.bfloat16]["grad"]
+    assert e["dh"] <= tol and e["dw"] <= tol
+
+
+def test_fp8_forward_then_backward_end_to_end():
+    from oracle import flce_forward_backward
+    from gpu_helpers import rel_max
+    n, d, v = 300, 256, 5000
+    wl = Workload("fp8_e2e", n, d, v, "bf16", 0.1, "uniform", 0.1, "mean", seed=85)
+    hq, hs, wq, ws, y = make_inputs_fp8(wl, threads=4)
+    say("[fp8] forward then backward, end to end")
+    _, _, rdh, rdw = flce_forward_backward(_deq(hq, hs), _deq(wq, ws), y)
+    args = (hq.to(DEV), hs.to(DEV), wq.to(DEV), ws.to(DEV), y.to(DEV))
+    _, lse = flce.linear_cross_entropy_forward_fp8(*args)
+    dh, dw = flce.linear_cross_entropy_backward_fp8(*args, lse)
+    torch.cuda.synchronize()
+    tol = TOL[torch.bfloat16]["grad"]
+    assert rel_max(to_f64(dh), rdh) <= tol and rel_max(to_f64(dw), rdw) <= tol
+
+
+@pytest.mark.slow
+def test_fp8_backward_llama3_8b_head_full_size():
+    from oracle import flce_dw_rows, flce_rows
+    from gpu_helpers import rel_max
+    wl = CONFIGS["llama3_8b_head"]
+    say(f"[fp8] backward llama3 8b head n={wl.n} d={wl.d} v={wl.v}")
+    hq, hs, wq, ws, y = make_inputs_fp8(wl)
+    h64, w64 = _deq(hq, hs), _deq(wq, ws)
+    _, rlse = flce_forward_fp8(hq, hs, wq, ws, y, reduction=wl.reduction, workers=WORKERS)
+    lse32 = rlse.astype(np.float32)
+    dh, dw = flce.linear_cross_entropy_backward_fp8(hq.to(DEV), hs.to(DEV), wq.to(DEV), ws.to(DEV), y.to(DEV),
+                                                    torch.from_numpy(lse32).to(DEV), reduction=wl.reduction)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(93)
+    rows = sorted({0, wl.n - 1, *(int(r) for r in rng.choice(wl.n, 12, replace=False))})
+    _, rdh = flce_rows(h64, w64, y, rows, reduction=wl.reduction)
+    cols = sorted({0, wl.v - 1, *(int(c) for c in rng.choice(wl.v, 8, replace=False))})
+    rdw = flce_dw_rows(h64, w64, y, lse32.astype(np.float64), cols, reduction=wl.reduction)
+    e_dh = rel_max(to_f64(dh[torch.tensor(rows, device=DEV)]), rdh)
+    e_dw = rel_max(to_f64(dw[torch.tensor(cols, device=DEV)]), rdw)
+    say(f"  sampled dH rel {e_dh:.2e}, dW rel {e_dw:.2e}")
+    tol = TOL[torch.bfloat16]["grad"]
+    assert e_dh <= tol and e_dw <= tol

@@ -18,7 +18,7 @@ import pytest
 import torch
 
 from oracle import (ce_on_logits, decode_e4m3, flce_backward_from_lse, flce_dw_rows, flce_forward, flce_forward_backward,
-                    flce_forward_fp8, flce_rows, log_sum_exp, merge_vocab_shards, vocab_shard_backward,
+                    flce_backward_fp8, flce_forward_fp8, flce_rows, log_sum_exp, merge_vocab_shards, vocab_shard_backward,
                     vocab_shard_partials)
 
 RTOL = 1e-12
@@ -556,4 +556,26 @@ def test_fp8_forward_zero_weight_codes():
     loss, lse = flce_forward_fp8(hq, np.full(n, 3.0), np.zeros((v, d), np.uint8), np.full(v, 2.0), np.arange(n))
     assert loss == pytest.approx(math.log(v), rel=1e-14)
     _close(lse, np.full(n, math.log(v)))
+
+
+def test_fp8_backward_torch_autograd():
+    """Library routine: torch autograd of grad_out * cross-entropy (float64) on the
+    dequantised matrices, from the forward's LSE."""
+    g = np.random.default_rng(62)
+    n, d, v = 19, 32, 40
+    hq = torch.from_numpy(g.standard_normal((n, d)).astype(np.float32) * 30).to(torch.float8_e4m3fn)
+    wq = torch.from_numpy(g.standard_normal((v, d)).astype(np.float32) * 30).to(torch.float8_e4m3fn)
+    hs = torch.from_numpy(g.uniform(0.002, 0.02, n).astype(np.float32))
+    ws = torch.from_numpy(g.uniform(0.002, 0.02, v).astype(np.float32))
+    y = g.integers(0, v, n).astype(np.int64)
+    y[2] = -100
+    _, lse = flce_forward_fp8(hq.view(torch.uint8), hs, wq.view(torch.uint8), ws, y, reduction="sum")
+    dh, dw = flce_backward_fp8(hq.view(torch.uint8), hs, wq.view(torch.uint8), ws, y, lse, grad_out=-0.8,
+                               reduction="sum")
+    ht = (hq.to(torch.float64) * hs.double()[:, None]).requires_grad_(True)
+    wt = (wq.to(torch.float64) * ws.double()[:, None]).requires_grad_(True)
+    lt = torch.nn.functional.cross_entropy(ht @ wt.T, torch.from_numpy(y), ignore_index=-100, reduction="sum")
+    lt.backward(torch.tensor(-0.8, dtype=torch.float64))
+    _close(dh, ht.grad.numpy())
+    _close(dw, wt.grad.numpy())
 
