@@ -1,13 +1,16 @@
 // fp32 engine: LDS-tiled FMA contractions for FLCE_F32 inputs.
 //
 // One 64x64 output tile per 256-thread block, 4x4 outputs per thread, K in
-// steps of 16 staged through LDS in k-major order.  Operands are described by
-// (pointer, leading dimension, k-major flag): a k-major operand has its
-// reduction index contiguous in memory.  The three contractions are
+// steps of 64 staged through LDS in [k][m] order.  The next step's operand
+// values are loaded into registers before the current step's FMAs, so their
+// latency hides under the arithmetic.  Operands are described by (pointer,
+// leading dimension, k-major flag): a k-major operand has its reduction index
+// contiguous in memory.  The three contractions are
 //   logits  Z[t, j]  = sum_k H[t, k] W[j, k]        A = H (k-major), B = W (k-major)
 //   dH      dH[t, k] = sum_j G[t, j] W[j, k]        A = G (k-major), B = W (n-major)
 //   dW      dW[j, k] = sum_t G[t, j] H[t, k]        A = G^T (m-major), B = H (n-major)
-// fp32 inputs keep fp32 products and sums, which the fp32 tolerances need.
+// fp32 inputs keep fp32 products and sums, which the fp32 tolerances need;
+// each output is one fmaf chain over k in increasing order.
 #include "device_util.h"
 #include "flce_internal.h"
 
@@ -15,74 +18,98 @@ namespace flce {
 
 namespace {
 
-constexpr int BM = 64, BN = 64, BK = 16;
-constexpr int kPad = 4;
+constexpr int BM = 64, BN = 64, BK = 64;
+constexpr int kPad = 4;  // keeps rows 16-byte aligned for the float4 fragment reads
+constexpr int kPer = BK * BM / 256;  // operand values each thread stages per step
 
 template <typename TA, typename TB, bool A_KMAJ, bool B_KMAJ>
 struct TileLoop {
+  // A thread stages 16 values per operand and step.  The 64 lanes of a wave
+  // run along the operand's contiguous index (k for a k-major operand, m
+  // otherwise), so each load instruction reads 64 consecutive values; the
+  // wave's other index steps by 4 from the wave number.  Loads use indices
+  // clamped into the operand and are issued unconditionally; the values
+  // outside it are replaced by 0 only when they are written to LDS, so
+  // nothing uses a loaded value before the step that needs it.
+  template <bool KMAJ, typename T>
+  static __device__ __forceinline__ void fetch(const T* __restrict__ P, int64_t ld, int64_t M, int64_t K,
+                                               int64_t m0, int64_t k0, float (&r)[kPer]) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t lim_fix = KMAJ ? K : M, lim_step = KMAJ ? M : K;
+    const int64_t g_fix = (KMAJ ? k0 : m0) + lane;
+    const int64_t c_fix = g_fix < lim_fix ? g_fix : lim_fix - 1;
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      const int64_t g_step = (KMAJ ? m0 : k0) + wave + 4 * q;
+      const int64_t c_step = g_step < lim_step ? g_step : lim_step - 1;
+      r[q] = Elem<T>::ld(P, c_step * ld + c_fix);
+    }
+  }
+
+  // LDS holds [k][m]: a k-major operand is transposed here.  (m0, k0) is the
+  // step the values were fetched for.
+  template <bool KMAJ>
+  static __device__ __forceinline__ void stash(float (*S)[BM + kPad], const float (&r)[kPer], int64_t M, int64_t K,
+                                               int64_t m0, int64_t k0) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t lim_fix = KMAJ ? K : M, lim_step = KMAJ ? M : K;
+    const bool fix_in = (KMAJ ? k0 : m0) + lane < lim_fix;
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      const bool in = fix_in && (KMAJ ? m0 : k0) + wave + 4 * q < lim_step;
+      const float x = in ? r[q] : 0.0f;
+      if (KMAJ)
+        S[lane][wave + 4 * q] = x;
+      else
+        S[wave + 4 * q][lane] = x;
+    }
+  }
+
   // Accumulate acc[4][4] for the tile at (m0, n0); rows m < M, cols n < N, k < K.
+  // M, N >= 1; K may be 0 (an empty vocabulary split), which leaves zeros.
   static __device__ __forceinline__ void run(const TA* __restrict__ A, int64_t lda, const TB* __restrict__ B,
                                              int64_t ldb, int64_t M, int64_t N, int64_t K, int64_t m0, int64_t n0,
                                              float (&acc)[4][4]) {
-    __shared__ float As[BK][BM + kPad];
-    __shared__ float Bs[BK][BN + kPad];
+    __shared__ __align__(16) float As[BK][BM + kPad];
+    __shared__ __align__(16) float Bs[BK][BN + kPad];
     const int tid = threadIdx.x;
     const int tx = tid & 15, ty = tid >> 4;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
+    if (K <= 0) return;
 
+    float ra[kPer], rb[kPer];
+    fetch<A_KMAJ>(A, lda, M, K, m0, 0, ra);
+    fetch<B_KMAJ>(B, ldb, N, K, n0, 0, rb);
     for (int64_t k0 = 0; k0 < K; k0 += BK) {
-      // A tile: BM x BK, 4 elements per thread
-      if (A_KMAJ) {
-        const int m = tid >> 2, kq = (tid & 3) * 4;
-        const int64_t gm = m0 + m;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int64_t gk = k0 + kq + q;
-          As[kq + q][m] = (gm < M && gk < K) ? Elem<TA>::ld(A, gm * lda + gk) : 0.0f;
-        }
-      } else {
-        const int k = tid >> 4, mq = (tid & 15) * 4;
-        const int64_t gk = k0 + k;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int64_t gm = m0 + mq + q;
-          As[k][mq + q] = (gm < M && gk < K) ? Elem<TA>::ld(A, gk * lda + gm) : 0.0f;
-        }
-      }
-      if (B_KMAJ) {
-        const int nn = tid >> 2, kq = (tid & 3) * 4;
-        const int64_t gn = n0 + nn;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int64_t gk = k0 + kq + q;
-          Bs[kq + q][nn] = (gn < N && gk < K) ? Elem<TB>::ld(B, gn * ldb + gk) : 0.0f;
-        }
-      } else {
-        const int k = tid >> 4, nq = (tid & 15) * 4;
-        const int64_t gk = k0 + k;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int64_t gn = n0 + nq + q;
-          Bs[k][nq + q] = (gn < N && gk < K) ? Elem<TB>::ld(B, gk * ldb + gn) : 0.0f;
-        }
-      }
+      __syncthreads();  // the previous step's fragment reads are done
+      stash<A_KMAJ>(As, ra, M, K, m0, k0);
+      stash<B_KMAJ>(Bs, rb, N, K, n0, k0);
       __syncthreads();
-#pragma unroll
+      // the next step's loads (clamped, so in bounds past the end too) fly
+      // under this step's FMAs
+      fetch<A_KMAJ>(A, lda, M, K, m0, k0 + BK, ra);
+      fetch<B_KMAJ>(B, ldb, N, K, n0, k0 + BK, rb);
+      // fragment reads one k ahead of the FMAs that use them
+      float4 a = *reinterpret_cast<const float4*>(&As[0][ty * 4]);
+      float4 b = *reinterpret_cast<const float4*>(&Bs[0][tx * 4]);
+#pragma unroll 8
       for (int kk = 0; kk < BK; ++kk) {
-        float a[4], b[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) a[i] = As[kk][ty * 4 + i];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) b[j] = Bs[kk][tx * 4 + j];
+        const int kn = kk + 1 < BK ? kk + 1 : kk;
+        const float4 an = *reinterpret_cast<const float4*>(&As[kn][ty * 4]);
+        const float4 bn = *reinterpret_cast<const float4*>(&Bs[kn][tx * 4]);
+        __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of this k's FMAs
+        const float av[4] = {a.x, a.y, a.z, a.w};
+        const float bv[4] = {b.x, b.y, b.z, b.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+          for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
+        a = an;
+        b = bn;
       }
-      __syncthreads();
     }
   }
 };

@@ -45,8 +45,8 @@ __device__ __forceinline__ float row_scale(int32_t nvalid, int32_t reduction) {
 // row's NLL lse - z_y.  With the gradient, each partial max is replaced by
 // the factor scale_i * exp(m_g - lse) that turns the stored exp(z - m_g) into
 // the scaled softmax, and the value the target column takes is precomputed.
-constexpr int kMergeRows = 64;
-constexpr int kMergeSlices = 16;
+constexpr int kMergeRows = 32;    // 128-byte segments of one group's partials
+constexpr int kMergeSlices = 32;
 
 __global__ __launch_bounds__(kMergeRows* kMergeSlices) void lse_merge_kernel(
     float* __restrict__ pm, const float* __restrict__ ps, int64_t C, int64_t G, int64_t rows,
@@ -62,6 +62,7 @@ __global__ __launch_bounds__(kMergeRows* kMergeSlices) void lse_merge_kernel(
 
   float m = -INFINITY;
   if (live)
+#pragma unroll 4
     for (int64_t g = sl; g < G; g += kMergeSlices) m = fmaxf(m, pm[g * C + t]);
   red[sl][r] = m;
   __syncthreads();
@@ -71,6 +72,7 @@ __global__ __launch_bounds__(kMergeRows* kMergeSlices) void lse_merge_kernel(
 
   float s = 0.0f;
   if (live)
+#pragma unroll 4
     for (int64_t g = sl; g < G; g += kMergeSlices) {
       const float mg = pm[g * C + t];
       s += ps[g * C + t] * fast_exp(mg - m);
