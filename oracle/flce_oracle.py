@@ -43,7 +43,10 @@ written from the pages:
   and W with one scale per row is the forward of the dequantised matrices,
   ``z_ij = s_h[i] s_w[j] sum_k q_h[i, k] q_w[j, k]``; e4m3 is the OCP 8-bit
   float with 1 sign bit, 4 exponent bits (bias 7) and 3 mantissa bits,
-  subnormals at exponent 0 and no infinities (S.1111.111 is NaN);
+  subnormals at exponent 0 and no infinities (S.1111.111 is NaN); the FP8
+  backward is the gradient of that same loss with respect to the dequantised
+  H and W, from the saved LSE (the blog page's backward section applied to
+  the dequantised matrices);
 * ``reduction="mean"`` as in the loss module call on the lecture page
   ("GPU MODE lecture 028 - Liger Kernel", the LigerCrossEntropyLoss example);
   the mean is taken over the rows whose label is not ``ignore_index``, and a
@@ -54,6 +57,11 @@ Everything is computed in float64 from the exact float64 images of the inputs
 (bf16 and fp32 values convert exactly).  The row blocking below only bounds
 host memory; every block sees the full vocabulary, so no online merging
 happens here.
+
+Every public function is pinned, in ``tests/test_oracle_pins.py``, to
+something other than itself: closed forms, brute-force loops, finite
+differences, torch's float64 cross-entropy and autograd, the figures the blog
+page prints, and planted-mistake checks.  None is left unpinned.
 """
 from __future__ import annotations
 
