@@ -246,7 +246,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="llama3_8b_head")
-    ap.add_argument("--cpu-rows", type=int, default=3072, help="tokens in the oracle's CPU-baseline sample")
+    ap.add_argument("--cpu-rows", type=int, default=6144, help="tokens in the oracle's CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--all-configs", action="store_true",
                     help="also time flce_fwd_bwd on every workload (inputs drawn per workload) and report each")
