@@ -457,10 +457,9 @@ def linear_cross_entropy_vocab_split(h, w, labels, num_shards: int = 2, ignore_i
     return loss, lse, dh, dw
 
 
-def linear_cross_entropy_forward_fp8(h_q, h_scale, w_q, w_scale, labels, ignore_index: int = -100,
-                                     reduction: str = "mean"):
-    """Loss and LSE (flce_fwd_fp8) from e4m3 H [n, d] and W [v, d] (uint8 or float8_e4m3fn
-    device tensors) with fp32 per-row scales [n] and [v]."""
+def _check_fp8_inputs(h_q, h_scale, w_q, w_scale, labels):
+    """(n, d, v) of e4m3 operands with per-row fp32 scales and int64 labels, all
+    contiguous tensors on one device; raises before anything reaches the library."""
     import torch
     for t, name in ((h_q, "h_q"), (w_q, "w_q")):
         if not t.is_cuda or t.dim() != 2 or t.element_size() != 1 or not t.is_contiguous():
@@ -468,10 +467,23 @@ def linear_cross_entropy_forward_fp8(h_q, h_scale, w_q, w_scale, labels, ignore_
     for t, name in ((h_scale, "h_scale"), (w_scale, "w_scale")):
         if not t.is_cuda or t.dtype != torch.float32 or t.dim() != 1 or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous fp32 1-D device tensor")
+    if not labels.is_cuda or labels.dtype != torch.int64 or not labels.is_contiguous():
+        raise ValueError("labels must be a contiguous int64 device tensor")
+    if len({t.device for t in (h_q, h_scale, w_q, w_scale, labels)}) != 1:
+        raise ValueError("all inputs must be on one device")
     n, d = h_q.shape
     v = w_q.shape[0]
     if w_q.shape[1] != d or h_scale.shape[0] != n or w_scale.shape[0] != v or labels.shape != (n,):
         raise ValueError("shape mismatch")
+    return n, d, v
+
+
+def linear_cross_entropy_forward_fp8(h_q, h_scale, w_q, w_scale, labels, ignore_index: int = -100,
+                                     reduction: str = "mean"):
+    """Loss and LSE (flce_fwd_fp8) from e4m3 H [n, d] and W [v, d] (uint8 or float8_e4m3fn
+    device tensors) with fp32 per-row scales [n] and [v]."""
+    import torch
+    n, d, v = _check_fp8_inputs(h_q, h_scale, w_q, w_scale, labels)
     loss = torch.empty(1, dtype=torch.float32, device=h_q.device)
     lse = torch.empty(n, dtype=torch.float32, device=h_q.device)
     st = flce_fwd_fp8(h_q, h_scale, w_q, w_scale, labels, n, d, v, ignore_index, _red_code(reduction), loss, lse,
@@ -486,12 +498,12 @@ def linear_cross_entropy_backward_fp8(h_q, h_scale, w_q, w_scale, labels, lse, g
     """dH and dW (bf16) of ``grad_out * loss`` with respect to the dequantised H and W,
     from the LSE flce_fwd_fp8 returned (flce_bwd_fp8)."""
     import torch
-    n, d = h_q.shape
-    v = w_q.shape[0]
-    if lse.dtype != torch.float32 or lse.shape != (n,) or not lse.is_contiguous() or not lse.is_cuda:
-        raise ValueError("lse must be a contiguous fp32 [n] device tensor")
-    if grad_out is not None and (grad_out.dtype != torch.float32 or grad_out.numel() != 1 or not grad_out.is_cuda):
-        raise ValueError("grad_out must be a one-element fp32 device tensor")
+    n, d, v = _check_fp8_inputs(h_q, h_scale, w_q, w_scale, labels)
+    if lse.dtype != torch.float32 or lse.shape != (n,) or not lse.is_contiguous() or lse.device != h_q.device:
+        raise ValueError("lse must be a contiguous fp32 [n] tensor on the inputs' device")
+    if grad_out is not None and (grad_out.dtype != torch.float32 or grad_out.numel() != 1
+                                 or not grad_out.is_contiguous() or grad_out.device != h_q.device):
+        raise ValueError("grad_out must be a one-element fp32 tensor on the inputs' device")
     dh = torch.empty(n, d, dtype=torch.bfloat16, device=h_q.device)
     dw = torch.empty(v, d, dtype=torch.bfloat16, device=h_q.device)
     st = flce_bwd_fp8(h_q, h_scale, w_q, w_scale, labels, lse, grad_out, n, d, v, ignore_index, _red_code(reduction), dh,

@@ -263,3 +263,16 @@ def test_no_cpu_fallback(monkeypatch, tmp_path):
     monkeypatch.setattr(flce, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError):
         flce.lib()
+
+
+def test_fp8_wrappers_reject_host_tensors():
+    """The FP8 wrappers check their tensors before anything reaches the library."""
+    import torch
+    hq = torch.zeros(4, 16, dtype=torch.uint8)
+    wq = torch.zeros(8, 16, dtype=torch.uint8)
+    hs, ws = torch.ones(4), torch.ones(8)
+    y = torch.zeros(4, dtype=torch.int64)
+    with pytest.raises(ValueError):
+        flce.linear_cross_entropy_forward_fp8(hq, hs, wq, ws, y)
+    with pytest.raises(ValueError):
+        flce.linear_cross_entropy_backward_fp8(hq, hs, wq, ws, y, torch.zeros(4))

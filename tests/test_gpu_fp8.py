@@ -148,3 +148,26 @@ def test_fp8_backward_llama3_8b_head_full_size():
     say(f"  sampled dH rel {e_dh:.2e}, dW rel {e_dw:.2e}")
     tol = TOL[torch.bfloat16]["grad"]
     assert e_dh <= tol and e_dw <= tol
+
+
+def test_fp8_wrappers_check_inputs():
+    """Wrong label dtype, non-contiguous codes, short scales and a misshaped LSE raise
+    ValueError in the wrappers, before the library is called."""
+    wl = Workload("fp8_checks", 8, 32, 64, "bf16", 0.1, "uniform", 0.0, "mean", seed=90)
+    hq, hs, wq, ws, y = (t.to(DEV) for t in make_inputs_fp8(wl, threads=1))
+    lse = torch.zeros(8, dtype=torch.float32, device=DEV)
+    bad = [
+        (hq, hs, wq, ws, y.to(torch.int32)),
+        (hq.t().contiguous().t(), hs, wq, ws, y),
+        (hq, hs[:-1], wq, ws, y),
+        (hq, hs, wq, ws[:-1], y),
+    ]
+    for args in bad:
+        with pytest.raises(ValueError):
+            flce.linear_cross_entropy_forward_fp8(*args)
+        with pytest.raises(ValueError):
+            flce.linear_cross_entropy_backward_fp8(*args, lse)
+    with pytest.raises(ValueError):
+        flce.linear_cross_entropy_backward_fp8(hq, hs, wq, ws, y, lse[:-1])
+    with pytest.raises(ValueError):
+        flce.linear_cross_entropy_backward_fp8(hq, hs, wq, ws, y, lse, torch.ones(2, device=DEV))
