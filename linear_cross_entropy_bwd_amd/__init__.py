@@ -277,6 +277,30 @@ def _check_inputs(h, w, labels):
         raise TypeError("labels must be int64")
     if not (h.is_contiguous() and w.is_contiguous() and labels.is_contiguous()):
         raise ValueError("h, w and labels must be contiguous")
+    if not (h.device == w.device == labels.device):
+        raise ValueError("h, w and labels must be on one device")
+
+
+def _check_vec(t, n: int, device, name: str):
+    """A contiguous fp32 [n] tensor on `device` (a saved LSE or an LSE output)."""
+    import torch
+    if t.dtype != torch.float32 or tuple(t.shape) != (n,) or not t.is_contiguous() or t.device != device:
+        raise ValueError(f"{name} must be a contiguous fp32 [{n}] tensor on {device}")
+
+
+def _check_scalar(t, device, name: str):
+    """None, or a contiguous one-element fp32 tensor on `device` (an upstream gradient, a loss output)."""
+    import torch
+    if t is None:
+        return
+    if t.dtype != torch.float32 or t.numel() != 1 or not t.is_contiguous() or t.device != device:
+        raise ValueError(f"{name} must be a contiguous one-element fp32 tensor on {device}")
+
+
+def _check_out(t, like, name: str):
+    """A caller-supplied output: same shape, dtype and device as `like`, contiguous."""
+    if t.shape != like.shape or t.dtype != like.dtype or t.device != like.device or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {like.dtype} {tuple(like.shape)} tensor on {like.device}")
 
 
 def linear_cross_entropy(h, w, labels, ignore_index: int = -100, reduction: str = "mean", out=None):
@@ -297,6 +321,10 @@ def linear_cross_entropy(h, w, labels, ignore_index: int = -100, reduction: str 
         dw = torch.empty_like(w)
     else:
         loss, lse, dh, dw = out
+        _check_scalar(loss, h.device, "out loss")
+        _check_vec(lse, n, h.device, "out lse")
+        _check_out(dh, h, "out dh")
+        _check_out(dw, w, "out dw")
     st = flce_fwd_bwd(h, w, labels, n, d, v, _dtype_code(h), ignore_index, _red_code(reduction), loss, lse, dh, dw,
                       torch.cuda.current_stream(h.device))
     if st != FLCE_OK:
@@ -331,11 +359,12 @@ def linear_cross_entropy_backward(h, w, labels, lse, grad_out=None, ignore_index
     _check_inputs(h, w, labels)
     n, d = h.shape
     v = w.shape[0]
-    if lse.dtype != torch.float32 or lse.shape != (n,) or not lse.is_contiguous() or not lse.is_cuda:
-        raise ValueError("lse must be a contiguous fp32 [n] device tensor")
-    if grad_out is not None and (grad_out.dtype != torch.float32 or grad_out.numel() != 1 or not grad_out.is_cuda):
-        raise ValueError("grad_out must be a one-element fp32 device tensor")
+    _check_vec(lse, n, h.device, "lse")
+    _check_scalar(grad_out, h.device, "grad_out")
     dh, dw = (torch.empty_like(h), torch.empty_like(w)) if out is None else out
+    if out is not None:
+        _check_out(dh, h, "out dh")
+        _check_out(dw, w, "out dw")
     st = flce_bwd(h, w, labels, lse, grad_out, n, d, v, _dtype_code(h), ignore_index, _red_code(reduction), dh, dw,
                   torch.cuda.current_stream(h.device))
     if st != FLCE_OK:
@@ -353,6 +382,8 @@ def _check_logits(logits, labels):
         raise TypeError("labels must be int64")
     if not (logits.is_contiguous() and labels.is_contiguous()):
         raise ValueError("logits and labels must be contiguous")
+    if logits.device != labels.device:
+        raise ValueError("logits and labels must be on one device")
 
 
 def cross_entropy(logits, labels, ignore_index: int = -100, reduction: str = "mean", grad: Optional[str] = None):
@@ -387,7 +418,11 @@ def cross_entropy_backward(logits, labels, lse, grad_scale=None, ignore_index: i
     import torch
     _check_logits(logits, labels)
     n, v = logits.shape
+    _check_vec(lse, n, logits.device, "lse")
+    _check_scalar(grad_scale, logits.device, "grad_scale")
     g = torch.empty_like(logits) if out is None else out
+    if out is not None:
+        _check_out(g, logits, "out")   # may be `logits` itself: the gradient over the logits
     st = flce_ce_logits(logits, labels, n, v, _dtype_code(logits), ignore_index, _red_code(reduction), lse,
                         grad_scale, None, None, g, torch.cuda.current_stream(logits.device))
     if st != FLCE_OK:
@@ -426,8 +461,7 @@ def linear_cross_entropy_vocab_split(h, w, labels, num_shards: int = 2, ignore_i
     if bounds[0][0] != 0 or bounds[-1][1] != v or any(a >= b for a, b in bounds) or any(
             bounds[q][1] != bounds[q + 1][0] for q in range(len(bounds) - 1)):
         raise ValueError("shards must be contiguous, non-empty and cover [0, v)")
-    if grad_out is not None and (grad_out.dtype != torch.float32 or grad_out.numel() != 1 or not grad_out.is_cuda):
-        raise ValueError("grad_out must be a one-element fp32 device tensor")
+    _check_scalar(grad_out, h.device, "grad_out")
     q_n = len(bounds)
     dev = h.device
     stream = torch.cuda.current_stream(dev)
@@ -499,11 +533,8 @@ def linear_cross_entropy_backward_fp8(h_q, h_scale, w_q, w_scale, labels, lse, g
     from the LSE flce_fwd_fp8 returned (flce_bwd_fp8)."""
     import torch
     n, d, v = _check_fp8_inputs(h_q, h_scale, w_q, w_scale, labels)
-    if lse.dtype != torch.float32 or lse.shape != (n,) or not lse.is_contiguous() or lse.device != h_q.device:
-        raise ValueError("lse must be a contiguous fp32 [n] tensor on the inputs' device")
-    if grad_out is not None and (grad_out.dtype != torch.float32 or grad_out.numel() != 1
-                                 or not grad_out.is_contiguous() or grad_out.device != h_q.device):
-        raise ValueError("grad_out must be a one-element fp32 tensor on the inputs' device")
+    _check_vec(lse, n, h_q.device, "lse")
+    _check_scalar(grad_out, h_q.device, "grad_out")
     dh = torch.empty(n, d, dtype=torch.bfloat16, device=h_q.device)
     dw = torch.empty(v, d, dtype=torch.bfloat16, device=h_q.device)
     st = flce_bwd_fp8(h_q, h_scale, w_q, w_scale, labels, lse, grad_out, n, d, v, ignore_index, _red_code(reduction), dh,

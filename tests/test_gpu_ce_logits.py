@@ -174,3 +174,31 @@ def test_ce_more_rows_than_one_grid():
     loss_f, lse_f, _ = flce.cross_entropy(z.to(DEV), y.to(DEV), grad=None)
     torch.cuda.synchronize()
     _check(float(loss_f.item()), to_f64(lse_f), None, ref, wl.torch_dtype, "ce 65537 rows, forward")
+
+
+def test_wrappers_check_saved_lse_scale_and_outputs():
+    """A misshaped or wrongly typed saved LSE, upstream scale or output buffer raises
+    ValueError in the wrappers, before the library is called."""
+    n, v = 16, 300
+    z = torch.randn(n, v, device=DEV, dtype=torch.bfloat16)
+    y = torch.randint(0, v, (n,), device=DEV)
+    lse = torch.zeros(n, dtype=torch.float32, device=DEV)
+    for bad_lse in (lse[:-1], lse.double(), torch.zeros(2 * n, device=DEV)[::2]):
+        with pytest.raises(ValueError):
+            flce.cross_entropy_backward(z, y, bad_lse)
+    with pytest.raises(ValueError):
+        flce.cross_entropy_backward(z, y, lse, torch.ones(2, device=DEV))
+    with pytest.raises(ValueError):
+        flce.cross_entropy_backward(z, y, lse, out=torch.empty(n, v, device=DEV))      # fp32 for bf16 logits
+    g = flce.cross_entropy_backward(z.clone(), y, lse, out=None)
+    assert g.shape == z.shape
+    h = torch.randn(n, 64, device=DEV, dtype=torch.bfloat16)
+    w = torch.randn(v, 64, device=DEV, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        flce.linear_cross_entropy_backward(h, w, y, lse[:-1])
+    with pytest.raises(ValueError):
+        flce.linear_cross_entropy_backward(h, w, y, lse, out=(torch.empty_like(h), torch.empty(v, 32, device=DEV,
+                                                                                                dtype=torch.bfloat16)))
+    with pytest.raises(ValueError):
+        flce.linear_cross_entropy(h, w, y, out=(torch.empty(1, device=DEV), torch.empty(n, device=DEV),
+                                                torch.empty_like(h), torch.empty_like(w).t()))
