@@ -159,7 +159,10 @@ hipError_t device_pool(int dev, hipMemPool_t* out) {
     if (e != hipSuccess) return e;
     uint64_t keep = UINT64_MAX;  // keep freed blocks cached for the next call
     e = hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess) {
+      (void)hipMemPoolDestroy(pool);
+      return e;
+    }
     g_pools[dev] = pool;
     g_pool_init[dev] = true;
   }
