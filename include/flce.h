@@ -53,6 +53,15 @@
  * is a caller error that is not diagnosed on the device: the kernels never
  * index memory with a label, such a row counts as valid with a target logit
  * of 0 and no one-hot term.
+ *
+ * Environment overrides (read at every call and by flce_plan_info and
+ * flce_workspace_bytes; meant for tests and tuning, positive integers only,
+ * anything else is ignored): FLCE_CHUNK_ROWS (token rows per chunk, capped at
+ * n), FLCE_WORKSPACE_CAP_BYTES (budget for the chunk's probability buffer,
+ * default 1 GiB), FLCE_DH_SPLITS (split of dH's vocabulary reduction),
+ * FLCE_GROUP_LOGITS, FLCE_GROUP_DH, FLCE_GROUP_DW (tile-order group sizes of
+ * the three contractions on the bf16 engine).  Results stay within the
+ * stated tolerances under any of them; bitwise results can change.
  */
 #ifndef FLCE_H_
 #define FLCE_H_
