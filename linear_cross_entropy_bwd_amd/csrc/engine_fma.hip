@@ -19,27 +19,50 @@ namespace flce {
 namespace {
 
 constexpr int BM = 64, BN = 64, BK = 64;
-constexpr int kPad = 4;  // keeps rows 16-byte aligned for the float4 fragment reads
-constexpr int kPer = BK * BM / 256;  // operand values each thread stages per step
+constexpr int kPad = 4;  // keeps rows 16-byte aligned for the vector fragment reads
+// The logits tiles are 64 tokens x 32 vocabulary columns: small problems then
+// spread over twice as many workgroups.  Their 32 columns are one statistics
+// group, so the plan's fp32 group width must equal kLogitsBN.
+constexpr int kLogitsBN = 32;
 
-template <typename TA, typename TB, bool A_KMAJ, bool B_KMAJ>
+// Values of one fragment row: 4 (float4) or 2 (float2) consecutive floats.
+template <int W>
+__device__ __forceinline__ void read_row(const float* p, float (&v)[W]) {
+  static_assert(W == 4 || W == 2, "fragment rows are 2 or 4 wide");
+  if constexpr (W == 4) {
+    const float4 x = *reinterpret_cast<const float4*>(p);
+    v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+  } else {
+    const float2 x = *reinterpret_cast<const float2*>(p);
+    v[0] = x.x; v[1] = x.y;
+  }
+}
+
+// Main loop of a 64 x BNT output tile (BNT = 64 or 32) per 256-thread block;
+// thread (ty, tx) = (tid / 16, tid % 16) owns rows 4 ty .. 4 ty + 3 and
+// columns (BNT / 16) tx .. (BNT / 16) tx + BNT / 16 - 1.
+template <typename TA, typename TB, bool A_KMAJ, bool B_KMAJ, int BNT = BN>
 struct TileLoop {
-  // A thread stages 16 values per operand and step.  The 64 lanes of a wave
-  // run along the operand's contiguous index (k for a k-major operand, m
-  // otherwise), so each load instruction reads 64 consecutive values; the
-  // wave's other index steps by 4 from the wave number.  Loads use indices
-  // clamped into the operand and are issued unconditionally; the values
-  // outside it are replaced by 0 only when they are written to LDS, so
+  static constexpr int JN = BNT / 16;
+
+  // An operand of extent E (64 or 32) along m: each thread stages BK E / 256
+  // values per step.  The 64 lanes of a wave run along the operand's
+  // contiguous index (k for a k-major operand, m otherwise; an m-major
+  // operand must span 64), so each load instruction reads 64 consecutive
+  // values; the wave's other index steps by 4 from the wave number.  Loads
+  // use indices clamped into the operand and are issued unconditionally; the
+  // values outside it are replaced by 0 only when they are written to LDS, so
   // nothing uses a loaded value before the step that needs it.
-  template <bool KMAJ, typename T>
+  template <bool KMAJ, int E, typename T>
   static __device__ __forceinline__ void fetch(const T* __restrict__ P, int64_t ld, int64_t M, int64_t K,
-                                               int64_t m0, int64_t k0, float (&r)[kPer]) {
+                                               int64_t m0, int64_t k0, float (&r)[BK * E / 256]) {
+    static_assert(KMAJ || E == 64, "an m-major operand spans 64 lanes");
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t lim_fix = KMAJ ? K : M, lim_step = KMAJ ? M : K;
     const int64_t g_fix = (KMAJ ? k0 : m0) + lane;
     const int64_t c_fix = g_fix < lim_fix ? g_fix : lim_fix - 1;
 #pragma unroll
-    for (int q = 0; q < kPer; ++q) {
+    for (int q = 0; q < BK * E / 256; ++q) {
       const int64_t g_step = (KMAJ ? m0 : k0) + wave + 4 * q;
       const int64_t c_step = g_step < lim_step ? g_step : lim_step - 1;
       r[q] = Elem<T>::ld(P, c_step * ld + c_fix);
@@ -48,14 +71,14 @@ struct TileLoop {
 
   // LDS holds [k][m]: a k-major operand is transposed here.  (m0, k0) is the
   // step the values were fetched for.
-  template <bool KMAJ>
-  static __device__ __forceinline__ void stash(float (*S)[BM + kPad], const float (&r)[kPer], int64_t M, int64_t K,
-                                               int64_t m0, int64_t k0) {
+  template <bool KMAJ, int E>
+  static __device__ __forceinline__ void stash(float (*S)[E + kPad], const float (&r)[BK * E / 256], int64_t M,
+                                               int64_t K, int64_t m0, int64_t k0) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t lim_fix = KMAJ ? K : M, lim_step = KMAJ ? M : K;
     const bool fix_in = (KMAJ ? k0 : m0) + lane < lim_fix;
 #pragma unroll
-    for (int q = 0; q < kPer; ++q) {
+    for (int q = 0; q < BK * E / 256; ++q) {
       const bool in = fix_in && (KMAJ ? m0 : k0) + wave + 4 * q < lim_step;
       const float x = in ? r[q] : 0.0f;
       if (KMAJ)
@@ -65,57 +88,59 @@ struct TileLoop {
     }
   }
 
-  // Accumulate acc[4][4] for the tile at (m0, n0); rows m < M, cols n < N, k < K.
+  // Accumulate acc[4][JN] for the tile at (m0, n0); rows m < M, cols n < N, k < K.
   // M, N >= 1; K may be 0 (an empty vocabulary split), which leaves zeros.
   static __device__ __forceinline__ void run(const TA* __restrict__ A, int64_t lda, const TB* __restrict__ B,
                                              int64_t ldb, int64_t M, int64_t N, int64_t K, int64_t m0, int64_t n0,
-                                             float (&acc)[4][4]) {
+                                             float (&acc)[4][JN]) {
     __shared__ __align__(16) float As[BK][BM + kPad];
-    __shared__ __align__(16) float Bs[BK][BN + kPad];
+    __shared__ __align__(16) float Bs[BK][BNT + kPad];
     const int tid = threadIdx.x;
     const int tx = tid & 15, ty = tid >> 4;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
+      for (int j = 0; j < JN; ++j) acc[i][j] = 0.0f;
     if (K <= 0) return;
 
-    float ra[kPer], rb[kPer];
-    fetch<A_KMAJ>(A, lda, M, K, m0, 0, ra);
-    fetch<B_KMAJ>(B, ldb, N, K, n0, 0, rb);
+    float ra[BK * BM / 256], rb[BK * BNT / 256];
+    fetch<A_KMAJ, BM>(A, lda, M, K, m0, 0, ra);
+    fetch<B_KMAJ, BNT>(B, ldb, N, K, n0, 0, rb);
     for (int64_t k0 = 0; k0 < K; k0 += BK) {
       __syncthreads();  // the previous step's fragment reads are done
-      stash<A_KMAJ>(As, ra, M, K, m0, k0);
-      stash<B_KMAJ>(Bs, rb, N, K, n0, k0);
+      stash<A_KMAJ, BM>(As, ra, M, K, m0, k0);
+      stash<B_KMAJ, BNT>(Bs, rb, N, K, n0, k0);
       __syncthreads();
       // the next step's loads (clamped, so in bounds past the end too) fly
       // under this step's FMAs
-      fetch<A_KMAJ>(A, lda, M, K, m0, k0 + BK, ra);
-      fetch<B_KMAJ>(B, ldb, N, K, n0, k0 + BK, rb);
+      fetch<A_KMAJ, BM>(A, lda, M, K, m0, k0 + BK, ra);
+      fetch<B_KMAJ, BNT>(B, ldb, N, K, n0, k0 + BK, rb);
       // fragment reads one k ahead of the FMAs that use them
-      float4 a = *reinterpret_cast<const float4*>(&As[0][ty * 4]);
-      float4 b = *reinterpret_cast<const float4*>(&Bs[0][tx * 4]);
+      float av[4], bv[JN];
+      read_row<4>(&As[0][ty * 4], av);
+      read_row<JN>(&Bs[0][tx * JN], bv);
 #pragma unroll 8
       for (int kk = 0; kk < BK; ++kk) {
         const int kn = kk + 1 < BK ? kk + 1 : kk;
-        const float4 an = *reinterpret_cast<const float4*>(&As[kn][ty * 4]);
-        const float4 bn = *reinterpret_cast<const float4*>(&Bs[kn][tx * 4]);
+        float an[4], bn[JN];
+        read_row<4>(&As[kn][ty * 4], an);
+        read_row<JN>(&Bs[kn][tx * JN], bn);
         __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of this k's FMAs
-        const float av[4] = {a.x, a.y, a.z, a.w};
-        const float bv[4] = {b.x, b.y, b.z, b.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
-        a = an;
-        b = bn;
+          for (int j = 0; j < JN; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) av[i] = an[i];
+#pragma unroll
+        for (int j = 0; j < JN; ++j) bv[j] = bn[j];
       }
     }
   }
 };
 
 // Logits tile (rows = chunk tokens, cols = vocabulary): per-row max and
-// sum-exp over the tile's 64 columns (one vocabulary group), the target
+// sum-exp over the tile's kLogitsBN columns (one vocabulary group), the target
 // logit, and optionally exp(z - group max) into the chunk's buffer.
 // Recompute mode (lse_in != nullptr, the backward from the saved LSE): the
 // buffer gets G = (exp(z - lse) - [j = y]) * scale directly, scale = upstream
@@ -130,9 +155,10 @@ __global__ __launch_bounds__(256) void fma_logits_kernel(const T* __restrict__ H
                                                          const int32_t* __restrict__ nvalid, int32_t reduction,
                                                          int64_t ignore_index) {
   const int64_t m0 = static_cast<int64_t>(blockIdx.x) * BM;
-  const int64_t n0 = static_cast<int64_t>(blockIdx.y) * BN;
-  float acc[4][4];
-  TileLoop<T, T, true, true>::run(H, d, W, d, rows, v, d, m0, n0, acc);
+  const int64_t n0 = static_cast<int64_t>(blockIdx.y) * kLogitsBN;
+  constexpr int JN = kLogitsBN / 16;  // columns per thread
+  float acc[4][JN];
+  TileLoop<T, T, true, true, kLogitsBN>::run(H, d, W, d, rows, v, d, m0, n0, acc);
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
   const int64_t g = blockIdx.y;
   if (lse_in != nullptr) {
@@ -147,8 +173,8 @@ __global__ __launch_bounds__(256) void fma_logits_kernel(const T* __restrict__ H
       const float sc = y != ignore_index ? go * red : 0.0f;
       const float l = lse_in[t];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t n = n0 + tx * 4 + j;
+      for (int j = 0; j < JN; ++j) {
+        const int64_t n = n0 + tx * JN + j;
         if (n >= vp) continue;
         const float gv = n < v ? (expf(acc[i][j] - l) - (n == y ? 1.0f : 0.0f)) * sc : 0.0f;
         prob[t * vp + n] = gv;
@@ -161,13 +187,13 @@ __global__ __launch_bounds__(256) void fma_logits_kernel(const T* __restrict__ H
     const int64_t t = m0 + ty * 4 + i;
     float mx = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (n0 + tx * 4 + j < v) mx = fmaxf(mx, acc[i][j]);
+    for (int j = 0; j < JN; ++j)
+      if (n0 + tx * JN + j < v) mx = fmaxf(mx, acc[i][j]);
     for (int off = 8; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-    float e[4], s = 0.0f;
+    float e[JN], s = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      e[j] = (n0 + tx * 4 + j < v) ? fast_exp(acc[i][j] - mx) : 0.0f;
+    for (int j = 0; j < JN; ++j) {
+      e[j] = (n0 + tx * JN + j < v) ? fast_exp(acc[i][j] - mx) : 0.0f;
       s += e[j];
     }
     for (int off = 8; off > 0; off >>= 1) s += __shfl_xor(s, off);
@@ -178,8 +204,8 @@ __global__ __launch_bounds__(256) void fma_logits_kernel(const T* __restrict__ H
       }
       const int64_t y = labels[t];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t n = n0 + tx * 4 + j;
+      for (int j = 0; j < JN; ++j) {
+        const int64_t n = n0 + tx * JN + j;
         if (n == y && n < v) zy[t] = acc[i][j];
         if (prob != nullptr && n < vp) prob[t * vp + n] = e[j];
       }
@@ -251,7 +277,8 @@ hipError_t fma_logits(const Plan& p, const Work& w, const ChunkArgs& a, int mode
   const float* lse_in = mode == LOGITS_GRAD_FROM_LSE ? a.lse_in : nullptr;
   // the grid spans the buffer's padded columns so that recompute mode clears them
   const int64_t cols = mode == LOGITS_GRAD_FROM_LSE ? p.vp : p.v;
-  fma_logits_kernel<float><<<grid2(a.rows, cols), 256, 0, s>>>(
+  const dim3 grid(static_cast<unsigned>((a.rows + BM - 1) / BM), static_cast<unsigned>((cols + kLogitsBN - 1) / kLogitsBN));
+  fma_logits_kernel<float><<<grid, 256, 0, s>>>(
       static_cast<const float*>(a.h), static_cast<const float*>(a.w), a.rows, p.d, p.v, p.vp, a.labels, w.zy, w.pm,
       w.ps, p.chunk, prob, lse_in, a.grad_out, w.nvalid, a.reduction, a.ignore_index);
   return hipGetLastError();

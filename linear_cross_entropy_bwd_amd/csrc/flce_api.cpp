@@ -74,7 +74,7 @@ int make_plan(int64_t n, int64_t d, int64_t v, int32_t dtype, int32_t with_bwd, 
   q.dtype = dtype;
   q.with_bwd = with_bwd ? 1 : 0;
   q.engine = dtype == FLCE_BF16 ? ENGINE_MFMA : ENGINE_FMA;
-  q.group = q.engine == ENGINE_MFMA ? 128 : 64;
+  q.group = q.engine == ENGINE_MFMA ? 128 : 32;  // each engine's logits tile width along the vocabulary
   const int64_t prob_elem = q.engine == ENGINE_MFMA ? 2 : 4;
   q.vp = (v + kVocabPad - 1) / kVocabPad * kVocabPad;
   q.ngroups = (v + q.group - 1) / q.group;
