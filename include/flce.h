@@ -57,10 +57,12 @@
  * Environment overrides (read at every call and by flce_plan_info and
  * flce_workspace_bytes; meant for tests and tuning, positive integers only,
  * anything else is ignored): FLCE_CHUNK_ROWS (token rows per chunk, capped at
- * n), FLCE_WORKSPACE_CAP_BYTES (budget for the chunk's probability buffer,
- * default 1 GiB), FLCE_DH_SPLITS (split of dH's vocabulary reduction),
- * FLCE_GROUP_LOGITS, FLCE_GROUP_DH, FLCE_GROUP_DW (tile-order group sizes of
- * the three contractions on the bf16 engine).  Results stay within the
+ * n), FLCE_WORKSPACE_CAP_BYTES (budget for one chunk's probability buffer,
+ * default 1 GiB; plans of four or more bf16 chunks with gradients hold two),
+ * FLCE_DW_PAIR_CHUNKS (fewest chunks that pair, default 4), FLCE_DH_SPLITS
+ * (split of dH's vocabulary reduction), FLCE_GROUP_LOGITS,
+ * FLCE_GROUP_DH, FLCE_GROUP_DW (tile-order group sizes of the three
+ * contractions on the bf16 engine).  Results stay within the
  * stated tolerances under any of them; bitwise results can change.
  */
 #ifndef FLCE_H_
@@ -300,7 +302,8 @@ typedef struct {
   int32_t engine;          /* 0: bf16 matrix-core engine, 1: fp32 FMA engine */
   int32_t dw_accumulator;  /* 1 if dW keeps a bf16 low half of its running sum in the workspace */
   size_t workspace_bytes;
-  size_t prob_buffer_bytes;   /* the chunk's [chunk_rows, vocab_pitch] buffer */
+  size_t prob_buffer_bytes;   /* the chunks' [chunk_rows, vocab_pitch] buffer(s) */
+  int32_t dw_pairs;        /* 1 if two chunk buffers sit side by side and each dW launch covers two chunks */
 } flce_plan_t;
 
 /* Fill *out with the plan for these sizes; returns 0 or FLCE_ERR_INVALID_ARG. */

@@ -60,6 +60,7 @@ class PlanInfo(ctypes.Structure):
         ("dw_accumulator", ctypes.c_int32),
         ("workspace_bytes", ctypes.c_size_t),
         ("prob_buffer_bytes", ctypes.c_size_t),
+        ("dw_pairs", ctypes.c_int32),
     ]
 
     def as_dict(self):

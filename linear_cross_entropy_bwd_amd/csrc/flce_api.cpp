@@ -58,7 +58,7 @@ static int64_t best_splits(int64_t tiles, int64_t slots, int64_t smax) {
 // multiple of 256 rows once that many fit), never more than half of the rows
 // (rounded up to 16) so that the buffer stays well below the [n, v] logits it
 // replaces, and at least 16.
-int make_plan(int64_t n, int64_t d, int64_t v, int32_t dtype, int32_t with_bwd, Plan* p) {
+int make_plan(int64_t n, int64_t d, int64_t v, int32_t dtype, int32_t with_bwd, Plan* p, int allow_pair) {
   if (p == nullptr || n <= 0 || d <= 0 || v <= 0) return FLCE_ERR_INVALID_ARG;
   if (dtype != FLCE_BF16 && dtype != FLCE_F32) return FLCE_ERR_INVALID_ARG;
   if (!mul_ok(n, d) || !mul_ok(v, d) || v > (int64_t(1) << 40) || n > (int64_t(1) << 40))
@@ -108,6 +108,10 @@ int make_plan(int64_t n, int64_t d, int64_t v, int32_t dtype, int32_t with_bwd, 
     q.dh_splits = s < 1 ? 1 : s;
   }
   q.dw_acc = (with_bwd && dtype == FLCE_BF16 && q.nchunks > 1) ? 1 : 0;
+  // Runs of four or more chunks keep two chunk buffers side by side, so that
+  // one dW launch reduces over 2 C tokens: half the launches and half the
+  // passes over the running sum, for one more chunk buffer.
+  q.dw_pair = (allow_pair && q.dw_acc && q.nchunks >= env_i64("FLCE_DW_PAIR_CHUNKS", 4)) ? 1 : 0;
   // Tile orders (see tile_coords): consecutive tiles share operand tiles in L2.
   q.group_m[0] = env_i64("FLCE_GROUP_LOGITS", 8);
   q.group_m[1] = env_i64("FLCE_GROUP_DH", 8);
@@ -127,7 +131,7 @@ int make_plan(int64_t n, int64_t d, int64_t v, int32_t dtype, int32_t with_bwd, 
   q.off_loss = take(sizeof(float) * n);
   q.off_pm = take(sizeof(float) * q.ngroups * q.chunk);
   q.off_ps = take(sizeof(float) * q.ngroups * q.chunk);
-  q.prob_bytes = with_bwd ? static_cast<size_t>(q.chunk * q.vp * prob_elem) : 0;
+  q.prob_bytes = with_bwd ? static_cast<size_t>(q.chunk * q.vp * prob_elem) * (q.dw_pair ? 2 : 1) : 0;
   q.off_prob = take(q.prob_bytes);
   q.off_dwacc = take(q.dw_acc ? sizeof(uint16_t) * static_cast<size_t>(v * d) : 0);
   q.off_dhpart = take(with_bwd && q.dh_splits > 1 ? sizeof(float) * q.dh_splits * q.chunk * d : 0);
@@ -234,6 +238,38 @@ Work carve(const Plan& p, char* base) {
   return w;
 }
 
+// The workspace as chunk c sees it: with paired chunk buffers, odd chunks use
+// the second buffer, which follows the first, so that a pair's gradient rows
+// are one contiguous [2 C, vp] array.
+Work chunk_work(const Plan& p, const Work& wk, int64_t c) {
+  Work wc = wk;
+  if (p.dw_pair && (c & 1)) {
+    const size_t elem = p.engine == ENGINE_MFMA ? 2 : 4;
+    wc.prob = static_cast<char*>(wk.prob) + static_cast<size_t>(p.chunk * p.vp) * elem;
+  }
+  return wc;
+}
+
+// dW after chunk c.  Unpaired: this chunk's contribution, first/middle/last by
+// position.  Paired: after each odd chunk (and after an even last chunk), one
+// launch over the group's rows, which start at the first buffer; the groups
+// take the first/middle/last roles, and a plan pairs only from four chunks on,
+// so there are always at least two groups.
+hipError_t run_dw(const Plan& p, const Work& wk, const ChunkArgs& a, int64_t c, const char* h, int64_t elem,
+                  hipStream_t s) {
+  if (!p.dw_pair)
+    return timed(K_DW, s, [&] { return p.engine == ENGINE_MFMA ? mfma_dw(p, wk, a, s) : fma_dw(p, wk, a, s); });
+  if (!(c & 1) && c != p.nchunks - 1) return hipSuccess;  // the pair's first chunk: wait for its partner
+  const int64_t first = c & ~int64_t(1);
+  const int64_t group = first / 2, groups = (p.nchunks + 1) / 2;
+  ChunkArgs ad = a;
+  ad.row0 = first * p.chunk;
+  ad.rows = a.row0 + a.rows - ad.row0;
+  ad.h = h + ad.row0 * p.d * elem;
+  ad.dw_mode = group == 0 ? DW_FIRST : (group == groups - 1 ? DW_LAST : DW_MID);
+  return timed(K_DW, s, [&] { return mfma_dw(p, wk, ad, s); });
+}
+
 // The kernel sequence of one call; workspace already allocated.
 // zy_out (optional): the per-row target logit (0 for ignored rows and for
 // labels outside [0, v)); loss_out may be null when zy_out is given.
@@ -248,6 +284,7 @@ hipError_t run(const Plan& p, const Work& wk, const void* h, const void* w, cons
   if (e != hipSuccess) return e;
   float* lse_base = lse_out != nullptr ? lse_out : wk.lse;
   for (int64_t c = 0; c < p.nchunks; ++c) {
+    const Work wc = chunk_work(p, wk, c);
     ChunkArgs a;
     a.row0 = c * p.chunk;
     a.rows = p.n - a.row0 < p.chunk ? p.n - a.row0 : p.chunk;
@@ -270,21 +307,21 @@ hipError_t run(const Plan& p, const Work& wk, const void* h, const void* w, cons
 
     const int mode = p.with_bwd ? LOGITS_PROB : LOGITS_STATS;
     e = timed(K_LOGITS, s, [&] {
-      return p.engine == ENGINE_MFMA ? mfma_logits(p, wk, a, mode, s) : fma_logits(p, wk, a, mode, s);
+      return p.engine == ENGINE_MFMA ? mfma_logits(p, wc, a, mode, s) : fma_logits(p, wc, a, mode, s);
     });
     if (e != hipSuccess) return e;
-    e = timed(K_LSE_MERGE, s, [&] { return launch_lse_merge(p, wk, a, p.with_bwd, s); });
+    e = timed(K_LSE_MERGE, s, [&] { return launch_lse_merge(p, wc, a, p.with_bwd, s); });
     if (e != hipSuccess) return e;
     if (!p.with_bwd) continue;
-    e = timed(K_GRAD, s, [&] { return launch_grad(p, wk, a, s); });
+    e = timed(K_GRAD, s, [&] { return launch_grad(p, wc, a, s); });
     if (e != hipSuccess) return e;
-    e = timed(K_DH, s, [&] { return p.engine == ENGINE_MFMA ? mfma_dh(p, wk, a, s) : fma_dh(p, wk, a, s); });
+    e = timed(K_DH, s, [&] { return p.engine == ENGINE_MFMA ? mfma_dh(p, wc, a, s) : fma_dh(p, wc, a, s); });
     if (e != hipSuccess) return e;
     if (p.dh_splits > 1) {
-      e = timed(K_DH_REDUCE, s, [&] { return launch_dh_reduce(p, wk, a, s); });
+      e = timed(K_DH_REDUCE, s, [&] { return launch_dh_reduce(p, wc, a, s); });
       if (e != hipSuccess) return e;
     }
-    e = timed(K_DW, s, [&] { return p.engine == ENGINE_MFMA ? mfma_dw(p, wk, a, s) : fma_dw(p, wk, a, s); });
+    e = run_dw(p, wk, a, c, static_cast<const char*>(h), elem, s);
     if (e != hipSuccess) return e;
   }
   if (loss_out == nullptr) return hipSuccess;
@@ -302,6 +339,7 @@ hipError_t run_bwd(const Plan& p, const Work& wk, const void* h, const void* w, 
   hipError_t e = timed(K_LABEL_SCAN, s, [&] { return launch_label_scan(p, wk, labels, ignore_index, s); });
   if (e != hipSuccess) return e;
   for (int64_t c = 0; c < p.nchunks; ++c) {
+    const Work wc = chunk_work(p, wk, c);
     ChunkArgs a;
     a.row0 = c * p.chunk;
     a.rows = p.n - a.row0 < p.chunk ? p.n - a.row0 : p.chunk;
@@ -322,17 +360,17 @@ hipError_t run_bwd(const Plan& p, const Work& wk, const void* h, const void* w, 
     a.h_scale = nullptr;
     a.w_scale = nullptr;
     e = timed(K_LOGITS, s, [&] {
-      return p.engine == ENGINE_MFMA ? mfma_logits(p, wk, a, LOGITS_GRAD_FROM_LSE, s)
-                                     : fma_logits(p, wk, a, LOGITS_GRAD_FROM_LSE, s);
+      return p.engine == ENGINE_MFMA ? mfma_logits(p, wc, a, LOGITS_GRAD_FROM_LSE, s)
+                                     : fma_logits(p, wc, a, LOGITS_GRAD_FROM_LSE, s);
     });
     if (e != hipSuccess) return e;
-    e = timed(K_DH, s, [&] { return p.engine == ENGINE_MFMA ? mfma_dh(p, wk, a, s) : fma_dh(p, wk, a, s); });
+    e = timed(K_DH, s, [&] { return p.engine == ENGINE_MFMA ? mfma_dh(p, wc, a, s) : fma_dh(p, wc, a, s); });
     if (e != hipSuccess) return e;
     if (p.dh_splits > 1) {
-      e = timed(K_DH_REDUCE, s, [&] { return launch_dh_reduce(p, wk, a, s); });
+      e = timed(K_DH_REDUCE, s, [&] { return launch_dh_reduce(p, wc, a, s); });
       if (e != hipSuccess) return e;
     }
-    e = timed(K_DW, s, [&] { return p.engine == ENGINE_MFMA ? mfma_dw(p, wk, a, s) : fma_dw(p, wk, a, s); });
+    e = run_dw(p, wk, a, c, static_cast<const char*>(h), elem, s);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
@@ -487,7 +525,7 @@ int call_bwd_fp8(const void* h_q, const float* h_scale, const void* w_q, const f
       (grad_out != nullptr && !aligned(grad_out, 4)))
     return FLCE_ERR_ALIGNMENT;
   Plan p, p8;
-  int st = make_plan(n, d, v, FLCE_BF16, 1, &p);
+  int st = make_plan(n, d, v, FLCE_BF16, 1, &p, /*allow_pair=*/0);
   if (st != FLCE_OK) return st;
   st = make_plan(n, d / 2, v, FLCE_BF16, 0, &p8);
   if (st != FLCE_OK) return st;
@@ -743,6 +781,7 @@ int flce_plan_info(int64_t n, int64_t d, int64_t v, flce_dtype dtype, int with_b
   out->dw_accumulator = p.dw_acc;
   out->workspace_bytes = p.total;
   out->prob_buffer_bytes = p.prob_bytes;
+  out->dw_pairs = p.dw_pair;
   return FLCE_OK;
 }
 

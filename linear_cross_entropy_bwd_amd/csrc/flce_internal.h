@@ -33,6 +33,7 @@ struct Plan {
   int64_t ngroups;
   int64_t dh_splits;   // split of the K = vocabulary reduction of dH
   int32_t dw_acc;      // dW's running sum needs a workspace low half (bf16 path, several chunks)
+  int32_t dw_pair;     // two chunk buffers; each dW launch reduces over a pair of consecutive chunks
   int64_t group_m[3];  // tile-row group of the logits, dH and dW tile orders
   // byte offsets inside the single workspace allocation
   size_t off_nvalid, off_zy, off_gy, off_lse, off_loss, off_pm, off_ps, off_prob, off_dwacc, off_dhpart;
@@ -40,7 +41,8 @@ struct Plan {
   size_t prob_bytes;
 };
 
-int make_plan(int64_t n, int64_t d, int64_t v, int32_t dtype, int32_t with_bwd, Plan* p);
+// allow_pair = 0 keeps one chunk buffer (for loops that run dW chunk by chunk).
+int make_plan(int64_t n, int64_t d, int64_t v, int32_t dtype, int32_t with_bwd, Plan* p, int allow_pair = 1);
 
 // Pointers into the workspace for one call.
 struct Work {

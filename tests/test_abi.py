@@ -52,8 +52,10 @@ def test_plan_invariants(dtype, shape):
     assert p["vocab_pitch"] >= v and p["vocab_pitch"] % 256 == 0
     assert p["workspace_bytes"] == flce.flce_workspace_bytes(n, d, v, dtype, 1)
     assert p["workspace_bytes"] >= p["prob_buffer_bytes"]
+    # two chunk buffers (one dW launch per chunk pair) exactly when a bf16 plan has four or more chunks
+    assert p["dw_pairs"] == int(dtype == flce.FLCE_BF16 and p["num_chunks"] >= 4)
     fwd = flce.flce_plan_info(n, d, v, dtype, 0)
-    assert fwd["prob_buffer_bytes"] == 0
+    assert fwd["prob_buffer_bytes"] == 0 and fwd["dw_pairs"] == 0
     assert fwd["workspace_bytes"] <= p["workspace_bytes"]
 
 
@@ -63,7 +65,8 @@ def test_plan_env_overrides(monkeypatch):
     monkeypatch.delenv("FLCE_CHUNK_ROWS")
     monkeypatch.setenv("FLCE_WORKSPACE_CAP_BYTES", str(64 * 1024 * 1024))
     p = flce.flce_plan_info(8192, 4096, 128256, flce.FLCE_BF16, 1)
-    assert p["prob_buffer_bytes"] <= 64 * 1024 * 1024
+    assert p["chunk_rows"] * p["vocab_pitch"] * 2 <= 64 * 1024 * 1024     # the cap bounds one chunk's buffer
+    assert p["dw_pairs"] == 1 and p["prob_buffer_bytes"] == 2 * p["chunk_rows"] * p["vocab_pitch"] * 2
 
 
 def test_invalid_sizes():

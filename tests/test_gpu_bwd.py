@@ -60,11 +60,14 @@ def test_bwd_from_oracle_lse(shape, dtype, reduction):
     _check_grads(to_f64(dh), to_f64(dw), rdh, rdw, wl.torch_dtype, "bwd")
 
 
-@pytest.mark.parametrize("chunk", ["64", "512"])
-def test_bwd_chunk_modes_bf16(monkeypatch, chunk):
-    """Interior 256x256 tiles with first/middle/last and single-chunk dW accumulation."""
+@pytest.mark.parametrize("chunk,chunks,paired", [("128", 3, 0), ("80", 4, 1), ("64", 5, 1), ("512", 1, 0)])
+def test_bwd_chunk_modes_bf16(monkeypatch, chunk, chunks, paired):
+    """Interior 256x256 tiles with first/middle/last and single-chunk dW accumulation,
+    chunk by chunk and over chunk pairs."""
     wl, (h, w, y) = _case(300, 256, 1500, "bf16", seed=33)
     monkeypatch.setenv("FLCE_CHUNK_ROWS", chunk)
+    p = flce.flce_plan_info(300, 256, 1500, flce.FLCE_BF16, 1)
+    assert (p["num_chunks"], p["dw_pairs"]) == (chunks, paired)
     _, lse64 = flce_forward(h, w, y)
     lse32 = torch.from_numpy(lse64.astype(np.float32))
     rdh, rdw = flce_backward_from_lse(h, w, y, lse32.double().numpy())

@@ -134,14 +134,20 @@ def test_chunk_size_invariance(monkeypatch, chunk):
     check(run_lib(h, w, y), ref, torch.float32, f"chunk {chunk}")
 
 
-@pytest.mark.parametrize("chunk", ["64", "512"])
+# chunk rows -> (chunks, paired): 128 rows give an unpaired first, middle and last
+# chunk; 80 rows two pairs, the second ragged; 64 rows a first pair, a middle pair
+# and a lone ragged last chunk; 512 rows a single chunk.
+CHUNK_MODES = {"128": (3, 0), "80": (4, 1), "64": (5, 1), "512": (1, 0)}
+
+
+@pytest.mark.parametrize("chunk", list(CHUNK_MODES))
 def test_chunk_modes_bf16(monkeypatch, chunk):
-    """The matrix engine's dW accumulation modes on interior 256x256 tiles: 64-row
-    chunks give a first, three middle and a last chunk; 512 rows a single chunk."""
+    """The matrix engine's dW accumulation modes on interior 256x256 tiles, chunk by
+    chunk and over chunk pairs (one launch reducing over two chunks' rows)."""
     wl, inp = _case(300, 256, 1500, "bf16", sigma_w=0.1, seed=25)
     monkeypatch.setenv("FLCE_CHUNK_ROWS", chunk)
     p = flce.flce_plan_info(300, 256, 1500, flce.FLCE_BF16, 1)
-    assert p["num_chunks"] == (5 if chunk == "64" else 1)
+    assert (p["num_chunks"], p["dw_pairs"]) == CHUNK_MODES[chunk]
     _parity(wl, inp, f"bf16 chunk {chunk}")
 
 
