@@ -1,7 +1,8 @@
 // fp32 engine: LDS-tiled FMA contractions for FLCE_F32 inputs.
 //
-// One 64x64 output tile per 256-thread block, 4x4 outputs per thread, K in
-// steps of 64 staged through LDS in [k][m] order.  The next step's operand
+// One output tile per 256-thread block: 64x64 (4x4 outputs per thread) for dH
+// and dW, 64x32 (4x2) for the logits; K in steps of 64 staged through LDS in
+// [k][m] order.  The next step's operand
 // values are loaded into registers before the current step's FMAs, so their
 // latency hides under the arithmetic.  Operands are described by (pointer,
 // leading dimension, k-major flag): a k-major operand has its reduction index
