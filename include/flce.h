@@ -31,8 +31,11 @@
  * Arithmetic: products accumulate in fp32 (bf16 inputs feed bf16 matrix
  * instructions with fp32 accumulation); loss and lse are fp32; dh_out and
  * dw_out are rounded to `dtype` with round-to-nearest-even.  The full [n, v]
- * logits tensor is never allocated: token rows are processed in chunks of
- * fewer than n rows (for n >= 32), see flce_plan_info().
+ * logits tensor is never allocated: calls that compute gradients process
+ * token rows in chunks of fewer than n rows (for n >= 32); forward-only calls
+ * keep no logits at all, only per-row partials of each vocabulary group, and
+ * take as many rows per chunk as those fit the workspace budget.  See
+ * flce_plan_info().
  *
  * Ownership: the caller owns every argument buffer; inputs are only read,
  * outputs are overwritten (never accumulated into) and must not alias the

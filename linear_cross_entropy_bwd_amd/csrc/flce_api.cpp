@@ -85,6 +85,15 @@ int make_plan(int64_t n, int64_t d, int64_t v, int32_t dtype, int32_t with_bwd, 
   if (c_budget < 16) c_budget = 16;
   const int64_t half = ((n + 1) / 2 + 15) / 16 * 16;
   int64_t c = c_budget < half ? c_budget : half;
+  if (!with_bwd) {
+    // No probability buffer: a forward-only chunk holds just its rows' group
+    // partials (8 bytes per row and group), so it spans every row that fits
+    // the same budget, and one launch covers the tokens of several chunks.
+    int64_t c_fwd = budget / (q.ngroups * 8);
+    c_fwd = c_fwd >= 256 ? c_fwd / 256 * 256 : (c_fwd / 16) * 16;
+    if (c_fwd < 16) c_fwd = 16;
+    c = c_fwd < n ? c_fwd : n;
+  }
   c = env_i64("FLCE_CHUNK_ROWS", c);
   if (c > n) c = n;
   q.chunk = c;
@@ -525,9 +534,10 @@ int call_bwd_fp8(const void* h_q, const float* h_scale, const void* w_q, const f
       (grad_out != nullptr && !aligned(grad_out, 4)))
     return FLCE_ERR_ALIGNMENT;
   Plan p, p8;
+  // both plans as for a backward (chunked, unpaired), so that their chunks match
   int st = make_plan(n, d, v, FLCE_BF16, 1, &p, /*allow_pair=*/0);
   if (st != FLCE_OK) return st;
-  st = make_plan(n, d / 2, v, FLCE_BF16, 0, &p8);
+  st = make_plan(n, d / 2, v, FLCE_BF16, 1, &p8, /*allow_pair=*/0);
   if (st != FLCE_OK) return st;
   if (p8.chunk != p.chunk || p8.vp != p.vp || !mul_ok(v, d)) return FLCE_ERR_INVALID_ARG;
   const size_t off_w16 = p.total;
