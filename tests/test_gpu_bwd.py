@@ -143,3 +143,33 @@ def test_bwd_llama3_8b_head_full_size():
     say(f"  sampled dH rel {e_dh:.2e}, dW rel {e_dw:.2e}")
     tol = TOL[torch.bfloat16]["grad"]
     assert e_dh <= tol and e_dw <= tol
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("path,chunk,chunks", [("fused", "1280", 7), ("split", "1152", 8)])
+def test_paired_chunks_at_scale(monkeypatch, path, chunk, chunks):
+    """Chunk pairs over many interior tiles (n = 8192, d = 1024, v = 32000, bf16):
+    the fused call with seven chunks (three pairs and a lone last chunk) against the
+    full oracle, and the backward from the oracle's LSE with eight chunks (the last
+    pair ragged) against the oracle's backward from that LSE."""
+    from oracle import flce_forward_backward
+    from workloads import Workload
+    wl = Workload(f"paired_{path}", 8192, 1024, 32000, "bf16", 0.05, "uniform", 0.05, "mean", seed=95)
+    h, w, y = make_inputs(wl, threads=8)
+    monkeypatch.setenv("FLCE_CHUNK_ROWS", chunk)
+    p = flce.flce_plan_info(wl.n, wl.d, wl.v, flce.FLCE_BF16, 1)
+    assert (p["num_chunks"], p["dw_pairs"]) == (chunks, 1)
+    say(f"[bwd] chunk pairs at scale, {path}: {chunks} chunks of {chunk} rows")
+    if path == "fused":
+        rl, rlse, rdh, rdw = flce_forward_backward(h, w, y)
+        loss, lse, dh, dw = flce.linear_cross_entropy(h.to(DEV), w.to(DEV), y.to(DEV))
+        torch.cuda.synchronize()
+        assert abs(float(loss.item()) - rl) <= TOL[torch.bfloat16]["loss"] * abs(rl)
+    else:
+        _, lse64 = flce_forward(h, w, y)
+        lse32 = lse64.astype(np.float32)
+        rdh, rdw = flce_backward_from_lse(h, w, y, lse32.astype(np.float64), grad_out=0.5)
+        go = torch.tensor([0.5], dtype=torch.float32, device=DEV)
+        dh, dw = flce.linear_cross_entropy_backward(h.to(DEV), w.to(DEV), y.to(DEV), torch.from_numpy(lse32).to(DEV), go)
+        torch.cuda.synchronize()
+    _check_grads(to_f64(dh), to_f64(dw), rdh, rdw, torch.bfloat16, f"paired {path}")
