@@ -618,7 +618,9 @@ __device__ __forceinline__ void logits_grad_epilogue(const LogitsArgs& a, Acc& a
   });
 }
 
-template <bool RECOMP, bool FP8 = false>
+// STORE_P: the epilogue also writes P = exp(z - group max) into the chunk buffer
+// (a compile-time choice, so that the statistics loop carries no branch).
+template <bool RECOMP, bool FP8 = false, bool STORE_P = false>
 __global__ __launch_bounds__(kThreads) void mfma_logits_kernel(LogitsArgs a) {
   const int64_t nb = a.tiles_m * a.tiles_n;
   const int64_t t = xcd_remap(blockIdx.x, nb);
@@ -694,6 +696,10 @@ __global__ __launch_bounds__(kThreads) void mfma_logits_kernel(LogitsArgs a) {
       const int64_t tok = n0 + wn * 128 + J * 32 + (lane & 31);
       const bool live = tok < a.rows;
       char* stage = reinterpret_cast<char*>(ring()[J]) + kWaveScratchBytes * wave;
+      // staging row t = token: 16-byte chunk c of the group lands at position c ^ (t % 16)
+      const int t = lane & 31;
+      char* srow = stage + t * 256 + 8 * half;
+      const int sx = t & 15;
       float mx = -INFINITY;
       static_for<4>([&](auto I) {
         static_for<16>([&](auto R) {
@@ -711,25 +717,22 @@ __global__ __launch_bounds__(kThreads) void mfma_logits_kernel(LogitsArgs a) {
             e[U] = in_vocab(acc_row(I, r, lane)) ? __builtin_amdgcn_exp2f(fmaf(acc.c[I][J][r], kLog2e, -mxl)) : 0.0f;
             s += e[U];
           });
-          if (a.prob != nullptr) {
-            // staging row t = token, 16-byte chunk I*4+Q (XOR-swizzled by the row)
-            const int t = lane & 31;
-            const int chunk = (I * 4 + Q) ^ (t & 15);
+          if constexpr (STORE_P) {
             uint2 pk;
             pk.x = pack_bf16x2(e[0], e[1]);
             pk.y = pack_bf16x2(e[2], e[3]);
-            *reinterpret_cast<uint2*>(stage + t * 256 + chunk * 16 + 8 * half) = pk;
+            *reinterpret_cast<uint2*>(srow + ((I * 4 + Q) ^ sx) * 16) = pk;
           }
         });
       });
-      if (a.prob != nullptr) {
+      if constexpr (STORE_P) {
         // The wave's 32 tokens x 128 vocabulary entries of P, 256 bytes per
         // token, go out as four whole token rows per store.
         __builtin_amdgcn_wave_barrier();
         static_for<8>([&](auto Rr) {
-          const int t = 4 * Rr + (lane >> 4), c = lane & 15;
-          const uint4 v = *reinterpret_cast<const uint4*>(stage + t * 256 + ((c ^ (t & 15)) * 16));
-          const int64_t tk = n0 + wn * 128 + J * 32 + t;
+          const int tr = 4 * Rr + (lane >> 4), c = lane & 15;
+          const uint4 v = *reinterpret_cast<const uint4*>(stage + tr * 256 + ((c ^ (tr & 15)) * 16));
+          const int64_t tk = n0 + wn * 128 + J * 32 + tr;
           if (tk < a.rows) *reinterpret_cast<uint4*>(a.prob + tk * a.vp + vbase + 8 * c) = v;
         });
       }
@@ -1055,8 +1058,10 @@ hipError_t mfma_logits(const Plan& p, const Work& w, const ChunkArgs& c, int mod
       mfma_logits_kernel<false, true><<<grid, kThreads, 0, s>>>(a);
   } else if (mode == LOGITS_GRAD_FROM_LSE) {
     mfma_logits_kernel<true><<<grid, kThreads, 0, s>>>(a);
+  } else if (mode == LOGITS_PROB) {
+    mfma_logits_kernel<false, false, true><<<grid, kThreads, 0, s>>>(a);
   } else {
-    mfma_logits_kernel<false><<<grid, kThreads, 0, s>>>(a);
+    mfma_logits_kernel<false, false, false><<<grid, kThreads, 0, s>>>(a);
   }
   return hipGetLastError();
 }
