@@ -62,6 +62,7 @@
  * anything else is ignored): FLCE_CHUNK_ROWS (token rows per chunk, capped at
  * n), FLCE_WORKSPACE_CAP_BYTES (budget for one chunk's probability buffer,
  * default 1 GiB; plans of four or more bf16 chunks with gradients hold two),
+ * FLCE_LOWMEM_BUFFER_BYTES (flce_fwd_bwd_lowmem's slice budget, default 256 MiB),
  * FLCE_DW_PAIR_CHUNKS (fewest chunks that pair, default 4), FLCE_DH_SPLITS
  * (split of dH's vocabulary reduction), FLCE_GROUP_LOGITS,
  * FLCE_GROUP_DH, FLCE_GROUP_DW (tile-order group sizes of the three
@@ -121,14 +122,35 @@ int flce_fwd_bwd(const void* h, const void* w, const int64_t* labels,
 
 /*
  * Forward only: loss and (optionally) the per-row LSE, the two quantities the
- * forward keeps ("only the final scalar loss and running normalizers are
- * stored", section "1. Fused Linear Cross-Entropy with Online LogSumExp",
- * step 5).  Arguments as for flce_fwd_bwd.
+ * forward keeps: section "1. Fused Linear Cross-Entropy with Online
+ * LogSumExp", step 5, retains just the loss and each row's normaliser.
+ * Arguments as for flce_fwd_bwd.
  */
 int flce_fwd(const void* h, const void* w, const int64_t* labels,
              int64_t n, int64_t d, int64_t v, flce_dtype dtype,
              int64_t ignore_index, flce_reduction reduction,
              float* loss_out, float* lse_out, hipStream_t stream);
+
+/*
+ * Low-memory variant of flce_fwd_bwd: the same loss, LSE and gradients (same
+ * arguments, layouts, errors and stream semantics) from a workspace of about
+ * 4 n d + 256 MiB bytes instead of one chunk's [C, v] buffer plus a v x d
+ * running sum.  The forward statistics run over the whole vocabulary first;
+ * the backward then walks the vocabulary in slices of vb rows, recomputing each
+ * slice's logits from the saved LSE and turning them into G (blog page,
+ * section "2. In-Kernel Gradient Computation During the Backward Pass": the
+ * backward recomputes tile logits from the per-token LSE).  Each slice's dW
+ * rows are one reduction over every token (fp32 accumulation, rounded once);
+ * dH sums the slices' terms in fp32.  Cost: 8 N D V flop instead of 6.
+ * The slice buffer holds vb = FLCE_LOWMEM_BUFFER_BYTES / (2 n) vocabulary
+ * rows (bf16; 4 n for fp32), rounded down to a multiple of 256, default
+ * budget 256 MiB; see flce_lowmem_plan_info().
+ */
+int flce_fwd_bwd_lowmem(const void* h, const void* w, const int64_t* labels,
+                        int64_t n, int64_t d, int64_t v, flce_dtype dtype,
+                        int64_t ignore_index, flce_reduction reduction,
+                        float* loss_out, float* lse_out, void* dh_out, void* dw_out,
+                        hipStream_t stream);
 
 /*
  * Backward pass from the saved per-token LSE, recomputing the logits: the
@@ -312,6 +334,21 @@ typedef struct {
 /* Fill *out with the plan for these sizes; returns 0 or FLCE_ERR_INVALID_ARG. */
 int flce_plan_info(int64_t n, int64_t d, int64_t v, flce_dtype dtype, int with_bwd, flce_plan_t* out);
 
+/* Workspace bytes of flce_fwd_bwd_lowmem (0 for invalid sizes); host-only. */
+size_t flce_workspace_bytes_lowmem(int64_t n, int64_t d, int64_t v, flce_dtype dtype);
+
+/* Plan of flce_fwd_bwd_lowmem (host-only). */
+typedef struct {
+  int64_t slice_cols;          /* vocabulary rows per slice (the last slice may be narrower) */
+  int64_t num_slices;
+  int64_t slice_chunk_rows;    /* token rows per chunk inside a slice (n when one chunk holds them all) */
+  int64_t slice_chunks;
+  int64_t fwd_chunk_rows;      /* token rows per launch of the forward statistics */
+  size_t buffer_budget_bytes;  /* the budget the slice width was chosen for */
+  size_t workspace_bytes;
+} flce_lowmem_plan_t;
+int flce_lowmem_plan_info(int64_t n, int64_t d, int64_t v, flce_dtype dtype, flce_lowmem_plan_t* out);
+
 /* Static text for a status code. */
 const char* flce_strerror(int status);
 
@@ -334,6 +371,16 @@ const char* flce_profile_kind_name(int kind);
  * with the [n, v] logits it does not allocate.
  */
 int flce_memory_high_water(int reset, uint64_t* used_high_bytes);
+
+/*
+ * The library's pool on the current device keeps the memory of released
+ * workspaces reserved for later calls.  flce_memory_reserved() reports how
+ * many bytes it holds now; flce_pool_trim() returns all but keep_bytes of the
+ * unused part to the device (call it after a synchronisation point, e.g. at
+ * the end of a training step, to give that memory back to other allocators).
+ */
+int flce_memory_reserved(uint64_t* reserved_bytes);
+int flce_pool_trim(uint64_t keep_bytes);
 
 #ifdef __cplusplus
 }

@@ -24,6 +24,7 @@ ENGINE_MFMA, ENGINE_FMA = 0, 1
 
 EXPORTED = (
     "flce_fwd_bwd",
+    "flce_fwd_bwd_lowmem",
     "flce_fwd",
     "flce_bwd",
     "flce_ce_logits",
@@ -34,12 +35,16 @@ EXPORTED = (
     "flce_bwd_shard",
     "flce_sum_parts",
     "flce_workspace_bytes",
+    "flce_workspace_bytes_lowmem",
     "flce_plan_info",
+    "flce_lowmem_plan_info",
     "flce_strerror",
     "flce_profile_enable",
     "flce_profile_read",
     "flce_profile_kind_name",
     "flce_memory_high_water",
+    "flce_memory_reserved",
+    "flce_pool_trim",
 )
 
 
@@ -67,6 +72,21 @@ class PlanInfo(ctypes.Structure):
         return {k: getattr(self, k) for k, _ in self._fields_}
 
 
+class LowmemPlanInfo(ctypes.Structure):
+    _fields_ = [
+        ("slice_cols", ctypes.c_int64),
+        ("num_slices", ctypes.c_int64),
+        ("slice_chunk_rows", ctypes.c_int64),
+        ("slice_chunks", ctypes.c_int64),
+        ("fwd_chunk_rows", ctypes.c_int64),
+        ("buffer_budget_bytes", ctypes.c_size_t),
+        ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+    def as_dict(self):
+        return {k: getattr(self, k) for k, _ in self._fields_}
+
+
 _lib = None
 
 
@@ -81,6 +101,16 @@ def lib() -> ctypes.CDLL:
     p, i64, i32, f = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
     L.flce_fwd_bwd.argtypes = [p, p, p, i64, i64, i64, i32, i64, i32, p, p, p, p, p]
     L.flce_fwd_bwd.restype = i32
+    L.flce_fwd_bwd_lowmem.argtypes = [p, p, p, i64, i64, i64, i32, i64, i32, p, p, p, p, p]
+    L.flce_fwd_bwd_lowmem.restype = i32
+    L.flce_workspace_bytes_lowmem.argtypes = [i64, i64, i64, i32]
+    L.flce_workspace_bytes_lowmem.restype = ctypes.c_size_t
+    L.flce_lowmem_plan_info.argtypes = [i64, i64, i64, i32, ctypes.POINTER(LowmemPlanInfo)]
+    L.flce_lowmem_plan_info.restype = i32
+    L.flce_memory_reserved.argtypes = [ctypes.POINTER(ctypes.c_uint64)]
+    L.flce_memory_reserved.restype = i32
+    L.flce_pool_trim.argtypes = [ctypes.c_uint64]
+    L.flce_pool_trim.restype = i32
     L.flce_fwd.argtypes = [p, p, p, i64, i64, i64, i32, i64, i32, p, p, p]
     L.flce_fwd.restype = i32
     L.flce_bwd.argtypes = [p, p, p, p, p, i64, i64, i64, i32, i64, i32, p, p, p]
@@ -149,6 +179,12 @@ def flce_fwd_bwd(h, w, labels, n, d, v, dtype, ignore_index, reduction, loss_out
                               _ptr(loss_out), _ptr(lse_out), _ptr(dh_out), _ptr(dw_out), _stream(stream))
 
 
+def flce_fwd_bwd_lowmem(h, w, labels, n, d, v, dtype, ignore_index, reduction, loss_out, lse_out, dh_out, dw_out,
+                        stream) -> int:
+    return lib().flce_fwd_bwd_lowmem(_ptr(h), _ptr(w), _ptr(labels), n, d, v, dtype, ignore_index, reduction,
+                                     _ptr(loss_out), _ptr(lse_out), _ptr(dh_out), _ptr(dw_out), _stream(stream))
+
+
 def flce_fwd(h, w, labels, n, d, v, dtype, ignore_index, reduction, loss_out, lse_out, stream) -> int:
     return lib().flce_fwd(_ptr(h), _ptr(w), _ptr(labels), n, d, v, dtype, ignore_index, reduction,
                           _ptr(loss_out), _ptr(lse_out), _stream(stream))
@@ -213,6 +249,18 @@ def flce_plan_info(n, d, v, dtype, with_bwd) -> dict:
     return info.as_dict()
 
 
+def flce_workspace_bytes_lowmem(n, d, v, dtype) -> int:
+    return int(lib().flce_workspace_bytes_lowmem(n, d, v, dtype))
+
+
+def flce_lowmem_plan_info(n, d, v, dtype) -> dict:
+    info = LowmemPlanInfo()
+    st = lib().flce_lowmem_plan_info(n, d, v, dtype, ctypes.byref(info))
+    if st != FLCE_OK:
+        raise FlceError(st, "flce_lowmem_plan_info")
+    return info.as_dict()
+
+
 def flce_strerror(status: int) -> str:
     return strerror(status)
 
@@ -243,6 +291,23 @@ def flce_memory_high_water(reset: bool = False) -> int:
     if st != FLCE_OK:
         raise FlceError(st, "flce_memory_high_water")
     return int(v.value)
+
+
+def flce_memory_reserved() -> int:
+    """Bytes the library's pool on the current device holds (in use or cached)."""
+    v = ctypes.c_uint64(0)
+    st = lib().flce_memory_reserved(ctypes.byref(v))
+    if st != FLCE_OK:
+        raise FlceError(st, "flce_memory_reserved")
+    return int(v.value)
+
+
+def flce_pool_trim(keep_bytes: int = 0) -> int:
+    """Return the pool's cached memory beyond keep_bytes to the device."""
+    st = lib().flce_pool_trim(int(keep_bytes))
+    if st != FLCE_OK:
+        raise FlceError(st, "flce_pool_trim")
+    return st
 
 
 # --- tensor-level convenience ---------------------------------------------------------
@@ -330,6 +395,32 @@ def linear_cross_entropy(h, w, labels, ignore_index: int = -100, reduction: str 
                       torch.cuda.current_stream(h.device))
     if st != FLCE_OK:
         raise FlceError(st, "flce_fwd_bwd")
+    return loss, lse, dh, dw
+
+
+def linear_cross_entropy_lowmem(h, w, labels, ignore_index: int = -100, reduction: str = "mean", out=None):
+    """As linear_cross_entropy, through flce_fwd_bwd_lowmem: the backward recomputes the
+    logits slice by slice of the vocabulary, so the workspace stays near 4 n d bytes plus
+    a 256 MiB slice buffer (8 N D V flop instead of 6)."""
+    import torch
+    _check_inputs(h, w, labels)
+    n, d = h.shape
+    v = w.shape[0]
+    if out is None:
+        loss = torch.empty(1, dtype=torch.float32, device=h.device)
+        lse = torch.empty(n, dtype=torch.float32, device=h.device)
+        dh = torch.empty_like(h)
+        dw = torch.empty_like(w)
+    else:
+        loss, lse, dh, dw = out
+        _check_scalar(loss, h.device, "out loss")
+        _check_vec(lse, n, h.device, "out lse")
+        _check_out(dh, h, "out dh")
+        _check_out(dw, w, "out dw")
+    st = flce_fwd_bwd_lowmem(h, w, labels, n, d, v, _dtype_code(h), ignore_index, _red_code(reduction), loss, lse,
+                             dh, dw, torch.cuda.current_stream(h.device))
+    if st != FLCE_OK:
+        raise FlceError(st, "flce_fwd_bwd_lowmem")
     return loss, lse, dh, dw
 
 

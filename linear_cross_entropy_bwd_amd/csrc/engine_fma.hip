@@ -220,7 +220,7 @@ template <typename T>
 // rows of W; with several splits `out` is split z's fp32 partial (part_stride apart).
 __global__ __launch_bounds__(256) void fma_dh_kernel(const float* __restrict__ G, int64_t vp, const T* __restrict__ W,
                                                      int64_t rows, int64_t d, int64_t v, int64_t k_split,
-                                                     int64_t part_stride, T* __restrict__ out) {
+                                                     int64_t part_stride, int accumulate, T* __restrict__ out) {
   const int64_t m0 = static_cast<int64_t>(blockIdx.x) * BM;
   const int64_t n0 = static_cast<int64_t>(blockIdx.y) * BN;
   const int64_t k_lo = static_cast<int64_t>(blockIdx.z) * k_split;
@@ -237,7 +237,7 @@ __global__ __launch_bounds__(256) void fma_dh_kernel(const float* __restrict__ G
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int64_t n = n0 + tx * 4 + j;
-      if (n < d) Elem<T>::st(out, t * d + n, acc[i][j]);
+      if (n < d) Elem<T>::st(out, t * d + n, accumulate ? Elem<T>::ld(out, t * d + n) + acc[i][j] : acc[i][j]);
     }
   }
 }
@@ -292,7 +292,8 @@ hipError_t fma_dh(const Plan& p, const Work& w, const ChunkArgs& a, hipStream_t 
   const int64_t k_split = (p.v + p.dh_splits - 1) / p.dh_splits;
   float* out = p.dh_splits > 1 ? w.dhpart : static_cast<float*>(a.dh);
   fma_dh_kernel<float><<<grid, 256, 0, s>>>(static_cast<const float*>(w.prob), p.vp, static_cast<const float*>(a.w),
-                                            a.rows, p.d, p.v, k_split, p.chunk * p.d, out);
+                                            a.rows, p.d, p.v, k_split, p.chunk * p.d,
+                                            p.dh_splits == 1 && a.dh_accumulate, out);
   return hipGetLastError();
 }
 

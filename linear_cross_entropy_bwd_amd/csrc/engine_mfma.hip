@@ -772,6 +772,7 @@ struct DhArgs {
   bf16_t* out_bf16;  // direct output (splits == 1, bf16)
   float* out_f32;    // direct fp32 output (splits == 1, fp32) or split partials [splits][C][d]
   int64_t part_stride;
+  int32_t accumulate;  // splits == 1, fp32 output: add to what out_f32 holds
 };
 
 __global__ __launch_bounds__(kThreads) void mfma_dh_kernel(DhArgs a) {
@@ -798,6 +799,8 @@ __global__ __launch_bounds__(kThreads) void mfma_dh_kernel(DhArgs a) {
           const float x = acc.c[I][J][R.value];
           if (a.out_bf16 != nullptr)
             a.out_bf16[row * a.d + col] = f32_to_bf16(x);
+          else if (a.accumulate)
+            a.out_f32[row * a.d + col] += x;
           else
             a.out_f32[sp * a.part_stride + row * a.d + col] = x;
         }
@@ -1080,6 +1083,7 @@ hipError_t mfma_dh(const Plan& p, const Work& w, const ChunkArgs& c, hipStream_t
   a.part_stride = p.chunk * p.d;
   a.out_bf16 = nullptr;
   a.out_f32 = nullptr;
+  a.accumulate = p.dh_splits == 1 && c.dh_accumulate;
   if (p.dh_splits > 1)
     a.out_f32 = w.dhpart;
   else if (p.dtype == FLCE_BF16 && !c.dh_f32)

@@ -19,6 +19,7 @@ namespace {
 
 constexpr size_t kAlign = 256;
 constexpr size_t kDefaultProbBudget = size_t(1) << 30;  // bytes for the chunk's [C, vp] buffer
+constexpr size_t kLowmemBudget = size_t(256) << 20;     // bytes for a vocabulary slice's [C, vb] buffer
 constexpr int64_t kVocabPad = 256;
 constexpr int64_t kMaxDim = int64_t(1) << 24;  // d <= 2^24, v <= 2^24 - 256
 constexpr int64_t kCus = 256;                   // compute units of an MI355X
@@ -58,7 +59,8 @@ static int64_t best_splits(int64_t tiles, int64_t slots, int64_t smax) {
 // multiple of 256 rows once that many fit), never more than half of the rows
 // (rounded up to 16) so that the buffer stays well below the [n, v] logits it
 // replaces, and at least 16.
-int make_plan(int64_t n, int64_t d, int64_t v, int32_t dtype, int32_t with_bwd, Plan* p, int allow_pair) {
+int make_plan(int64_t n, int64_t d, int64_t v, int32_t dtype, int32_t with_bwd, Plan* p, int allow_pair,
+              int64_t budget_req, int whole_rows) {
   if (p == nullptr || n <= 0 || d <= 0 || v <= 0) return FLCE_ERR_INVALID_ARG;
   if (dtype != FLCE_BF16 && dtype != FLCE_F32) return FLCE_ERR_INVALID_ARG;
   if (!mul_ok(n, d) || !mul_ok(v, d) || v > (int64_t(1) << 40) || n > (int64_t(1) << 40))
@@ -79,12 +81,14 @@ int make_plan(int64_t n, int64_t d, int64_t v, int32_t dtype, int32_t with_bwd, 
   q.vp = (v + kVocabPad - 1) / kVocabPad * kVocabPad;
   q.ngroups = (v + q.group - 1) / q.group;
 
-  const int64_t budget = env_i64("FLCE_WORKSPACE_CAP_BYTES", static_cast<int64_t>(kDefaultProbBudget));
+  const int64_t budget =
+      budget_req > 0 ? budget_req : env_i64("FLCE_WORKSPACE_CAP_BYTES", static_cast<int64_t>(kDefaultProbBudget));
   int64_t c_budget = budget / (q.vp * prob_elem);
   c_budget = c_budget >= 256 ? c_budget / 256 * 256 : (c_budget / 16) * 16;
   if (c_budget < 16) c_budget = 16;
   const int64_t half = ((n + 1) / 2 + 15) / 16 * 16;
-  int64_t c = c_budget < half ? c_budget : half;
+  const int64_t c_cap = whole_rows ? n : half;
+  int64_t c = c_budget < c_cap ? c_budget : c_cap;
   if (!with_bwd) {
     // No probability buffer: a forward-only chunk holds just its rows' group
     // partials (8 bytes per row and group), so it spans every row that fits
@@ -111,6 +115,11 @@ int make_plan(int64_t n, int64_t d, int64_t v, int32_t dtype, int32_t with_bwd, 
     const int64_t tiles = ((q.chunk + tm - 1) / tm) * ((d + tm - 1) / tm);
     int64_t smax = q.vp / (mfma ? 4096 : 256);
     if (smax > (mfma ? 8 : 16)) smax = mfma ? 8 : 16;
+    // the fp32 partials ([S][C][d]) stay within half of the chunk buffer's bytes,
+    // so that they never dominate the workspace
+    const int64_t part_bytes = q.chunk * d * 4;
+    const int64_t s_bytes = (q.chunk * q.vp * prob_elem / 2) / part_bytes;
+    if (smax > s_bytes) smax = s_bytes < 1 ? 1 : s_bytes;
     int64_t s = best_splits(tiles, kCus, smax);
     s = env_i64("FLCE_DH_SPLITS", s);
     if (s > q.vp / 64) s = q.vp / 64;  // every split keeps at least one 64-column stage
@@ -310,6 +319,7 @@ hipError_t run(const Plan& p, const Work& wk, const void* h, const void* w, cons
     a.grad_out = nullptr;
     a.zy_rows = zy_out != nullptr ? zy_out + a.row0 : nullptr;
     a.dh_f32 = 0;
+    a.dh_accumulate = 0;
     a.fp8 = h_scale != nullptr ? 1 : 0;
     a.h_scale = h_scale != nullptr ? h_scale + a.row0 : nullptr;
     a.w_scale = w_scale;
@@ -339,10 +349,11 @@ hipError_t run(const Plan& p, const Work& wk, const void* h, const void* w, cons
 
 // The backward from the saved LSE (recompute): per chunk the logits are
 // recomputed and their epilogue writes G directly; then dH and dW as above.
-// dh_f32: dh_out is an fp32 array whatever the dtype (a vocabulary shard's dH partial).
+// dh_f32: dh_out is an fp32 array whatever the dtype (a vocabulary shard's dH partial);
+// dh_accumulate: dh_out (fp32) already holds a partial sum, to which this call's dH is added.
 hipError_t run_bwd(const Plan& p, const Work& wk, const void* h, const void* w, const int64_t* labels,
                    const float* lse, const float* grad_out, int64_t ignore_index, int32_t reduction, void* dh_out,
-                   void* dw_out, hipStream_t s, int dh_f32 = 0) {
+                   void* dw_out, hipStream_t s, int dh_f32 = 0, int dh_accumulate = 0) {
   const int64_t elem = p.dtype == FLCE_BF16 ? 2 : 4;
   const int64_t dh_elem = dh_f32 ? 4 : elem;
   hipError_t e = timed(K_LABEL_SCAN, s, [&] { return launch_label_scan(p, wk, labels, ignore_index, s); });
@@ -365,6 +376,7 @@ hipError_t run_bwd(const Plan& p, const Work& wk, const void* h, const void* w, 
     a.grad_out = grad_out;
     a.zy_rows = nullptr;
     a.dh_f32 = dh_f32;
+    a.dh_accumulate = dh_accumulate;
     a.fp8 = 0;
     a.h_scale = nullptr;
     a.w_scale = nullptr;
@@ -435,6 +447,103 @@ int call_bwd(const void* h, const void* w, const int64_t* labels, const float* l
   if (st != FLCE_OK) return st;
   return with_workspace(p, stream, [&](const Work& wk) {
     return run_bwd(p, wk, h, w, labels, lse, grad_out, ignore_index, reduction, dh_out, dw_out, stream);
+  });
+}
+
+// ---- low-memory fused call: the forward statistics over the whole vocabulary,
+// then the backward over vocabulary slices with the logits recomputed ----------
+
+}  // namespace
+
+// Plan of flce_fwd_bwd_lowmem: a forward-only plan, then slices of `vb`
+// vocabulary rows (the last one narrower), each run as a backward from the
+// saved LSE whose chunks span as many token rows as the buffer budget allows
+// (all n at the sizes measured here, so a slice's dW is one reduction over all
+// tokens with no running sum).  The slices' dH terms add up in an fp32 [n, d]
+// array (bf16) or in dh_out itself (fp32).  Layout of the one workspace:
+// [lse n fp32][dH sum n x d fp32, bf16 only][shifted labels n int64][union of
+// the forward plan's and the slice plans' workspaces, used one after another].
+int make_lowmem_plan(int64_t n, int64_t d, int64_t v, int32_t dtype, LowmemPlan* lp) {
+  if (lp == nullptr || n <= 0 || d <= 0 || v <= 0) return FLCE_ERR_INVALID_ARG;
+  if (dtype != FLCE_BF16 && dtype != FLCE_F32) return FLCE_ERR_INVALID_ARG;
+  if (!mul_ok(n, d) || !mul_ok(v, d) || v > (int64_t(1) << 40) || n > (int64_t(1) << 40))
+    return FLCE_ERR_INVALID_ARG;
+  LowmemPlan q;
+  memset(&q, 0, sizeof(q));
+  q.budget = env_i64("FLCE_LOWMEM_BUFFER_BYTES", static_cast<int64_t>(kLowmemBudget));
+  const int64_t prob_elem = dtype == FLCE_BF16 ? 2 : 4;
+  // slice width: whole 256-row blocks, as many as one all-token buffer fits, and at
+  // most half of the vocabulary, so that no buffer spans [n, v]; a vocabulary of
+  // 256 rows or fewer is one slice whose chunks keep below half of the rows
+  int64_t vb = q.budget / (n * prob_elem) / 256 * 256;
+  if (vb < 256) vb = 256;
+  const int64_t half_v = ((v + 1) / 2 + 255) / 256 * 256;
+  if (vb > half_v) vb = half_v;
+  const int whole_rows = vb < v ? 1 : 0;
+  if (vb > v) vb = v;
+  q.vb = vb;
+  q.nslices = (v + vb - 1) / vb;
+  int st = make_plan(n, d, v, dtype, 0, &q.fwd, 1, q.budget);
+  if (st != FLCE_OK) return st;
+  st = make_plan(n, d, vb, dtype, 1, &q.slice, 0, q.budget, whole_rows);
+  if (st != FLCE_OK) return st;
+  const int64_t v_last = v - (q.nslices - 1) * vb;
+  st = make_plan(n, d, v_last, dtype, 1, &q.last, 0, q.budget, whole_rows);
+  if (st != FLCE_OK) return st;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align_up(bytes);
+    return o;
+  };
+  q.off_lse = take(sizeof(float) * static_cast<size_t>(n));
+  q.off_dhsum = take(dtype == FLCE_BF16 ? sizeof(float) * static_cast<size_t>(n) * static_cast<size_t>(d) : 0);
+  q.off_labels = take(sizeof(int64_t) * static_cast<size_t>(n));
+  q.off_union = off;
+  size_t u = q.fwd.total;
+  if (q.slice.total > u) u = q.slice.total;
+  if (q.last.total > u) u = q.last.total;
+  q.total = off + u;
+  *lp = q;
+  return FLCE_OK;
+}
+
+namespace {
+
+int call_lowmem(const void* h, const void* w, const int64_t* labels, int64_t n, int64_t d, int64_t v,
+                flce_dtype dtype, int64_t ignore_index, flce_reduction reduction, float* loss_out, float* lse_out,
+                void* dh_out, void* dw_out, hipStream_t stream) {
+  int st = check_common(h, w, labels, n, d, v, dtype, reduction, loss_out, lse_out);
+  if (st != FLCE_OK) return st;
+  if (dh_out == nullptr || dw_out == nullptr) return FLCE_ERR_INVALID_ARG;
+  if (!aligned(dh_out, 16) || !aligned(dw_out, 16)) return FLCE_ERR_ALIGNMENT;
+  LowmemPlan lp;
+  st = make_lowmem_plan(n, d, v, dtype, &lp);
+  if (st != FLCE_OK) return st;
+  // every slice's first id, shifted off the labels and the ignore value, must not wrap
+  if (ignore_index < INT64_MIN + v) return FLCE_ERR_INVALID_ARG;
+  Plan whole = lp.fwd;
+  whole.total = lp.total;
+  const int64_t elem = dtype == FLCE_BF16 ? 2 : 4;
+  return with_workspace(whole, stream, [&](const Work& all) {
+    char* base = all.base;
+    float* lse = lse_out != nullptr ? lse_out : reinterpret_cast<float*>(base + lp.off_lse);
+    float* dh_sum = dtype == FLCE_BF16 ? reinterpret_cast<float*>(base + lp.off_dhsum) : static_cast<float*>(dh_out);
+    int64_t* shifted = reinterpret_cast<int64_t*>(base + lp.off_labels);
+    const Work wf = carve(lp.fwd, base + lp.off_union);
+    hipError_t e = run(lp.fwd, wf, h, w, labels, ignore_index, reduction, loss_out, lse, nullptr, nullptr, stream);
+    for (int64_t q = 0; e == hipSuccess && q < lp.nslices; ++q) {
+      const int64_t v0 = q * lp.vb;
+      const Plan& ps = q + 1 < lp.nslices ? lp.slice : lp.last;
+      const Work ws = carve(ps, base + lp.off_union);
+      e = launch_shift_labels(labels, n, v0, shifted, stream);
+      if (e != hipSuccess) break;
+      e = run_bwd(ps, ws, h, static_cast<const char*>(w) + v0 * d * elem, shifted, lse, nullptr, ignore_index - v0,
+                  reduction, dh_sum, static_cast<char*>(dw_out) + v0 * d * elem, stream, 1, q > 0 ? 1 : 0);
+    }
+    if (e == hipSuccess && dtype == FLCE_BF16)
+      e = timed(K_DH_REDUCE, stream, [&] { return launch_sum_parts(dh_sum, 1, n * d, FLCE_BF16, dh_out, stream); });
+    return e;
   });
 }
 
@@ -563,6 +672,7 @@ int call_bwd_fp8(const void* h_q, const float* h_scale, const void* w_q, const f
       a.grad_out = grad_out;
       a.zy_rows = nullptr;
       a.dh_f32 = 0;
+      a.dh_accumulate = 0;
       a.dw_mode = p.nchunks == 1 ? DW_SINGLE : (c == 0 ? DW_FIRST : (c == p.nchunks - 1 ? DW_LAST : DW_MID));
       // recompute: fp8 operands, G into the chunk buffer
       a.fp8 = 1;
@@ -712,6 +822,34 @@ int flce_fwd_bwd(const void* h, const void* w, const int64_t* labels, int64_t n,
                     1);
 }
 
+int flce_fwd_bwd_lowmem(const void* h, const void* w, const int64_t* labels, int64_t n, int64_t d, int64_t v,
+                        flce_dtype dtype, int64_t ignore_index, flce_reduction reduction, float* loss_out,
+                        float* lse_out, void* dh_out, void* dw_out, hipStream_t stream) {
+  return flce::call_lowmem(h, w, labels, n, d, v, dtype, ignore_index, reduction, loss_out, lse_out, dh_out, dw_out,
+                           stream);
+}
+
+size_t flce_workspace_bytes_lowmem(int64_t n, int64_t d, int64_t v, flce_dtype dtype) {
+  flce::LowmemPlan lp;
+  if (flce::make_lowmem_plan(n, d, v, dtype, &lp) != FLCE_OK) return 0;
+  return lp.total;
+}
+
+int flce_lowmem_plan_info(int64_t n, int64_t d, int64_t v, flce_dtype dtype, flce_lowmem_plan_t* out) {
+  if (out == nullptr) return FLCE_ERR_INVALID_ARG;
+  flce::LowmemPlan lp;
+  const int st = flce::make_lowmem_plan(n, d, v, dtype, &lp);
+  if (st != FLCE_OK) return st;
+  out->slice_cols = lp.vb;
+  out->num_slices = lp.nslices;
+  out->slice_chunk_rows = lp.slice.chunk;
+  out->slice_chunks = lp.slice.nchunks;
+  out->fwd_chunk_rows = lp.fwd.chunk;
+  out->buffer_budget_bytes = static_cast<size_t>(lp.budget);
+  out->workspace_bytes = lp.total;
+  return FLCE_OK;
+}
+
 int flce_fwd(const void* h, const void* w, const int64_t* labels, int64_t n, int64_t d, int64_t v, flce_dtype dtype,
              int64_t ignore_index, flce_reduction reduction, float* loss_out, float* lse_out, hipStream_t stream) {
   return flce::call(h, w, labels, n, d, v, dtype, ignore_index, reduction, loss_out, lse_out, nullptr, nullptr,
@@ -838,6 +976,26 @@ int flce_profile_read(int max_kinds, int64_t* launches, double* total_ms) {
 const char* flce_profile_kind_name(int kind) {
   if (kind < 0 || kind >= flce::K_NUM_KINDS) return nullptr;
   return flce::kKindNames[kind];
+}
+
+int flce_memory_reserved(uint64_t* reserved_bytes) {
+  if (reserved_bytes == nullptr) return FLCE_ERR_INVALID_ARG;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FLCE_ERR_HIP;
+  hipMemPool_t pool;
+  if (flce::device_pool(dev, &pool) != hipSuccess) return FLCE_ERR_HIP;
+  uint64_t v = 0;
+  if (hipMemPoolGetAttribute(pool, hipMemPoolAttrReservedMemCurrent, &v) != hipSuccess) return FLCE_ERR_HIP;
+  *reserved_bytes = v;
+  return FLCE_OK;
+}
+
+int flce_pool_trim(uint64_t keep_bytes) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FLCE_ERR_HIP;
+  hipMemPool_t pool;
+  if (flce::device_pool(dev, &pool) != hipSuccess) return FLCE_ERR_HIP;
+  return hipMemPoolTrimTo(pool, static_cast<size_t>(keep_bytes)) == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
 }
 
 int flce_memory_high_water(int reset, uint64_t* used_high_bytes) {

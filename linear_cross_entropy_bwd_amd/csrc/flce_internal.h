@@ -42,7 +42,24 @@ struct Plan {
 };
 
 // allow_pair = 0 keeps one chunk buffer (for loops that run dW chunk by chunk).
-int make_plan(int64_t n, int64_t d, int64_t v, int32_t dtype, int32_t with_bwd, Plan* p, int allow_pair = 1);
+// budget > 0 replaces the default byte budget of one chunk's buffer (or, for a
+// forward-only plan, of its group partials).  whole_rows = 1 lets a chunk hold
+// every row that fits the budget, up to all n (a vocabulary slice's buffer,
+// which is narrower than the vocabulary); otherwise a gradient plan keeps its
+// chunks below half of the rows.
+int make_plan(int64_t n, int64_t d, int64_t v, int32_t dtype, int32_t with_bwd, Plan* p, int allow_pair = 1,
+              int64_t budget = 0, int whole_rows = 0);
+
+// Plan of the low-memory fused call (flce_fwd_bwd_lowmem).
+struct LowmemPlan {
+  Plan fwd;          // forward-only plan over the whole vocabulary
+  Plan slice, last;  // backward plans of a full-width and of the last vocabulary slice
+  int64_t vb;        // vocabulary rows per slice
+  int64_t nslices;
+  int64_t budget;    // bytes of one slice's gradient buffer (and of the forward's group partials)
+  size_t off_lse, off_dhsum, off_labels, off_union, total;
+};
+int make_lowmem_plan(int64_t n, int64_t d, int64_t v, int32_t dtype, LowmemPlan* lp);
 
 // Pointers into the workspace for one call.
 struct Work {
@@ -99,6 +116,7 @@ struct ChunkArgs {
   const float* grad_out;    // upstream gradient of the loss (device scalar) or nullptr for 1
   float* zy_rows;           // chunk's slice of a per-row target-logit output, or nullptr
   int32_t dh_f32;           // 1: dh is an fp32 array whatever the dtype (a shard's dH partial)
+  int32_t dh_accumulate;    // 1: dh (fp32) already holds a partial sum; this chunk's term is added to it
   int32_t fp8;              // 1: h and w hold e4m3 bytes (d counts byte pairs), scaled per row
   const float* h_scale;     // fp8: chunk's first token scale
   const float* w_scale;     // fp8: vocabulary row scales

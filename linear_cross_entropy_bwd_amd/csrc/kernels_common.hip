@@ -169,13 +169,15 @@ __global__ __launch_bounds__(256) void grad_kernel(TP* __restrict__ prob, int64_
   }
 }
 
-// dH rows = sum of the split partials, rounded to the output type.
+// dH rows = sum of the split partials (added to what `out` holds when
+// accumulating), rounded to the output type.
 template <typename TO>
 __global__ __launch_bounds__(256) void dh_reduce_kernel(const float* __restrict__ part, int64_t splits,
-                                                        int64_t stride, int64_t count, TO* __restrict__ out) {
+                                                        int64_t stride, int64_t count, int accumulate,
+                                                        TO* __restrict__ out) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (i >= count) return;
-  float acc = 0.0f;
+  float acc = accumulate ? Elem<TO>::ld(out, i) : 0.0f;
   for (int64_t s = 0; s < splits; ++s) acc += part[s * stride + i];
   Elem<TO>::st(out, i, acc);
 }
@@ -294,10 +296,10 @@ hipError_t launch_dh_reduce(const Plan& p, const Work& w, const ChunkArgs& a, hi
   const int64_t count = a.rows * p.d;
   const unsigned blocks = static_cast<unsigned>((count + 255) / 256);
   if (p.dtype == FLCE_BF16 && !a.dh_f32)
-    dh_reduce_kernel<bf16_t><<<blocks, 256, 0, s>>>(w.dhpart, p.dh_splits, p.chunk * p.d, count,
+    dh_reduce_kernel<bf16_t><<<blocks, 256, 0, s>>>(w.dhpart, p.dh_splits, p.chunk * p.d, count, 0,
                                                     static_cast<bf16_t*>(a.dh));
   else
-    dh_reduce_kernel<float><<<blocks, 256, 0, s>>>(w.dhpart, p.dh_splits, p.chunk * p.d, count,
+    dh_reduce_kernel<float><<<blocks, 256, 0, s>>>(w.dhpart, p.dh_splits, p.chunk * p.d, count, a.dh_accumulate,
                                                    static_cast<float*>(a.dh));
   return hipGetLastError();
 }
@@ -339,9 +341,9 @@ hipError_t launch_sum_parts(const float* parts, int64_t num_parts, int64_t count
                             hipStream_t s) {
   const unsigned blocks = static_cast<unsigned>((count + 255) / 256);
   if (dtype == FLCE_BF16)
-    dh_reduce_kernel<bf16_t><<<blocks, 256, 0, s>>>(parts, num_parts, count, count, static_cast<bf16_t*>(out));
+    dh_reduce_kernel<bf16_t><<<blocks, 256, 0, s>>>(parts, num_parts, count, count, 0, static_cast<bf16_t*>(out));
   else
-    dh_reduce_kernel<float><<<blocks, 256, 0, s>>>(parts, num_parts, count, count, static_cast<float*>(out));
+    dh_reduce_kernel<float><<<blocks, 256, 0, s>>>(parts, num_parts, count, count, 0, static_cast<float*>(out));
   return hipGetLastError();
 }
 

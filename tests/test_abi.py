@@ -279,3 +279,39 @@ def test_fp8_wrappers_reject_host_tensors():
         flce.linear_cross_entropy_forward_fp8(hq, hs, wq, ws, y)
     with pytest.raises(ValueError):
         flce.linear_cross_entropy_backward_fp8(hq, hs, wq, ws, y, torch.zeros(4))
+
+
+@pytest.mark.parametrize("dtype", [flce.FLCE_BF16, flce.FLCE_F32])
+@pytest.mark.parametrize("shape", [(256, 512, 4096), (8192, 4096, 128256), (4096, 3584, 151936),
+                                   (32768, 4096, 128256), (16384, 4096, 32000), (37, 72, 1001), (300, 128, 2500)])
+def test_lowmem_plan_invariants(dtype, shape):
+    n, d, v = shape
+    p = flce.flce_lowmem_plan_info(n, d, v, dtype)
+    vb, q = p["slice_cols"], p["num_slices"]
+    assert q == -(-v // vb) and (vb % 256 == 0 or q == 1)
+    assert q >= 2 or p["slice_chunk_rows"] < n or n < 32      # no buffer spans [n, v]
+    elem = 2 if dtype == flce.FLCE_BF16 else 4
+    assert p["slice_chunk_rows"] * vb * elem <= max(p["buffer_budget_bytes"], p["slice_chunk_rows"] * 256 * elem)
+    assert p["workspace_bytes"] == flce.flce_workspace_bytes_lowmem(n, d, v, dtype)
+    assert p["workspace_bytes"] < n * v * 4
+    if (n, d, v) == (8192, 4096, 128256):
+        # the Llama-3 head: the low-memory path holds under a fifth of the fp32 logits it avoids
+        assert p["workspace_bytes"] <= 0.2 * n * v * 4
+        assert p["slice_chunks"] == 1                          # each slice's dW is one reduction over all tokens
+
+
+def test_lowmem_budget_override(monkeypatch):
+    monkeypatch.setenv("FLCE_LOWMEM_BUFFER_BYTES", str(600 * 1000))
+    p = flce.flce_lowmem_plan_info(300, 128, 2500, flce.FLCE_BF16)
+    assert p["slice_cols"] == 768 and p["num_slices"] == 4          # 600 kB / (300 rows x 2 B) -> 3 x 256 columns
+    assert flce.flce_workspace_bytes_lowmem(0, 8, 8, flce.FLCE_BF16) == 0
+
+
+def test_dh_split_partials_stay_below_the_chunk_buffer():
+    for shape, dtype in [((256, 512, 4096), flce.FLCE_F32), ((4096, 3584, 151936), flce.FLCE_BF16),
+                         ((37, 72, 1001), flce.FLCE_F32), ((8192, 4096, 128256), flce.FLCE_BF16)]:
+        n, d, v = shape
+        p = flce.flce_plan_info(n, d, v, dtype, 1)
+        if p["dh_splits"] > 1:
+            assert p["dh_splits"] * p["chunk_rows"] * d * 4 <= max(p["prob_buffer_bytes"] // 2, p["chunk_rows"] * d * 4)
+        assert p["workspace_bytes"] < n * v * 4 or n < 256   # tiny shapes: 16-row chunk rounding and alignment
