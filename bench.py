@@ -4,7 +4,17 @@ One step = one flce_fwd_bwd call (label scan, logits GEMM with the online
 LSE / target epilogue, merge, in-place gradient, dH and dW GEMMs, loss
 reduction) over the Llama-3-8B LM-head workload: N=8192 tokens, D=4096,
 V=128256, bf16, 5% ignored labels, mean reduction.  Inputs are synthetic,
-seeded and resident in HBM before timing starts.
+seeded and resident in HBM before timing starts.  The headline `value` and
+`ms_per_step` come from steps timed without any per-kernel instrumentation;
+a second pass with the library's HIP-event instrumentation gives the
+per-kernel split and the roofline figures.
+
+By default the line also carries every workload (`per_config`: tokens/s,
+matrix-peak fraction, extra device memory against the N V 4 bytes of logits
+avoided, and parity against the fp64 oracle), the parity of the headline
+workload, the low-memory path and a memory/speed sweep, the other entry
+points (split forward/backward, forward only, vocabulary split, FP8,
+cross-entropy on given logits) and the oracle's CPU baseline.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
@@ -72,40 +82,203 @@ def cpu_baseline(wl, h, w, y, rows: int):
                       f"{dt:.1f} s incl. fp64 conversion"}
 
 
-def all_configs_measure(flce, torch, args, stream):
-    """flce_fwd_bwd on every workload: median step time, tokens/s, MFMA % (6 N D V against
-    the workload dtype's matrix peak) and the extra device memory against the N V 4 bytes
-    of logits it avoids."""
-    from workloads import CONFIGS, logits_bytes_avoided, make_inputs
-    out = {}
-    for name, wl in CONFIGS.items():
-        h, w, y = make_inputs(wl)
-        dev = torch.device("cuda:0")
-        hd, wd, yd = h.to(dev), w.to(dev), y.to(dev)
-        del h, w
-        o = (torch.empty(1, dtype=torch.float32, device=dev), torch.empty(wl.n, dtype=torch.float32, device=dev),
-             torch.empty_like(hd), torch.empty_like(wd))
-        for _ in range(max(1, args.warmup)):
-            flce.linear_cross_entropy(hd, wd, yd, reduction=wl.reduction, out=o)
-        torch.cuda.synchronize()
-        flce.flce_memory_high_water(reset=True)
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-        ev[0].record(stream)
-        for i in range(args.steps):
-            flce.linear_cross_entropy(hd, wd, yd, reduction=wl.reduction, out=o)
-            ev[i + 1].record(stream)
-        torch.cuda.synchronize()
-        extra = flce.flce_memory_high_water()
-        t = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
-        med = t[len(t) // 2] if len(t) % 2 else 0.5 * (t[len(t) // 2 - 1] + t[len(t) // 2])
-        flop = 6.0 * wl.n * wl.d * wl.v
-        out[name] = {"n": wl.n, "d": wl.d, "v": wl.v, "dtype": wl.dtype, "ms_median": med, "ms_min": t[0],
-                     "tokens_per_s": wl.n / (med * 1e-3),
-                     "mfma_pct": 100.0 * flop / (med * 1e-3) / (PEAK_TFLOPS[wl.dtype] * 1e12),
-                     "extra_device_bytes": extra, "logits_bytes_avoided": logits_bytes_avoided(wl.n, wl.v)}
-        log(f"[bench] {name}: {med:.3f} ms median, {out[name]['mfma_pct']:.1f}% of the {wl.dtype} peak")
-        del hd, wd, yd, o
-        torch.cuda.empty_cache()
+def median(xs):
+    t = sorted(xs)
+    return t[len(t) // 2] if len(t) % 2 else 0.5 * (t[len(t) // 2 - 1] + t[len(t) // 2])
+
+
+def time_steps(torch, fn, stream, steps, warmup):
+    """Per-step milliseconds of `fn` (HIP events on `stream` between the steps), after
+    `warmup` untimed calls; no instrumentation of the library is on."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(stream)
+    for i in range(steps):
+        fn()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    return [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)], ev[0].elapsed_time(ev[-1])
+
+
+def sample_rows(n, chunk, y, rng):
+    """Token rows the parity check compares: the first and last row, both sides of every
+    chunk boundary, 16 random rows and up to 4 ignored rows."""
+    import numpy as np
+    rows = {0, n - 1}
+    for c in range(chunk, n, chunk):
+        rows.update({c - 1, c})
+    rows.update(int(r) for r in rng.choice(n, size=min(16, n), replace=False))
+    ign = np.flatnonzero(y == -100)
+    if ign.size:
+        rows.update(int(r) for r in rng.choice(ign, size=min(4, ign.size), replace=False))
+    return sorted(r for r in rows if 0 <= r < n)
+
+
+def sample_vocab(v, y, rng):
+    """Vocabulary rows of dW the parity check compares: both ends, 6 label ids, 6 random ids."""
+    cols = {0, 1, v - 1, v - 2}
+    valid = y[y >= 0]
+    if valid.size:
+        cols.update(int(c) for c in rng.choice(valid, size=min(6, valid.size), replace=False))
+    cols.update(int(c) for c in rng.choice(v, size=min(6, v), replace=False))
+    return sorted(c for c in cols if 0 <= c < v)
+
+
+def gpu_samples(torch, out, rows, cols):
+    """Host copies of what the parity check compares: loss, every LSE, sampled dH and dW rows."""
+    loss, lse, dh, dw = out
+    dev = dh.device
+    return {"loss": float(loss.item()), "lse": lse.double().cpu().numpy(),
+            "dh": dh[torch.as_tensor(rows, device=dev)].float().double().cpu().numpy(),
+            "dw": dw[torch.as_tensor(cols, device=dev)].float().double().cpu().numpy(),
+            "dh_ignored_zero": None}
+
+
+def parity_against_oracle(wl, h, w, y, got, rows, cols, workers):
+    """Errors of the GPU results against the fp64 oracle: the loss and every row's LSE from
+    the oracle's whole forward, dH on sampled token rows and dW on sampled vocabulary rows
+    (from the oracle's own LSE); the norms and tolerances of the parity tests."""
+    import numpy as np
+
+    from oracle import flce_dw_rows, flce_forward, flce_rows
+    t0 = time.perf_counter()
+    w64 = w.float().double().numpy() if hasattr(w, "numpy") else w
+    rloss, rlse = flce_forward(h, w64, y, reduction=wl.reduction, workers=workers)
+    _, rdh = flce_rows(h, w64, y, rows, reduction=wl.reduction)
+    rdw = flce_dw_rows(h, w64, y, rlse, cols, reduction=wl.reduction)
+
+    def rel_max(a, b):
+        den = float(np.max(np.abs(b)))
+        return float(np.max(np.abs(a - b))) / den if den > 0 else float(np.max(np.abs(a - b)))
+    tol = {"bf16": (2e-3, 2e-2), "f32": (1e-5, 1e-4)}[wl.dtype]
+    e = {"loss_rel": abs(got["loss"] - rloss) / abs(rloss) if rloss != 0 else abs(got["loss"] - rloss),
+         "lse_max_rel": float(np.max(np.abs(got["lse"] - rlse) / np.abs(rlse))),
+         "dh_rel_sampled": rel_max(got["dh"], rdh), "dw_rel_sampled": rel_max(got["dw"], rdw),
+         "rows_sampled": len(rows), "vocab_rows_sampled": len(cols),
+         "tolerance": {"loss_lse": tol[0], "grad": tol[1]}}
+    e["within_tolerance"] = bool(e["loss_rel"] <= tol[0] and e["lse_max_rel"] <= tol[0]
+                                 and e["dh_rel_sampled"] <= tol[1] and e["dw_rel_sampled"] <= tol[1])
+    e["oracle_s"] = time.perf_counter() - t0
+    return e
+
+
+def measure_workload(flce, torch, wl, args, stream, h, w, y, with_kernels=False):
+    """flce_fwd_bwd on one workload: uninstrumented per-step times, the pool's peak and
+    reserved bytes, optionally a second instrumented pass (per-kernel times), and the
+    host copies the parity check needs."""
+    import numpy as np
+
+    from workloads import logits_bytes_avoided
+    dev = torch.device("cuda:0")
+    hd, wd, yd = h.to(dev), w.to(dev), y.to(dev)
+    o = (torch.empty(1, dtype=torch.float32, device=dev), torch.empty(wl.n, dtype=torch.float32, device=dev),
+         torch.empty_like(hd), torch.empty_like(wd))
+    dt = flce.FLCE_BF16 if wl.dtype == "bf16" else flce.FLCE_F32
+    plan = flce.flce_plan_info(wl.n, wl.d, wl.v, dt, 1)
+
+    def step():
+        flce.linear_cross_entropy(hd, wd, yd, reduction=wl.reduction, out=o)
+    step()
+    torch.cuda.synchronize()
+    flce.flce_memory_high_water(reset=True)
+    per, total = time_steps(torch, step, stream, args.steps, max(1, args.warmup))
+    extra = flce.flce_memory_high_water()
+    reserved = flce.flce_memory_reserved()
+    flop = 6.0 * wl.n * wl.d * wl.v
+    res = {"n": wl.n, "d": wl.d, "v": wl.v, "dtype": wl.dtype, "reduction": wl.reduction,
+           "ms_per_step": total / args.steps, "ms_median": median(per), "ms_min": min(per),
+           "tokens_per_s": wl.n * args.steps / (total * 1e-3),
+           "mfma_pct": 100.0 * flop / (total / args.steps * 1e-3) / (PEAK_TFLOPS[wl.dtype] * 1e12),
+           "extra_device_bytes": extra, "pool_reserved_bytes": reserved,
+           "logits_bytes_avoided": logits_bytes_avoided(wl.n, wl.v),
+           "memory_ratio": extra / logits_bytes_avoided(wl.n, wl.v), "plan": plan}
+    if with_kernels:
+        flce.flce_profile_read()
+        flce.flce_profile_enable(True)
+        _, total_i = time_steps(torch, step, stream, args.steps, 0)
+        flce.flce_profile_enable(False)
+        res["ms_per_step_instrumented"] = total_i / args.steps
+        res["kernels"] = flce.flce_profile_read()
+    rng = np.random.default_rng(4242)
+    rows = sample_rows(wl.n, plan["chunk_rows"], y.numpy(), rng)
+    cols = sample_vocab(wl.v, y.numpy(), rng)
+    got = gpu_samples(torch, o, rows, cols)
+    ign = torch.from_numpy(y.numpy() == -100).to(dev)
+    res["ignored_rows_dh_zero"] = bool((o[2][ign] == 0).all()) if bool(ign.any()) else None
+    log(f"[bench] {wl.name}: {res['ms_per_step']:.3f} ms/step (median {res['ms_median']:.3f}), "
+        f"{res['mfma_pct']:.1f}% of the {wl.dtype} peak, extra {extra / 1e6:.1f} MB "
+        f"({res['memory_ratio']:.3f} of the fp32 logits)")
+    handles = (hd, wd, yd, o)
+    return res, got, rows, cols, handles
+
+
+def lowmem_measure(flce, torch, wl, args, stream, hd, wd, yd, budgets):
+    """flce_fwd_bwd_lowmem (forward statistics, then the backward over vocabulary slices
+    with the logits recomputed): per budget of the slice buffer, the step time and the
+    pool's peak against the fp32 logits; credited 6 N D V like the fused call."""
+    from workloads import logits_bytes_avoided
+    o = (torch.empty(1, dtype=torch.float32, device=hd.device), torch.empty(wl.n, dtype=torch.float32, device=hd.device),
+         torch.empty_like(hd), torch.empty_like(wd))
+    dt = flce.FLCE_BF16 if wl.dtype == "bf16" else flce.FLCE_F32
+    out = []
+    for b in budgets:
+        if b is not None:
+            os.environ["FLCE_LOWMEM_BUFFER_BYTES"] = str(b)
+        try:
+            plan = flce.flce_lowmem_plan_info(wl.n, wl.d, wl.v, dt)
+
+            def step():
+                flce.linear_cross_entropy_lowmem(hd, wd, yd, reduction=wl.reduction, out=o)
+            step()
+            torch.cuda.synchronize()
+            flce.flce_memory_high_water(reset=True)
+            _, total = time_steps(torch, step, stream, max(3, args.steps // 2), 1)
+            peak = flce.flce_memory_high_water()
+        finally:
+            os.environ.pop("FLCE_LOWMEM_BUFFER_BYTES", None)
+        ms = total / max(3, args.steps // 2)
+        out.append({"path": "flce_fwd_bwd_lowmem", "slice_budget_bytes": plan["buffer_budget_bytes"],
+                    "slices": plan["num_slices"], "slice_cols": plan["slice_cols"], "ms_per_step": ms,
+                    "tokens_per_s": wl.n / (ms * 1e-3),
+                    "mfma_pct_6ndv": 100.0 * 6.0 * wl.n * wl.d * wl.v / (ms * 1e-3) / (PEAK_TFLOPS[wl.dtype] * 1e12),
+                    "mfma_pct_8ndv": 100.0 * 8.0 * wl.n * wl.d * wl.v / (ms * 1e-3) / (PEAK_TFLOPS[wl.dtype] * 1e12),
+                    "extra_device_bytes": peak, "memory_ratio": peak / logits_bytes_avoided(wl.n, wl.v)})
+        log(f"[bench] {wl.name} lowmem budget {plan['buffer_budget_bytes'] >> 20} MiB: {ms:.3f} ms/step, "
+            f"peak {peak / 1e6:.1f} MB ({out[-1]['memory_ratio']:.3f})")
+    return out
+
+
+def fused_cap_measure(flce, torch, wl, args, stream, hd, wd, yd, caps):
+    """flce_fwd_bwd under smaller chunk-buffer budgets (FLCE_WORKSPACE_CAP_BYTES): step
+    time against the pool's peak."""
+    from workloads import logits_bytes_avoided
+    o = (torch.empty(1, dtype=torch.float32, device=hd.device), torch.empty(wl.n, dtype=torch.float32, device=hd.device),
+         torch.empty_like(hd), torch.empty_like(wd))
+    dt = flce.FLCE_BF16 if wl.dtype == "bf16" else flce.FLCE_F32
+    out = []
+    for cap in caps:
+        os.environ["FLCE_WORKSPACE_CAP_BYTES"] = str(cap)
+        try:
+            plan = flce.flce_plan_info(wl.n, wl.d, wl.v, dt, 1)
+
+            def step():
+                flce.linear_cross_entropy(hd, wd, yd, reduction=wl.reduction, out=o)
+            step()
+            torch.cuda.synchronize()
+            flce.flce_memory_high_water(reset=True)
+            _, total = time_steps(torch, step, stream, max(3, args.steps // 2), 1)
+            peak = flce.flce_memory_high_water()
+        finally:
+            os.environ.pop("FLCE_WORKSPACE_CAP_BYTES", None)
+        ms = total / max(3, args.steps // 2)
+        out.append({"path": "flce_fwd_bwd", "chunk_budget_bytes": cap, "chunk_rows": plan["chunk_rows"],
+                    "chunks": plan["num_chunks"], "ms_per_step": ms, "tokens_per_s": wl.n / (ms * 1e-3),
+                    "mfma_pct_6ndv": 100.0 * 6.0 * wl.n * wl.d * wl.v / (ms * 1e-3) / (PEAK_TFLOPS[wl.dtype] * 1e12),
+                    "extra_device_bytes": peak, "memory_ratio": peak / logits_bytes_avoided(wl.n, wl.v)})
+        log(f"[bench] {wl.name} fused, chunk budget {cap >> 20} MiB ({plan['chunk_rows']} rows): {ms:.3f} ms/step, "
+            f"peak {peak / 1e6:.1f} MB ({out[-1]['memory_ratio']:.3f})")
     return out
 
 
@@ -248,8 +421,12 @@ def main() -> int:
     ap.add_argument("--config", default="llama3_8b_head")
     ap.add_argument("--cpu-rows", type=int, default=6144, help="tokens in the oracle's CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--all-configs", action="store_true",
-                    help="also time flce_fwd_bwd on every workload (inputs drawn per workload) and report each")
+    ap.add_argument("--no-per-config", action="store_true",
+                    help="skip the other four workloads (by default every workload is timed and reported)")
+    ap.add_argument("--no-parity", action="store_true",
+                    help="skip the comparison with the fp64 oracle (by default every workload is checked)")
+    ap.add_argument("--no-memory-sweep", action="store_true",
+                    help="skip the low-memory path and the chunk-budget sweep")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run a 1 GiB device copy (counter calibration), one step and one cross-entropy on "
                          "the workload's logits, print nothing else; meant to run under rocprofv3 --pmc "
@@ -274,18 +451,17 @@ def main() -> int:
     dev = torch.device("cuda:0")
     log(f"[bench] generating {wl.name}: n={wl.n} d={wl.d} v={wl.v} {wl.dtype}")
     h, w, y = make_inputs(wl)
-    hd, wd, yd = h.to(dev), w.to(dev), y.to(dev)
-    out = (torch.empty(1, dtype=torch.float32, device=dev), torch.empty(wl.n, dtype=torch.float32, device=dev),
-           torch.empty_like(hd), torch.empty_like(wd))
     plan = flce.flce_plan_info(wl.n, wl.d, wl.v, flce.FLCE_BF16 if wl.dtype == "bf16" else flce.FLCE_F32, 1)
     log(f"[bench] plan {plan}")
 
-    for i in range(args.warmup):
-        flce.linear_cross_entropy(hd, wd, yd, reduction=wl.reduction, out=out)
-    torch.cuda.synchronize()
-    log(f"[bench] {args.warmup} warm-up steps done")
-
     if args.traffic_probe:
+        hd, wd, yd = h.to(dev), w.to(dev), y.to(dev)
+        out = (torch.empty(1, dtype=torch.float32, device=dev), torch.empty(wl.n, dtype=torch.float32, device=dev),
+               torch.empty_like(hd), torch.empty_like(wd))
+        for i in range(args.warmup):
+            flce.linear_cross_entropy(hd, wd, yd, reduction=wl.reduction, out=out)
+        torch.cuda.synchronize()
+        log(f"[bench] {args.warmup} warm-up steps done")
         # A plain copy of exactly COPY_BYTES (read COPY_BYTES, write COPY_BYTES) calibrates
         # the FETCH_SIZE / WRITE_SIZE counters against a known byte count.
         src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
@@ -310,34 +486,13 @@ def main() -> int:
         log("[bench] traffic probe done")
         return 0
 
-    # peak extra device memory of one call
-    flce.flce_memory_high_water(reset=True)
-    flce.linear_cross_entropy(hd, wd, yd, reduction=wl.reduction, out=out)
-    torch.cuda.synchronize()
-    extra = flce.flce_memory_high_water()
-
     stream = torch.cuda.current_stream(dev)
-    flce.flce_profile_read()                 # clear
-    flce.flce_profile_enable(True)
-    torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    wall0 = time.perf_counter()
-    ev[0].record(stream)
-    for i in range(args.steps):
-        flce.linear_cross_entropy(hd, wd, yd, reduction=wl.reduction, out=out)
-        ev[i + 1].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    flce.flce_profile_enable(False)
-    kern = flce.flce_profile_read()
-    ms_total = ev[0].elapsed_time(ev[-1])
-    ms_step = ms_total / args.steps
-    per_step = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
-    ms_median = per_step[len(per_step) // 2] if len(per_step) % 2 else 0.5 * (
-        per_step[len(per_step) // 2 - 1] + per_step[len(per_step) // 2])
-    log(f"[bench] {args.steps} steps: {ms_step:.3f} ms/step (median {ms_median:.3f}, min {per_step[0]:.3f}; "
-        f"wall {wall:.2f} s); kernels {kern}")
-
+    # The headline: flce_fwd_bwd on this workload, timed without instrumentation, then a
+    # second, instrumented pass for the per-kernel split (the roofline's dominant kernel).
+    head, head_got, head_rows, head_cols, handles = measure_workload(flce, torch, wl, args, stream, h, w, y,
+                                                                     with_kernels=True)
+    kern = head["kernels"]
+    ms_step = head["ms_per_step"]
     flops_step = 6.0 * wl.n * wl.d * wl.v
     peak = PEAK_TFLOPS[wl.dtype]
     # dominant kernel: the contraction kind with the largest total time
@@ -346,17 +501,20 @@ def main() -> int:
     flops_launch = 2.0 * wl.n * wl.d * wl.v / plan["num_chunks"]      # 2*C*D*V per chunk launch (avg)
     dom_avg_ms = dom_ms / max(launches, 1)
     achieved = flops_launch / (dom_avg_ms * 1e-3) / 1e12
+    log(f"[bench] {args.steps} steps: {ms_step:.3f} ms/step uninstrumented (median {head['ms_median']:.3f}, "
+        f"min {head['ms_min']:.3f}), {head['ms_per_step_instrumented']:.3f} instrumented; kernels {kern}")
 
     result = {
         "metric": METRIC,
-        "value": wl.n * args.steps / (ms_total * 1e-3),
+        "value": head["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_step,
-        "ms_per_step_median": ms_median,
-        "ms_per_step_min": per_step[0],
+        "ms_per_step_median": head["ms_median"],
+        "ms_per_step_min": head["ms_min"],
+        "ms_per_step_instrumented": head["ms_per_step_instrumented"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -368,18 +526,30 @@ def main() -> int:
         "tflops": flops_step / (ms_step * 1e-3) / 1e12,
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                      "frac": achieved / peak, "traffic": measured_traffic(dom),
-                     "avg_launch_ms": dom_avg_ms, "flop_per_launch": flops_launch},
+                     "avg_launch_ms": dom_avg_ms, "flop_per_launch": flops_launch,
+                     "timing": "HIP events around each launch on the call's stream (instrumented pass)"},
         "kernels_ms_per_step": {k: v[1] / args.steps for k, v in kern.items() if v[0]},
-        "memory": {"extra_device_bytes": extra, "logits_bytes_avoided": logits_bytes_avoided(wl.n, wl.v),
-                   "ratio": extra / logits_bytes_avoided(wl.n, wl.v)},
+        "kernels_ms_per_launch": {k: v[1] / v[0] for k, v in kern.items() if v[0]},
+        "memory": {"extra_device_bytes": head["extra_device_bytes"],
+                   "pool_reserved_bytes": head["pool_reserved_bytes"],
+                   "logits_bytes_avoided": logits_bytes_avoided(wl.n, wl.v),
+                   "ratio": head["memory_ratio"]},
         "plan": plan,
     }
-    # The split path an autograd function uses: flce_fwd (loss, LSE) then flce_bwd
-    # (logits recomputed from the saved LSE), 8 N D V flop per step.
+    hd, wd, yd, out = handles
     dt_code = flce.FLCE_BF16 if wl.dtype == "bf16" else flce.FLCE_F32
     red_code = flce.FLCE_MEAN if wl.reduction == "mean" else flce.FLCE_SUM
     loss_s, lse_s, dh_s, dw_s = out
 
+    # The low-memory path and the memory/speed trade-off on this workload.
+    if not args.no_memory_sweep:
+        lm = lowmem_measure(flce, torch, wl, args, stream, hd, wd, yd, [None, 128 << 20, 512 << 20])
+        result["lowmem"] = lm[0]
+        result["memory_tradeoff"] = {"workload": wl.name, "points": fused_cap_measure(
+            flce, torch, wl, args, stream, hd, wd, yd, [1 << 30, 512 << 20, 256 << 20]) + lm}
+
+    # The split path an autograd function uses: flce_fwd (loss, LSE) then flce_bwd
+    # (logits recomputed from the saved LSE), 8 N D V flop per step.
     def split_step():
         st = flce.flce_fwd(hd, wd, yd, wl.n, wl.d, wl.v, dt_code, -100, red_code, loss_s, lse_s, stream)
         st = st or flce.flce_bwd(hd, wd, yd, lse_s, None, wl.n, wl.d, wl.v, dt_code, -100, red_code, dh_s, dw_s,
@@ -387,17 +557,8 @@ def main() -> int:
         if st != flce.FLCE_OK:
             raise flce.FlceError(st, "split step")
 
-    for _ in range(max(1, args.warmup)):
-        split_step()
-    torch.cuda.synchronize()
-    s0 = torch.cuda.Event(enable_timing=True)
-    s1 = torch.cuda.Event(enable_timing=True)
-    s0.record(stream)
-    for _ in range(args.steps):
-        split_step()
-    s1.record(stream)
-    torch.cuda.synchronize()
-    ms_split = s0.elapsed_time(s1) / args.steps
+    _, tot = time_steps(torch, split_step, stream, args.steps, max(1, args.warmup))
+    ms_split = tot / args.steps
     log(f"[bench] split fwd + bwd-from-LSE: {ms_split:.3f} ms/step")
     result["split_fwd_bwd"] = {
         "ms_per_step": ms_split,
@@ -406,21 +567,15 @@ def main() -> int:
         "mfma_pct_8ndv": 100.0 * 8.0 * wl.n * wl.d * wl.v / (ms_split * 1e-3) / (peak * 1e12),
         "path": "flce_fwd then flce_bwd (logits recomputed from the saved LSE)",
     }
+
     # the forward alone (loss and LSE), 2 N D V flop
     def fwd_only():
         st = flce.flce_fwd(hd, wd, yd, wl.n, wl.d, wl.v, dt_code, -100, red_code, loss_s, lse_s, stream)
         if st != flce.FLCE_OK:
             raise flce.FlceError(st, "flce_fwd")
 
-    for _ in range(max(1, args.warmup)):
-        fwd_only()
-    torch.cuda.synchronize()
-    s0.record(stream)
-    for _ in range(args.steps):
-        fwd_only()
-    s1.record(stream)
-    torch.cuda.synchronize()
-    ms_fwd = s0.elapsed_time(s1) / args.steps
+    _, tot = time_steps(torch, fwd_only, stream, args.steps, max(1, args.warmup))
+    ms_fwd = tot / args.steps
     log(f"[bench] forward only: {ms_fwd:.3f} ms/call")
     result["forward_only"] = {
         "ms_per_call": ms_fwd,
@@ -429,21 +584,15 @@ def main() -> int:
         "mfma_pct_2ndv": 100.0 * 2.0 * wl.n * wl.d * wl.v / (ms_fwd * 1e-3) / (peak * 1e12),
         "path": "flce_fwd (loss and LSE; logits statistics only)",
     }
+
     # vocabulary split in eight shards (the shard shape of an eight-way vocabulary-parallel
     # head): per shard the partial forward, the merge, per shard the backward from the merged
     # LSE, the sum of the dH terms; 8 N D V flop
     def split8():
         flce.linear_cross_entropy_vocab_split(hd, wd, yd, num_shards=8, reduction=wl.reduction)
 
-    for _ in range(max(1, args.warmup)):
-        split8()
-    torch.cuda.synchronize()
-    s0.record(stream)
-    for _ in range(args.steps):
-        split8()
-    s1.record(stream)
-    torch.cuda.synchronize()
-    ms_vs = s0.elapsed_time(s1) / args.steps
+    _, tot = time_steps(torch, split8, stream, args.steps, max(1, args.warmup))
+    ms_vs = tot / args.steps
     log(f"[bench] vocabulary split, 8 shards: {ms_vs:.3f} ms/step")
     result["vocab_split_8"] = {
         "ms_per_step": ms_vs,
@@ -455,8 +604,36 @@ def main() -> int:
     }
     result["forward_fp8"] = fp8_forward_measure(flce, torch, wl, args, stream)
     result["ce_logits"] = ce_logits_measure(flce, torch, hd, wd, yd, wl, args, stream)
-    if args.all_configs:
-        result["per_config"] = all_configs_measure(flce, torch, args, stream)
+    del hd, wd, yd, out, loss_s, lse_s, dh_s, dw_s, handles
+    torch.cuda.empty_cache()
+
+    # Every workload: flce_fwd_bwd timed the same way; results kept on the host for parity.
+    pending = [(wl, h, w, y, head_got, head_rows, head_cols)]
+    per_config = {wl.name: {k: v for k, v in head.items() if k not in ("kernels",)}}
+    if not args.no_per_config:
+        for name, other in CONFIGS.items():
+            if name == wl.name:
+                continue
+            log(f"[bench] generating {name}: n={other.n} d={other.d} v={other.v} {other.dtype}")
+            ho, wo, yo = make_inputs(other)
+            res, got, rows, cols, hh = measure_workload(flce, torch, other, args, stream, ho, wo, yo)
+            del hh
+            torch.cuda.empty_cache()
+            per_config[name] = res
+            pending.append((other, ho, wo, yo, got, rows, cols))
+    result["per_config"] = per_config
+
+    # Parity against the fp64 oracle (host cores), after all GPU timing.
+    if not args.no_parity:
+        workers = min(16, len(os.sched_getaffinity(0)))
+        for owl, ho, wo, yo, got, rows, cols in pending:
+            par = parity_against_oracle(owl, ho, wo, yo, got, rows, cols, workers)
+            per_config[owl.name]["parity"] = par
+            log(f"[bench] parity {owl.name}: loss {par['loss_rel']:.2e}, lse {par['lse_max_rel']:.2e}, "
+                f"dH {par['dh_rel_sampled']:.2e}, dW {par['dw_rel_sampled']:.2e} ({par['oracle_s']:.1f} s)")
+        result["parity"] = per_config[wl.name]["parity"]
+    del pending
+
     if not args.no_cpu_baseline:
         log(f"[bench] CPU baseline: oracle on {args.cpu_rows} rows")
         result["cpu_baseline"] = cpu_baseline(wl, h, w, y, args.cpu_rows)

@@ -68,6 +68,9 @@
  * FLCE_GROUP_DH, FLCE_GROUP_DW (tile-order group sizes of the three
  * contractions on the bf16 engine).  Results stay within the
  * stated tolerances under any of them; bitwise results can change.
+ * FLCE_TEST_ALLOC_LIMIT_BYTES is a test hook: a workspace request above that
+ * many bytes fails as an allocation failure would (FLCE_ERR_OOM, nothing
+ * enqueued, nothing written).
  */
 #ifndef FLCE_H_
 #define FLCE_H_

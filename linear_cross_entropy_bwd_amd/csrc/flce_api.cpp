@@ -192,6 +192,20 @@ hipError_t device_pool(int dev, hipMemPool_t* out) {
   return hipSuccess;
 }
 
+// A stream-ordered workspace from the device's pool; false when it cannot be had.
+// FLCE_TEST_ALLOC_LIMIT_BYTES (a test hook) makes every request above that many
+// bytes fail here, before anything is enqueued, as a real allocation failure would.
+bool pool_alloc(void** base, size_t bytes, hipMemPool_t pool, hipStream_t stream) {
+  *base = nullptr;
+  const int64_t limit = env_i64("FLCE_TEST_ALLOC_LIMIT_BYTES", 0);
+  if (limit > 0 && bytes > static_cast<size_t>(limit)) return false;
+  if (hipMallocFromPoolAsync(base, bytes, pool, stream) != hipSuccess || *base == nullptr) {
+    (void)hipGetLastError();
+    return false;
+  }
+  return true;
+}
+
 // ---- timing instrumentation -------------------------------------------------------
 
 struct Prof {
@@ -405,10 +419,7 @@ int with_workspace(const Plan& p, hipStream_t stream, Body&& body) {
   hipMemPool_t pool;
   if (device_pool(dev, &pool) != hipSuccess) return FLCE_ERR_HIP;
   void* base = nullptr;
-  if (hipMallocFromPoolAsync(&base, p.total, pool, stream) != hipSuccess || base == nullptr) {
-    (void)hipGetLastError();
-    return FLCE_ERR_OOM;
-  }
+  if (!pool_alloc(&base, p.total, pool, stream)) return FLCE_ERR_OOM;
   const Work wk = carve(p, static_cast<char*>(base));
   hipError_t e = body(wk);
   hipError_t f = hipFreeAsync(base, stream);
@@ -572,10 +583,7 @@ int call_ce_logits(const void* logits, const int64_t* labels, int64_t n, int64_t
   const size_t off_lse = off_loss + ((sizeof(float) * static_cast<size_t>(n) + kAlign - 1) / kAlign) * kAlign;
   const size_t total = off_lse + sizeof(float) * static_cast<size_t>(n);
   void* base = nullptr;
-  if (hipMallocFromPoolAsync(&base, total, pool, stream) != hipSuccess || base == nullptr) {
-    (void)hipGetLastError();
-    return FLCE_ERR_OOM;
-  }
+  if (!pool_alloc(&base, total, pool, stream)) return FLCE_ERR_OOM;
   char* b = static_cast<char*>(base);
   CeArgs a;
   a.logits = logits;
@@ -760,10 +768,7 @@ int call_merge_shards(const float* lse_parts, const float* zy_parts, int64_t num
   const size_t off_lse = off_loss + align_up(sizeof(float) * static_cast<size_t>(n));
   const size_t total = off_lse + sizeof(float) * static_cast<size_t>(n);
   void* base = nullptr;
-  if (hipMallocFromPoolAsync(&base, total, pool, stream) != hipSuccess || base == nullptr) {
-    (void)hipGetLastError();
-    return FLCE_ERR_OOM;
-  }
+  if (!pool_alloc(&base, total, pool, stream)) return FLCE_ERR_OOM;
   char* b = static_cast<char*>(base);
   int32_t* nvalid = reinterpret_cast<int32_t*>(b);
   float* loss_rows = reinterpret_cast<float*>(b + off_loss);
