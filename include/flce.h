@@ -96,7 +96,8 @@ enum {
                                 size overflow */
   FLCE_ERR_ALIGNMENT = -2,   /* pointer or row pitch not aligned as documented above */
   FLCE_ERR_OOM = -3,         /* workspace allocation failed */
-  FLCE_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed */
+  FLCE_ERR_HIP = -4,         /* a HIP runtime call or kernel launch failed */
+  FLCE_ERR_SCRATCH = -5      /* flce_fwd_noalloc: the sizes need more than its fixed scratch area */
 };
 
 /*
@@ -133,6 +134,26 @@ int flce_fwd(const void* h, const void* w, const int64_t* labels,
              int64_t n, int64_t d, int64_t v, flce_dtype dtype,
              int64_t ignore_index, flce_reduction reduction,
              float* loss_out, float* lse_out, hipStream_t stream);
+
+/*
+ * flce_fwd without any allocation, for callers that cannot allocate device
+ * memory during the call: code being captured into a HIP graph, tight serving
+ * or scoring loops, harnesses that forbid allocation.  Same arguments, results
+ * and errors as flce_fwd (loss and LSE bitwise equal to it), but the workspace
+ * is a fixed scratch area of FLCE_NOALLOC_SCRATCH_BYTES (64 MiB) of device
+ * memory that the library holds on each device it runs on until the process
+ * ends; the chunk of token rows per launch shrinks until the workspace fits.
+ * Sizes that need more than the area even at the smallest chunk (about
+ * 8 n + 8 ceil(v / 128) * 16 bytes) return FLCE_ERR_SCRATCH before anything
+ * is enqueued.  Every call on one device shares that device's area: calls
+ * that overlap on one GPU (different streams, or different host threads
+ * without ordering) race on it and must be serialised by the caller.
+ */
+#define FLCE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int flce_fwd_noalloc(const void* h, const void* w, const int64_t* labels,
+                     int64_t n, int64_t d, int64_t v, flce_dtype dtype,
+                     int64_t ignore_index, flce_reduction reduction,
+                     float* loss_out, float* lse_out, hipStream_t stream);
 
 /*
  * Low-memory variant of flce_fwd_bwd: the same loss, LSE and gradients (same

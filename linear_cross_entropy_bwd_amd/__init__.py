@@ -20,12 +20,15 @@ LIB_PATH = os.path.join(PKG, "libflce.so")
 FLCE_BF16, FLCE_F32 = 0, 1
 FLCE_MEAN, FLCE_SUM = 0, 1
 FLCE_OK, FLCE_ERR_INVALID_ARG, FLCE_ERR_ALIGNMENT, FLCE_ERR_OOM, FLCE_ERR_HIP = 0, -1, -2, -3, -4
+FLCE_ERR_SCRATCH = -5
+FLCE_NOALLOC_SCRATCH_BYTES = 64 << 20
 ENGINE_MFMA, ENGINE_FMA = 0, 1
 
 EXPORTED = (
     "flce_fwd_bwd",
     "flce_fwd_bwd_lowmem",
     "flce_fwd",
+    "flce_fwd_noalloc",
     "flce_bwd",
     "flce_ce_logits",
     "flce_fwd_fp8",
@@ -113,6 +116,8 @@ def lib() -> ctypes.CDLL:
     L.flce_pool_trim.restype = i32
     L.flce_fwd.argtypes = [p, p, p, i64, i64, i64, i32, i64, i32, p, p, p]
     L.flce_fwd.restype = i32
+    L.flce_fwd_noalloc.argtypes = [p, p, p, i64, i64, i64, i32, i64, i32, p, p, p]
+    L.flce_fwd_noalloc.restype = i32
     L.flce_bwd.argtypes = [p, p, p, p, p, i64, i64, i64, i32, i64, i32, p, p, p]
     L.flce_bwd.restype = i32
     L.flce_ce_logits.argtypes = [p, p, i64, i64, i32, i64, i32, p, p, p, p, p, p]
@@ -188,6 +193,11 @@ def flce_fwd_bwd_lowmem(h, w, labels, n, d, v, dtype, ignore_index, reduction, l
 def flce_fwd(h, w, labels, n, d, v, dtype, ignore_index, reduction, loss_out, lse_out, stream) -> int:
     return lib().flce_fwd(_ptr(h), _ptr(w), _ptr(labels), n, d, v, dtype, ignore_index, reduction,
                           _ptr(loss_out), _ptr(lse_out), _stream(stream))
+
+
+def flce_fwd_noalloc(h, w, labels, n, d, v, dtype, ignore_index, reduction, loss_out, lse_out, stream) -> int:
+    return lib().flce_fwd_noalloc(_ptr(h), _ptr(w), _ptr(labels), n, d, v, dtype, ignore_index, reduction,
+                                  _ptr(loss_out), _ptr(lse_out), _stream(stream))
 
 
 def flce_bwd(h, w, labels, lse, grad_out, n, d, v, dtype, ignore_index, reduction, dh_out, dw_out, stream) -> int:

@@ -558,6 +558,31 @@ int call_lowmem(const void* h, const void* w, const int64_t* labels, int64_t n, 
   });
 }
 
+// Forward-only call in a workspace the caller provides (no allocation): the
+// forward plan's chunk shrinks until its workspace fits `ws_bytes`;
+// FLCE_ERR_SCRATCH when even the smallest chunk does not.
+int call_fwd_in(const void* h, const void* w, const int64_t* labels, int64_t n, int64_t d, int64_t v,
+                flce_dtype dtype, int64_t ignore_index, flce_reduction reduction, float* loss_out, float* lse_out,
+                void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_common(h, w, labels, n, d, v, dtype, reduction, loss_out, lse_out);
+  if (st != FLCE_OK) return st;
+  if (ws == nullptr) return FLCE_ERR_INVALID_ARG;
+  Plan p;
+  int64_t budget = static_cast<int64_t>(ws_bytes);
+  for (;;) {
+    st = make_plan(n, d, v, dtype, 0, &p, 1, budget);
+    if (st != FLCE_OK) return st;
+    if (p.total <= ws_bytes) break;
+    // shrink the partials' budget by the excess plus one 16-row step of partials
+    const int64_t step = static_cast<int64_t>(p.total - ws_bytes) + p.ngroups * 8 * 16;
+    if (p.chunk <= 16 || budget <= step) return FLCE_ERR_SCRATCH;
+    budget -= step;
+  }
+  const Work wk = carve(p, static_cast<char*>(ws));
+  hipError_t e = run(p, wk, h, w, labels, ignore_index, reduction, loss_out, lse_out, nullptr, nullptr, stream);
+  return e == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
+}
+
 int call_ce_logits(const void* logits, const int64_t* labels, int64_t n, int64_t v, flce_dtype dtype,
                    int64_t ignore_index, flce_reduction reduction, const float* lse_in, const float* grad_scale,
                    float* loss_out, float* lse_out, void* grad_out, hipStream_t stream) {
@@ -816,6 +841,13 @@ int call_sum_parts(const float* parts, int64_t num_parts, int64_t count, flce_dt
 }
 
 }  // namespace
+
+int fwd_in_workspace(const void* h, const void* w, const int64_t* labels, int64_t n, int64_t d, int64_t v,
+                     flce_dtype dtype, int64_t ignore_index, flce_reduction reduction, float* loss_out,
+                     float* lse_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return call_fwd_in(h, w, labels, n, d, v, dtype, ignore_index, reduction, loss_out, lse_out, ws, ws_bytes, stream);
+}
+
 }  // namespace flce
 
 extern "C" {
@@ -945,6 +977,7 @@ const char* flce_strerror(int status) {
     case FLCE_ERR_ALIGNMENT: return "misaligned pointer or row pitch (rows must start on 16-byte boundaries)";
     case FLCE_ERR_OOM: return "workspace allocation failed";
     case FLCE_ERR_HIP: return "HIP runtime or kernel launch error";
+    case FLCE_ERR_SCRATCH: return "problem too large for the fixed scratch area of flce_fwd_noalloc";
     default: return "unknown status";
   }
 }

@@ -61,6 +61,12 @@ struct LowmemPlan {
 };
 int make_lowmem_plan(int64_t n, int64_t d, int64_t v, int32_t dtype, LowmemPlan* lp);
 
+// Forward only (flce_fwd) inside a workspace of ws_bytes at ws, allocating nothing;
+// FLCE_ERR_SCRATCH when the sizes need more.
+int fwd_in_workspace(const void* h, const void* w, const int64_t* labels, int64_t n, int64_t d, int64_t v,
+                     flce_dtype dtype, int64_t ignore_index, flce_reduction reduction, float* loss_out,
+                     float* lse_out, void* ws, size_t ws_bytes, hipStream_t stream);
+
 // Pointers into the workspace for one call.
 struct Work {
   char* base;        // the call's whole workspace
