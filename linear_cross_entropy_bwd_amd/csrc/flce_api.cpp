@@ -115,11 +115,18 @@ int make_plan(int64_t n, int64_t d, int64_t v, int32_t dtype, int32_t with_bwd, 
     const int64_t tiles = ((q.chunk + tm - 1) / tm) * ((d + tm - 1) / tm);
     int64_t smax = q.vp / (mfma ? 4096 : 256);
     if (smax > (mfma ? 8 : 16)) smax = mfma ? 8 : 16;
-    // the fp32 partials ([S][C][d]) stay within half of the chunk buffer's bytes,
-    // so that they never dominate the workspace
+    // the fp32 partials ([S][C][d]) stay within the chunk buffer's bytes, and the
+    // whole workspace below the fp32 [n, v] logits the method avoids (the chunk
+    // buffer, the group partials and the per-row arrays taken into account)
     const int64_t part_bytes = q.chunk * d * 4;
-    const int64_t s_bytes = (q.chunk * q.vp * prob_elem / 2) / part_bytes;
+    int64_t s_bytes = (q.chunk * q.vp * prob_elem) / part_bytes;
+    const int64_t others = q.chunk * q.vp * prob_elem + 8 * q.ngroups * q.chunk + 16 * n + 16 * q.chunk + 4096;
+    if (mul_ok(n, v) && n * v * 4 > others) {
+      const int64_t s_fit = (n * v * 4 - others) / part_bytes;
+      if (s_fit < s_bytes) s_bytes = s_fit;
+    }
     if (smax > s_bytes) smax = s_bytes < 1 ? 1 : s_bytes;
+    if (whole_rows) smax = 1;  // a vocabulary slice of the low-memory path: no partials
     int64_t s = best_splits(tiles, kCus, smax);
     s = env_i64("FLCE_DH_SPLITS", s);
     if (s > q.vp / 64) s = q.vp / 64;  // every split keeps at least one 64-column stage
