@@ -427,11 +427,17 @@ def main() -> int:
                     help="skip the comparison with the fp64 oracle (by default every workload is checked)")
     ap.add_argument("--no-memory-sweep", action="store_true",
                     help="skip the low-memory path and the chunk-budget sweep")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="time only the headline workload's flce_fwd_bwd (no other entry points, workloads "
+                         "or sweeps), so that a profiler's per-kernel averages cover the headline launches "
+                         "alone")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run a 1 GiB device copy (counter calibration), one step and one cross-entropy on "
                          "the workload's logits, print nothing else; meant to run under rocprofv3 --pmc "
                          "FETCH_SIZE / WRITE_SIZE")
     args = ap.parse_args()
+    if args.headline_only:
+        args.no_per_config = args.no_memory_sweep = True
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the fused linear cross-entropy path here has no multi-GPU "
@@ -548,62 +554,64 @@ def main() -> int:
         result["memory_tradeoff"] = {"workload": wl.name, "points": fused_cap_measure(
             flce, torch, wl, args, stream, hd, wd, yd, [1 << 30, 512 << 20, 256 << 20]) + lm}
 
-    # The split path an autograd function uses: flce_fwd (loss, LSE) then flce_bwd
-    # (logits recomputed from the saved LSE), 8 N D V flop per step.
-    def split_step():
-        st = flce.flce_fwd(hd, wd, yd, wl.n, wl.d, wl.v, dt_code, -100, red_code, loss_s, lse_s, stream)
-        st = st or flce.flce_bwd(hd, wd, yd, lse_s, None, wl.n, wl.d, wl.v, dt_code, -100, red_code, dh_s, dw_s,
-                                 stream)
-        if st != flce.FLCE_OK:
-            raise flce.FlceError(st, "split step")
+    # The other entry points on this workload (skipped with --headline-only).
+    if not args.headline_only:
+        # The split path an autograd function uses: flce_fwd (loss, LSE) then flce_bwd
+        # (logits recomputed from the saved LSE), 8 N D V flop per step.
+        def split_step():
+            st = flce.flce_fwd(hd, wd, yd, wl.n, wl.d, wl.v, dt_code, -100, red_code, loss_s, lse_s, stream)
+            st = st or flce.flce_bwd(hd, wd, yd, lse_s, None, wl.n, wl.d, wl.v, dt_code, -100, red_code, dh_s, dw_s,
+                                     stream)
+            if st != flce.FLCE_OK:
+                raise flce.FlceError(st, "split step")
 
-    _, tot = time_steps(torch, split_step, stream, args.steps, max(1, args.warmup))
-    ms_split = tot / args.steps
-    log(f"[bench] split fwd + bwd-from-LSE: {ms_split:.3f} ms/step")
-    result["split_fwd_bwd"] = {
-        "ms_per_step": ms_split,
-        "tokens_per_s": wl.n / (ms_split * 1e-3),
-        "tflops_8ndv": 8.0 * wl.n * wl.d * wl.v / (ms_split * 1e-3) / 1e12,
-        "mfma_pct_8ndv": 100.0 * 8.0 * wl.n * wl.d * wl.v / (ms_split * 1e-3) / (peak * 1e12),
-        "path": "flce_fwd then flce_bwd (logits recomputed from the saved LSE)",
-    }
+        _, tot = time_steps(torch, split_step, stream, args.steps, max(1, args.warmup))
+        ms_split = tot / args.steps
+        log(f"[bench] split fwd + bwd-from-LSE: {ms_split:.3f} ms/step")
+        result["split_fwd_bwd"] = {
+            "ms_per_step": ms_split,
+            "tokens_per_s": wl.n / (ms_split * 1e-3),
+            "tflops_8ndv": 8.0 * wl.n * wl.d * wl.v / (ms_split * 1e-3) / 1e12,
+            "mfma_pct_8ndv": 100.0 * 8.0 * wl.n * wl.d * wl.v / (ms_split * 1e-3) / (peak * 1e12),
+            "path": "flce_fwd then flce_bwd (logits recomputed from the saved LSE)",
+        }
 
-    # the forward alone (loss and LSE), 2 N D V flop
-    def fwd_only():
-        st = flce.flce_fwd(hd, wd, yd, wl.n, wl.d, wl.v, dt_code, -100, red_code, loss_s, lse_s, stream)
-        if st != flce.FLCE_OK:
-            raise flce.FlceError(st, "flce_fwd")
+        # the forward alone (loss and LSE), 2 N D V flop
+        def fwd_only():
+            st = flce.flce_fwd(hd, wd, yd, wl.n, wl.d, wl.v, dt_code, -100, red_code, loss_s, lse_s, stream)
+            if st != flce.FLCE_OK:
+                raise flce.FlceError(st, "flce_fwd")
 
-    _, tot = time_steps(torch, fwd_only, stream, args.steps, max(1, args.warmup))
-    ms_fwd = tot / args.steps
-    log(f"[bench] forward only: {ms_fwd:.3f} ms/call")
-    result["forward_only"] = {
-        "ms_per_call": ms_fwd,
-        "tokens_per_s": wl.n / (ms_fwd * 1e-3),
-        "tflops_2ndv": 2.0 * wl.n * wl.d * wl.v / (ms_fwd * 1e-3) / 1e12,
-        "mfma_pct_2ndv": 100.0 * 2.0 * wl.n * wl.d * wl.v / (ms_fwd * 1e-3) / (peak * 1e12),
-        "path": "flce_fwd (loss and LSE; logits statistics only)",
-    }
+        _, tot = time_steps(torch, fwd_only, stream, args.steps, max(1, args.warmup))
+        ms_fwd = tot / args.steps
+        log(f"[bench] forward only: {ms_fwd:.3f} ms/call")
+        result["forward_only"] = {
+            "ms_per_call": ms_fwd,
+            "tokens_per_s": wl.n / (ms_fwd * 1e-3),
+            "tflops_2ndv": 2.0 * wl.n * wl.d * wl.v / (ms_fwd * 1e-3) / 1e12,
+            "mfma_pct_2ndv": 100.0 * 2.0 * wl.n * wl.d * wl.v / (ms_fwd * 1e-3) / (peak * 1e12),
+            "path": "flce_fwd (loss and LSE; logits statistics only)",
+        }
 
-    # vocabulary split in eight shards (the shard shape of an eight-way vocabulary-parallel
-    # head): per shard the partial forward, the merge, per shard the backward from the merged
-    # LSE, the sum of the dH terms; 8 N D V flop
-    def split8():
-        flce.linear_cross_entropy_vocab_split(hd, wd, yd, num_shards=8, reduction=wl.reduction)
+        # vocabulary split in eight shards (the shard shape of an eight-way vocabulary-parallel
+        # head): per shard the partial forward, the merge, per shard the backward from the merged
+        # LSE, the sum of the dH terms; 8 N D V flop
+        def split8():
+            flce.linear_cross_entropy_vocab_split(hd, wd, yd, num_shards=8, reduction=wl.reduction)
 
-    _, tot = time_steps(torch, split8, stream, args.steps, max(1, args.warmup))
-    ms_vs = tot / args.steps
-    log(f"[bench] vocabulary split, 8 shards: {ms_vs:.3f} ms/step")
-    result["vocab_split_8"] = {
-        "ms_per_step": ms_vs,
-        "tokens_per_s": wl.n / (ms_vs * 1e-3),
-        "tflops_8ndv": 8.0 * wl.n * wl.d * wl.v / (ms_vs * 1e-3) / 1e12,
-        "mfma_pct_8ndv": 100.0 * 8.0 * wl.n * wl.d * wl.v / (ms_vs * 1e-3) / (peak * 1e12),
-        "shards": flce.vocab_shard_bounds(wl.v, 8),
-        "path": "flce_fwd_shard x8, flce_merge_shards, flce_bwd_shard x8, flce_sum_parts",
-    }
-    result["forward_fp8"] = fp8_forward_measure(flce, torch, wl, args, stream)
-    result["ce_logits"] = ce_logits_measure(flce, torch, hd, wd, yd, wl, args, stream)
+        _, tot = time_steps(torch, split8, stream, args.steps, max(1, args.warmup))
+        ms_vs = tot / args.steps
+        log(f"[bench] vocabulary split, 8 shards: {ms_vs:.3f} ms/step")
+        result["vocab_split_8"] = {
+            "ms_per_step": ms_vs,
+            "tokens_per_s": wl.n / (ms_vs * 1e-3),
+            "tflops_8ndv": 8.0 * wl.n * wl.d * wl.v / (ms_vs * 1e-3) / 1e12,
+            "mfma_pct_8ndv": 100.0 * 8.0 * wl.n * wl.d * wl.v / (ms_vs * 1e-3) / (peak * 1e12),
+            "shards": flce.vocab_shard_bounds(wl.v, 8),
+            "path": "flce_fwd_shard x8, flce_merge_shards, flce_bwd_shard x8, flce_sum_parts",
+        }
+        result["forward_fp8"] = fp8_forward_measure(flce, torch, wl, args, stream)
+        result["ce_logits"] = ce_logits_measure(flce, torch, hd, wd, yd, wl, args, stream)
     del hd, wd, yd, out, loss_s, lse_s, dh_s, dw_s, handles
     torch.cuda.empty_cache()
 
