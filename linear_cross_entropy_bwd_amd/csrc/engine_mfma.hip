@@ -298,6 +298,12 @@ __device__ __forceinline__ bf16_t (*ring())[kStageElems] {
 }
 constexpr int kWaveScratchBytes = 8192;
 
+// Placement inside one k-step of 16 MFMAs: fragment read f (A 0..3, then B
+// 0..3) of the next k-step and direct load q issue after MFMA kReadAfter[f] and
+// kLoadAfter[q] of the current one.
+constexpr int kReadAfter[8] = {0, 1, 2, 3, 4, 5, 6, 7};
+constexpr int kLoadAfter[4] = {8, 9, 10, 11};
+
 // Instruction-class masks of __builtin_amdgcn_sched_group_barrier.
 constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100;
 
@@ -393,6 +399,36 @@ __device__ __forceinline__ void tile_loop(const Operand& A, const Operand& B, in
       }
   };
   auto next = [](int s, int d) { return s + d >= kSlots ? s + d - kSlots : s + d; };
+  // One k-step: the 16 MFMAs on `cur` (when MMA), with the 8 fragment reads of
+  // k-step KS into `nxt` and the direct loads load(0..3) placed between them
+  // as kReadAfter / kLoadAfter say.  Scheduling barriers pin this order:
+  // the scheduler sees no LDS read in the transpose reads' inline assembly
+  // and would otherwise bunch them behind the MFMAs, leaving the next
+  // k-step's wait uncovered.
+  auto phase = [&](auto mma_on, const Frags& cur, Frags& nxt, int sa_, int sb_, auto ks, auto&& load) {
+    constexpr bool MMA = decltype(mma_on)::value;
+    constexpr int KS = decltype(ks)::value;
+    const uint32_t slot_a = lds0 + sa_ * kStageElems * 2, slot_b = lds0 + sb_ * kStageElems * 2;
+    static_for<16>([&](auto mc) {
+      constexpr int m = decltype(mc)::value;
+      if constexpr (MMA)
+        acc.c[m / 4][m % 4] =
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.a[m / 4], cur.b[m % 4], acc.c[m / 4][m % 4], 0, 0, 0);
+      static_for<8>([&](auto fc) {
+        constexpr int f = decltype(fc)::value;
+        if constexpr (kReadAfter[f] == m) {
+          if constexpr (f < 4)
+            nxt.a[f] = read_frag<A_KMAJ, KS>(lds[sa_], slot_a, foa, f);
+          else
+            nxt.b[f - 4] = read_frag<B_KMAJ, KS>(lds[sb_], slot_b, fob, f - 4);
+        }
+      });
+      static_for<4>([&](auto qc) {
+        if constexpr (kLoadAfter[decltype(qc)::value] == m) load(qc);
+      });
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
 
   // Prologue: A_0, B_0, A_1 in flight; wait for A_0 and B_0.
   load_stage<0, kLoadsPerStage, A_KMAJ>(A, m0, k_of(0), lds[0], offa);
@@ -410,42 +446,40 @@ __device__ __forceinline__ void tile_loop(const Operand& A, const Operand& B, in
   auto body = [&](int64_t j, auto first, auto fast) {
     constexpr bool kFirst = decltype(first)::value;
     constexpr bool kFast = decltype(fast)::value;
-    constexpr int kPrevMfma = kFirst ? 0 : 16;
     bf16_t* slot_b = lds[next(sb, 2)];  // B_{j+1}: slot of A_{j-1}
     bf16_t* slot_a = lds[next(sa, 4)];  // A_{j+2}: slot of B_{j-1}
     const int64_t kb = k_of(j + 1), ka = k_of(j + 2);
-    auto load_b = [&](auto i0) {
-      if constexpr (kFast)
-        load_stage_fast<decltype(i0)::value, 4, B_KMAJ>(B, n0, kb, slot_b, offb);
-      else
-        load_stage<decltype(i0)::value, 4, B_KMAJ>(B, n0, kb, slot_b, offb);
+    // direct load I0 + q of B_{j+1} / A_{j+2}, one per call
+    auto load_b_at = [&](auto i0) {
+      return [&, i0](auto q) {
+        constexpr int I = decltype(i0)::value + decltype(q)::value;
+        if constexpr (kFast)
+          load_stage_fast<I, 1, B_KMAJ>(B, n0, kb, slot_b, offb);
+        else
+          load_stage<I, 1, B_KMAJ>(B, n0, kb, slot_b, offb);
+      };
     };
-    auto load_a = [&](auto i0) {
-      if constexpr (kFast)
-        load_stage_fast<decltype(i0)::value, 4, A_KMAJ>(A, m0, ka, slot_a, offa);
-      else
-        load_stage<decltype(i0)::value, 4, A_KMAJ>(A, m0, ka, slot_a, offa);
+    auto load_a_at = [&](auto i0) {
+      return [&, i0](auto q) {
+        constexpr int I = decltype(i0)::value + decltype(q)::value;
+        if constexpr (kFast)
+          load_stage_fast<I, 1, A_KMAJ>(A, m0, ka, slot_a, offa);
+        else
+          load_stage<I, 1, A_KMAJ>(A, m0, ka, slot_a, offa);
+      };
     };
+    auto load_b0 = load_b_at(std::integral_constant<int, 0>{});
+    auto load_b4 = load_b_at(std::integral_constant<int, 4>{});
+    auto load_a0 = load_a_at(std::integral_constant<int, 0>{});
+    auto load_a4 = load_a_at(std::integral_constant<int, 4>{});
     if constexpr (!kFirst) wait_frags<A_KMAJ, B_KMAJ>(f1);
-    read(sa, sb, std::integral_constant<int, 0>{}, f0);
-    if constexpr (!kFirst) mma(f1);
-    load_b(std::integral_constant<int, 0>{});
-    interleave_hint<kPrevMfma, kReads>();
+    phase(std::bool_constant<!kFirst>{}, f1, f0, sa, sb, std::integral_constant<int, 0>{}, load_b0);
     wait_frags<A_KMAJ, B_KMAJ>(f0);
-    read(sa, sb, std::integral_constant<int, 1>{}, f1);
-    mma(f0);
-    load_b(std::integral_constant<int, 4>{});
-    interleave_hint<16, kReads>();
+    phase(std::true_type{}, f0, f1, sa, sb, std::integral_constant<int, 1>{}, load_b4);
     wait_frags<A_KMAJ, B_KMAJ>(f1);
-    read(sa, sb, std::integral_constant<int, 2>{}, f0);
-    mma(f1);
-    load_a(std::integral_constant<int, 0>{});
-    interleave_hint<16, kReads>();
+    phase(std::true_type{}, f1, f0, sa, sb, std::integral_constant<int, 2>{}, load_a0);
     wait_frags<A_KMAJ, B_KMAJ>(f0);
-    read(sa, sb, std::integral_constant<int, 3>{}, f1);
-    mma(f0);
-    load_a(std::integral_constant<int, 4>{});
-    interleave_hint<16, kReads>();
+    phase(std::true_type{}, f0, f1, sa, sb, std::integral_constant<int, 3>{}, load_a4);
     wait_stages(1);
     stage_barrier();
     sa = next(sa, 2);
