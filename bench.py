@@ -14,7 +14,8 @@ matrix-peak fraction, extra device memory against the N V 4 bytes of logits
 avoided, and parity against the fp64 oracle), the parity of the headline
 workload, the low-memory path and a memory/speed sweep, the other entry
 points (split forward/backward, forward only, vocabulary split, FP8,
-cross-entropy on given logits) and the oracle's CPU baseline.
+cross-entropy on given logits), torch's hipBLASLt products on the same
+contraction shapes for context, and the oracle's CPU baseline.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
@@ -352,6 +353,42 @@ def fp8_backward_measure(flce, torch, wl, args, stream, inputs):
             "flop": "2NDV fp8 (logits recompute) + 4NDV bf16 (dH, dW)"}
 
 
+def vendor_gemm_measure(torch, hd, wd, yd, wl, args, stream, chunk):
+    """torch's own bf16 matrix products (hipBLASLt) on the three contraction shapes of
+    one chunk of `chunk` tokens: Z = H_c W^T, dH_c = G W and dW = G^T H_c, with G the
+    real softmax-minus-one-hot gradient of that chunk.  Context for the library's
+    contraction kernels on the same chip and clock limits, not a path of the library."""
+    c = min(chunk, wl.n)
+    hc = hd[:c].contiguous()
+    z = torch.matmul(hc, wd.t())
+    g = torch.softmax(z.float(), dim=-1)
+    yc = yd[:c]
+    keep = yc != -100
+    rows = torch.arange(c, device=hd.device)[keep]
+    g[rows, yc[keep]] -= 1.0
+    g = (g / max(1, int((yd != -100).sum()))).to(z.dtype)
+    gt = g.t().contiguous()                    # dW's left operand, laid out as the library reads it
+    flop = 2.0 * c * wl.d * wl.v
+    peak = PEAK_TFLOPS[wl.dtype]
+    res = {"chunk_rows": c, "flop_per_product": flop, "library": "torch.matmul (hipBLASLt)",
+           "g": "softmax(H_c W^T) minus one-hot, divided by the valid-token count, bf16"}
+    prods = {"logits_z": lambda: torch.matmul(hc, wd.t()),
+             "dh_gw": lambda: torch.matmul(g, wd),
+             "dw_gth": lambda: torch.matmul(gt, hc)}
+    total = 0.0
+    for name, fn in prods.items():
+        _, tot = time_steps(torch, fn, stream, args.steps, max(1, args.warmup))
+        ms = tot / args.steps
+        total += ms
+        res[name] = {"ms": ms, "tflops": flop / (ms * 1e-3) / 1e12, "frac": flop / (ms * 1e-3) / (peak * 1e12)}
+        log(f"[bench] hipBLASLt {name}: {ms:.3f} ms ({res[name]['tflops']:.0f} TFLOP/s, "
+            f"{100 * res[name]['frac']:.1f}% of peak)")
+    res["three_products_ms"] = total
+    res["frac_three_products"] = 3 * flop / (total * 1e-3) / (peak * 1e12)
+    del z, g, gt, hc
+    return res
+
+
 def ce_logits_measure(flce, torch, hd, wd, yd, wl, args, stream):
     """Cross-entropy on materialised logits (flce_ce_logits) for this workload's
     logits Z = H W^T: forward only, forward + gradient into a separate buffer,
@@ -612,6 +649,7 @@ def main() -> int:
         }
         result["forward_fp8"] = fp8_forward_measure(flce, torch, wl, args, stream)
         result["ce_logits"] = ce_logits_measure(flce, torch, hd, wd, yd, wl, args, stream)
+        result["vendor_gemm"] = vendor_gemm_measure(torch, hd, wd, yd, wl, args, stream, plan["chunk_rows"])
     del hd, wd, yd, out, loss_s, lse_s, dh_s, dw_s, handles
     torch.cuda.empty_cache()
 
