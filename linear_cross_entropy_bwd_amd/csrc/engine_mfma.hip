@@ -43,7 +43,6 @@ constexpr int TM = 256;       // tile rows (MFMA M)
 constexpr int TN = 256;       // tile cols (MFMA N)
 constexpr int TK = 64;        // k per LDS stage: 128-byte row segments, whole cache lines
 constexpr int kSlots = 5;     // LDS ring of operand-stage slots: 5 x 32 KB
-constexpr int KSTEPS = TK / 16;
 constexpr int kThreads = 256;
 constexpr int kStageElems = TM * TK;  // one operand, one stage: 32 KB
 
@@ -304,20 +303,6 @@ constexpr int kWaveScratchBytes = 8192;
 constexpr int kReadAfter[8] = {0, 1, 2, 3, 4, 5, 6, 7};
 constexpr int kLoadAfter[4] = {8, 9, 10, 11};
 
-// Instruction-class masks of __builtin_amdgcn_sched_group_barrier.
-constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100;
-
-// Ask the scheduler to alternate the `mfmas` MFMAs of a k-step with `reads`
-// LDS reads (the global->LDS loads it places by itself).
-template <int mfmas, int reads>
-__device__ __forceinline__ void interleave_hint() {
-#pragma unroll
-  for (int k = 0; k < (mfmas > reads ? mfmas : reads); ++k) {
-    if (k < mfmas) __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-    if (k < reads) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-  }
-}
-
 // Main loop: acc += A[m0 .. m0+255, k_lo .. k_hi) * B[n0 .. n0+255, k_lo .. k_hi)^T
 //
 // LDS is a ring of 5 operand-stage slots of 32 KB (the whole 160 KB):
@@ -351,7 +336,6 @@ __device__ __forceinline__ void tile_loop(const Operand& A, const Operand& B, in
                                           int64_t k_hi, Acc& acc) {
   static_assert(!FP8 || (A_KMAJ && B_KMAJ), "the fp8 loop takes k-major operands");
   bf16_t (*lds)[kStageElems] = ring();
-  constexpr int kReads = (A_KMAJ ? 4 : 8) + (B_KMAJ ? 4 : 8);  // LDS reads per k-step
   const int wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 #pragma unroll
@@ -370,14 +354,7 @@ __device__ __forceinline__ void tile_loop(const Operand& A, const Operand& B, in
   const int64_t nk = (k_hi - k_lo + TK - 1) / TK;
   auto k_of = [&](int64_t st) { return st < nk ? k_lo + st * TK : k_hi; };  // past the end: zeros
   const uint32_t lds0 = lds_addr(lds[0]);
-  auto read = [&](int sa, int sb, auto ks, Frags& f) {
-    constexpr int KS = decltype(ks)::value;
-    const uint32_t slot_a = lds0 + sa * kStageElems * 2, slot_b = lds0 + sb * kStageElems * 2;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) f.a[i] = read_frag<A_KMAJ, KS>(lds[sa], slot_a, foa, i);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) f.b[j] = read_frag<B_KMAJ, KS>(lds[sb], slot_b, fob, j);
-  };
+
   auto mma = [&](const Frags& f) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -385,18 +362,19 @@ __device__ __forceinline__ void tile_loop(const Operand& A, const Operand& B, in
       for (int j = 0; j < 4; ++j)
         acc.c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc.c[i][j], 0, 0, 0);
   };
+  auto mma8_one = [&](int i, int j, const Frags& lo, const Frags& hi) {
+    const v4i32 al = __builtin_bit_cast(v4i32, lo.a[i]), ah = __builtin_bit_cast(v4i32, hi.a[i]);
+    const v4i32 bl = __builtin_bit_cast(v4i32, lo.b[j]), bh = __builtin_bit_cast(v4i32, hi.b[j]);
+    const v8i32 a8 = __builtin_shufflevector(al, ah, 0, 1, 2, 3, 4, 5, 6, 7);
+    const v8i32 b8 = __builtin_shufflevector(bl, bh, 0, 1, 2, 3, 4, 5, 6, 7);
+    // formats 0, 0: both operands e4m3; no block scales
+    acc.c[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, acc.c[i][j], 0, 0, 0, 0, 0, 0);
+  };
   auto mma8 = [&](const Frags& lo, const Frags& hi) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const v4i32 al = __builtin_bit_cast(v4i32, lo.a[i]), ah = __builtin_bit_cast(v4i32, hi.a[i]);
-        const v4i32 bl = __builtin_bit_cast(v4i32, lo.b[j]), bh = __builtin_bit_cast(v4i32, hi.b[j]);
-        const v8i32 a8 = __builtin_shufflevector(al, ah, 0, 1, 2, 3, 4, 5, 6, 7);
-        const v8i32 b8 = __builtin_shufflevector(bl, bh, 0, 1, 2, 3, 4, 5, 6, 7);
-        // formats 0, 0: both operands e4m3; no block scales
-        acc.c[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, acc.c[i][j], 0, 0, 0, 0, 0, 0);
-      }
+      for (int j = 0; j < 4; ++j) mma8_one(i, j, lo, hi);
   };
   auto next = [](int s, int d) { return s + d >= kSlots ? s + d - kSlots : s + d; };
   // One k-step: the 16 MFMAs on `cur` (when MMA), with the 8 fragment reads of
@@ -441,8 +419,7 @@ __device__ __forceinline__ void tile_loop(const Operand& A, const Operand& B, in
   int sa = 0, sb = 1;  // slots of stage j
   // One iteration.  FIRST: there is no k-step 3 of a previous stage to
   // finish.  FAST: both loaded stages lie inside their operands, so the loads
-  // need no bounds checks and the iteration is one basic block, in which the
-  // scheduler can interleave loads, LDS reads and MFMAs.
+  // need no bounds checks and the iteration is one basic block.
   auto body = [&](int64_t j, auto first, auto fast) {
     constexpr bool kFirst = decltype(first)::value;
     constexpr bool kFast = decltype(fast)::value;
@@ -451,7 +428,7 @@ __device__ __forceinline__ void tile_loop(const Operand& A, const Operand& B, in
     const int64_t kb = k_of(j + 1), ka = k_of(j + 2);
     // direct load I0 + q of B_{j+1} / A_{j+2}, one per call
     auto load_b_at = [&](auto i0) {
-      return [&, i0](auto q) {
+      return [&](auto q) {
         constexpr int I = decltype(i0)::value + decltype(q)::value;
         if constexpr (kFast)
           load_stage_fast<I, 1, B_KMAJ>(B, n0, kb, slot_b, offb);
@@ -460,7 +437,7 @@ __device__ __forceinline__ void tile_loop(const Operand& A, const Operand& B, in
       };
     };
     auto load_a_at = [&](auto i0) {
-      return [&, i0](auto q) {
+      return [&](auto q) {
         constexpr int I = decltype(i0)::value + decltype(q)::value;
         if constexpr (kFast)
           load_stage_fast<I, 1, A_KMAJ>(A, m0, ka, slot_a, offa);
@@ -505,36 +482,50 @@ __device__ __forceinline__ void tile_loop(const Operand& A, const Operand& B, in
     }
   } else {
     Frags g0h, g1h;  // second halves of the two fp8 k-steps' operands (f0, f1 hold the first)
+    // One fp8 k-step: its 16 MFMAs on (clo, chi) when MMA, the 16 fragment reads
+    // of the next one (bf16-layout k-steps KS and KS + 1 into nlo, nhi), two after
+    // each of the first 8 MFMAs, and the stage's 8 direct loads load(0..7), one
+    // after each of the last 8, in the order scheduling barriers pin (as phase).
+    auto phase8 = [&](auto mma_on, const Frags& clo, const Frags& chi, Frags& nlo, Frags& nhi, auto ks,
+                      auto&& load) {
+      constexpr bool MMA = decltype(mma_on)::value;
+      constexpr int KS = decltype(ks)::value;
+      const uint32_t slot_a = lds0 + sa * kStageElems * 2, slot_b = lds0 + sb * kStageElems * 2;
+      static_for<16>([&](auto mc) {
+        constexpr int m = decltype(mc)::value;
+        if constexpr (MMA) mma8_one(m / 4, m % 4, clo, chi);
+        if constexpr (m < 4) {
+          nlo.a[m] = read_frag<A_KMAJ, KS>(lds[sa], slot_a, foa, m);
+          nhi.a[m] = read_frag<A_KMAJ, KS + 1>(lds[sa], slot_a, foa, m);
+        } else if constexpr (m < 8) {
+          nlo.b[m - 4] = read_frag<B_KMAJ, KS>(lds[sb], slot_b, fob, m - 4);
+          nhi.b[m - 4] = read_frag<B_KMAJ, KS + 1>(lds[sb], slot_b, fob, m - 4);
+        } else {
+          load(std::integral_constant<int, m - 8>{});
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    };
     auto body8 = [&](int64_t j, auto first, auto fast) {
       constexpr bool kFirst = decltype(first)::value;
       constexpr bool kFast = decltype(fast)::value;
       bf16_t* slot_b = lds[next(sb, 2)];
       bf16_t* slot_a = lds[next(sa, 4)];
       const int64_t kb = k_of(j + 1), ka = k_of(j + 2);
-      auto load_b = [&](auto i0) {
+      auto load_b = [&](auto q) {
         if constexpr (kFast)
-          load_stage_fast<decltype(i0)::value, 4, B_KMAJ>(B, n0, kb, slot_b, offb);
+          load_stage_fast<decltype(q)::value, 1, B_KMAJ>(B, n0, kb, slot_b, offb);
         else
-          load_stage<decltype(i0)::value, 4, B_KMAJ>(B, n0, kb, slot_b, offb);
+          load_stage<decltype(q)::value, 1, B_KMAJ>(B, n0, kb, slot_b, offb);
       };
-      auto load_a = [&](auto i0) {
+      auto load_a = [&](auto q) {
         if constexpr (kFast)
-          load_stage_fast<decltype(i0)::value, 4, A_KMAJ>(A, m0, ka, slot_a, offa);
+          load_stage_fast<decltype(q)::value, 1, A_KMAJ>(A, m0, ka, slot_a, offa);
         else
-          load_stage<decltype(i0)::value, 4, A_KMAJ>(A, m0, ka, slot_a, offa);
+          load_stage<decltype(q)::value, 1, A_KMAJ>(A, m0, ka, slot_a, offa);
       };
-      read(sa, sb, std::integral_constant<int, 0>{}, f0);
-      read(sa, sb, std::integral_constant<int, 1>{}, g0h);
-      if constexpr (!kFirst) mma8(f1, g1h);
-      load_b(std::integral_constant<int, 0>{});
-      load_b(std::integral_constant<int, 4>{});
-      interleave_hint<kFirst ? 0 : 16, 16>();
-      read(sa, sb, std::integral_constant<int, 2>{}, f1);
-      read(sa, sb, std::integral_constant<int, 3>{}, g1h);
-      mma8(f0, g0h);
-      load_a(std::integral_constant<int, 0>{});
-      load_a(std::integral_constant<int, 4>{});
-      interleave_hint<16, 16>();
+      phase8(std::bool_constant<!kFirst>{}, f1, g1h, f0, g0h, std::integral_constant<int, 0>{}, load_b);
+      phase8(std::true_type{}, f0, g0h, f1, g1h, std::integral_constant<int, 2>{}, load_a);
       wait_stages(1);
       stage_barrier();
       sa = next(sa, 2);
