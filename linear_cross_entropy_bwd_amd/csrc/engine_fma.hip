@@ -1,7 +1,7 @@
 // fp32 engine: LDS-tiled FMA contractions for FLCE_F32 inputs.
 //
-// One output tile per 256-thread block: 64x64 (4x4 outputs per thread) for dH
-// and dW, 64x32 (4x2) for the logits; K in steps of 64 staged through LDS in
+// One output tile per 256-thread block: 64x64 (4x4 outputs per thread) for dW,
+// 64x32 (4x2) for the logits and dH; K in steps of 64 staged through LDS in
 // [k][m] order.  The next step's operand
 // values are loaded into registers before the current step's FMAs, so their
 // latency hides under the arithmetic.  Operands are described by (pointer,
@@ -25,6 +25,8 @@ constexpr int kPad = 4;  // keeps rows 16-byte aligned for the vector fragment r
 // spread over twice as many workgroups.  Their 32 columns are one statistics
 // group, so the plan's fp32 group width must equal kLogitsBN.
 constexpr int kLogitsBN = 32;
+// dH's tile width (its tiles are 64 x kDhBN); the plan counts dH tiles the same way.
+constexpr int kDhBN = kFmaDhTileCols;
 
 // Values of one fragment row: 4 (float4) or 2 (float2) consecutive floats.
 template <int W>
@@ -47,24 +49,37 @@ struct TileLoop {
   static constexpr int JN = BNT / 16;
 
   // An operand of extent E (64 or 32) along m: each thread stages BK E / 256
-  // values per step.  The 64 lanes of a wave run along the operand's
-  // contiguous index (k for a k-major operand, m otherwise; an m-major
-  // operand must span 64), so each load instruction reads 64 consecutive
-  // values; the wave's other index steps by 4 from the wave number.  Loads
-  // use indices clamped into the operand and are issued unconditionally; the
-  // values outside it are replaced by 0 only when they are written to LDS, so
-  // nothing uses a loaded value before the step that needs it.
+  // values per step.  The lanes of a wave run along the operand's contiguous
+  // index (k for a k-major operand, m otherwise), so each load instruction
+  // reads consecutive values: all 64 lanes along it, or, for an m-major
+  // operand of extent 32, lanes 0-31 and 32-63 on two consecutive k.  The
+  // wave's other index steps from the wave number.  Loads use indices clamped
+  // into the operand and are issued unconditionally; the values outside it
+  // are replaced by 0 only when they are written to LDS, so nothing uses a
+  // loaded value before the step that needs it.
+  //   fix  = the contiguous index of lane l: l (or l % 32)
+  //   step = the other index of value q: w + 4 q (or 2 w + l / 32 + 8 q)
+  template <bool KMAJ, int E>
+  static __device__ __forceinline__ void lane_indices(int& fix, int (&step)[BK * E / 256]) {
+    static_assert(E == 64 || E == 32, "extents are 64 or 32");
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    constexpr bool kPair = !KMAJ && E == 32;
+    fix = kPair ? (lane & 31) : lane;
+#pragma unroll
+    for (int q = 0; q < BK * E / 256; ++q) step[q] = kPair ? 2 * wave + (lane >> 5) + 8 * q : wave + 4 * q;
+  }
+
   template <bool KMAJ, int E, typename T>
   static __device__ __forceinline__ void fetch(const T* __restrict__ P, int64_t ld, int64_t M, int64_t K,
                                                int64_t m0, int64_t k0, float (&r)[BK * E / 256]) {
-    static_assert(KMAJ || E == 64, "an m-major operand spans 64 lanes");
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int fix, step[BK * E / 256];
+    lane_indices<KMAJ, E>(fix, step);
     const int64_t lim_fix = KMAJ ? K : M, lim_step = KMAJ ? M : K;
-    const int64_t g_fix = (KMAJ ? k0 : m0) + lane;
+    const int64_t g_fix = (KMAJ ? k0 : m0) + fix;
     const int64_t c_fix = g_fix < lim_fix ? g_fix : lim_fix - 1;
 #pragma unroll
     for (int q = 0; q < BK * E / 256; ++q) {
-      const int64_t g_step = (KMAJ ? m0 : k0) + wave + 4 * q;
+      const int64_t g_step = (KMAJ ? m0 : k0) + step[q];
       const int64_t c_step = g_step < lim_step ? g_step : lim_step - 1;
       r[q] = Elem<T>::ld(P, c_step * ld + c_fix);
     }
@@ -75,17 +90,18 @@ struct TileLoop {
   template <bool KMAJ, int E>
   static __device__ __forceinline__ void stash(float (*S)[E + kPad], const float (&r)[BK * E / 256], int64_t M,
                                                int64_t K, int64_t m0, int64_t k0) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int fix, step[BK * E / 256];
+    lane_indices<KMAJ, E>(fix, step);
     const int64_t lim_fix = KMAJ ? K : M, lim_step = KMAJ ? M : K;
-    const bool fix_in = (KMAJ ? k0 : m0) + lane < lim_fix;
+    const bool fix_in = (KMAJ ? k0 : m0) + fix < lim_fix;
 #pragma unroll
     for (int q = 0; q < BK * E / 256; ++q) {
-      const bool in = fix_in && (KMAJ ? m0 : k0) + wave + 4 * q < lim_step;
+      const bool in = fix_in && (KMAJ ? m0 : k0) + step[q] < lim_step;
       const float x = in ? r[q] : 0.0f;
       if (KMAJ)
-        S[lane][wave + 4 * q] = x;
+        S[fix][step[q]] = x;
       else
-        S[wave + 4 * q][lane] = x;
+        S[step[q]][fix] = x;
     }
   }
 
@@ -214,29 +230,32 @@ __global__ __launch_bounds__(256) void fma_logits_kernel(const T* __restrict__ H
   }
 }
 
-// dH[t, :] (or a split partial) = G[t, :] . W
-template <typename T>
+// dH[t, :] (or a split partial) = G[t, :] . W, in 64 x kDhBN tiles: dH has
+// few rows per chunk, so narrow tiles give the vocabulary splits more
+// workgroups for the same fp32 partials.
 // blockIdx.z = vocabulary split: columns [z k_split, (z+1) k_split) of G and
 // rows of W; with several splits `out` is split z's fp32 partial (part_stride apart).
+template <typename T>
 __global__ __launch_bounds__(256) void fma_dh_kernel(const float* __restrict__ G, int64_t vp, const T* __restrict__ W,
                                                      int64_t rows, int64_t d, int64_t v, int64_t k_split,
                                                      int64_t part_stride, int accumulate, T* __restrict__ out) {
+  constexpr int JN = kDhBN / 16;
   const int64_t m0 = static_cast<int64_t>(blockIdx.x) * BM;
-  const int64_t n0 = static_cast<int64_t>(blockIdx.y) * BN;
+  const int64_t n0 = static_cast<int64_t>(blockIdx.y) * kDhBN;
   const int64_t k_lo = static_cast<int64_t>(blockIdx.z) * k_split;
   const int64_t k_hi = k_lo + k_split < v ? k_lo + k_split : v;
   out += static_cast<int64_t>(blockIdx.z) * part_stride;
-  float acc[4][4];
-  TileLoop<float, T, true, false>::run(G + k_lo, vp, W + k_lo * d, d, rows, d, k_hi > k_lo ? k_hi - k_lo : 0, m0, n0,
-                                       acc);
+  float acc[4][JN];
+  TileLoop<float, T, true, false, kDhBN>::run(G + k_lo, vp, W + k_lo * d, d, rows, d, k_hi > k_lo ? k_hi - k_lo : 0,
+                                              m0, n0, acc);
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int64_t t = m0 + ty * 4 + i;
     if (t >= rows) continue;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t n = n0 + tx * 4 + j;
+    for (int j = 0; j < JN; ++j) {
+      const int64_t n = n0 + tx * JN + j;
       if (n < d) Elem<T>::st(out, t * d + n, accumulate ? Elem<T>::ld(out, t * d + n) + acc[i][j] : acc[i][j]);
     }
   }
@@ -287,8 +306,8 @@ hipError_t fma_logits(const Plan& p, const Work& w, const ChunkArgs& a, int mode
 
 hipError_t fma_dh(const Plan& p, const Work& w, const ChunkArgs& a, hipStream_t s) {
   if (p.dtype != FLCE_F32) return hipErrorInvalidValue;
-  dim3 grid = grid2(a.rows, p.d);
-  grid.z = static_cast<unsigned>(p.dh_splits);
+  dim3 grid(static_cast<unsigned>((a.rows + BM - 1) / BM), static_cast<unsigned>((p.d + kDhBN - 1) / kDhBN),
+            static_cast<unsigned>(p.dh_splits));
   const int64_t k_split = (p.v + p.dh_splits - 1) / p.dh_splits;
   float* out = p.dh_splits > 1 ? w.dhpart : static_cast<float*>(a.dh);
   fma_dh_kernel<float><<<grid, 256, 0, s>>>(static_cast<const float*>(w.prob), p.vp, static_cast<const float*>(a.w),

@@ -103,7 +103,7 @@ int make_plan(int64_t n, int64_t d, int64_t v, int32_t dtype, int32_t with_bwd, 
   q.chunk = c;
   q.nchunks = (n + c - 1) / c;
   // dH = G.W has few output tiles (ceil(C/256) x ceil(d/256) on the matrix
-  // engine, 64 x 64 tiles on the FMA engine); its vocabulary reduction is split
+  // engine, 64 x 32 tiles on the FMA engine); its vocabulary reduction is split
   // in s parts, s chosen by best_splits: the fewest waves of one workgroup per
   // CU (256 on MI355X) per unit of work.  Each split keeps at least 4096
   // (matrix engine) or 256 (FMA engine) vocabulary columns; splits cost fp32
@@ -111,8 +111,8 @@ int make_plan(int64_t n, int64_t d, int64_t v, int32_t dtype, int32_t with_bwd, 
   q.dh_splits = 1;
   if (with_bwd) {
     const bool mfma = q.engine == ENGINE_MFMA;
-    const int64_t tm = mfma ? 256 : 64;
-    const int64_t tiles = ((q.chunk + tm - 1) / tm) * ((d + tm - 1) / tm);
+    const int64_t tm = mfma ? 256 : 64, tn = mfma ? 256 : kFmaDhTileCols;
+    const int64_t tiles = ((q.chunk + tm - 1) / tm) * ((d + tn - 1) / tn);
     int64_t smax = q.vp / (mfma ? 4096 : 256);
     if (smax > (mfma ? 8 : 16)) smax = mfma ? 8 : 16;
     // the fp32 partials ([S][C][d]) stay within the chunk buffer's bytes, and the

@@ -12,6 +12,10 @@ namespace flce {
 
 enum Engine : int32_t { ENGINE_MFMA = 0, ENGINE_FMA = 1 };
 
+// Output tiles of the dH contraction: 256 x 256 on the matrix engine, 64 rows x
+// kFmaDhTileCols columns on the fp32 engine (the plan's split choice counts them).
+constexpr int kFmaDhTileCols = 32;
+
 // dW epilogue mode for one chunk of the token reduction.
 enum DwMode : int32_t {
   DW_SINGLE = 0,  // only chunk: out = partial
