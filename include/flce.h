@@ -92,7 +92,7 @@ typedef enum { FLCE_MEAN = 0, FLCE_SUM = 1 } flce_reduction;
 
 enum {
   FLCE_OK = 0,
-  FLCE_ERR_INVALID_ARG = -1, /* null required pointer, n/d/v <= 0, d > 2^24, v > 2^24 - 256, unknown enum,
+  FLCE_ERR_INVALID_ARG = -1, /* null required pointer, n/d/v <= 0, n >= 2^31, d > 2^24, v > 2^24 - 256, unknown enum,
                                 size overflow */
   FLCE_ERR_ALIGNMENT = -2,   /* pointer or row pitch not aligned as documented above */
   FLCE_ERR_OOM = -3,         /* workspace allocation failed */
@@ -110,7 +110,9 @@ enum {
  *
  *   h, w           inputs, see Layout above.
  *   labels         int64 [n]; ignore_index marks rows that do not count.
- *   n, d, v        tokens, hidden size, vocabulary size (all > 0).
+ *   n, d, v        tokens, hidden size, vocabulary size (all > 0; n < 2^31,
+ *                  since the count of valid rows is 32-bit; d <= 2^24 and
+ *                  v <= 2^24 - 256).
  *   dtype          element type of h, w, dh_out, dw_out.
  *   reduction      FLCE_MEAN or FLCE_SUM.
  *   loss_out       fp32 [1], required.

@@ -22,6 +22,7 @@ constexpr size_t kDefaultProbBudget = size_t(1) << 30;  // bytes for the chunk's
 constexpr size_t kLowmemBudget = size_t(256) << 20;     // bytes for a vocabulary slice's [C, vb] buffer
 constexpr int64_t kVocabPad = 256;
 constexpr int64_t kMaxDim = int64_t(1) << 24;  // d <= 2^24, v <= 2^24 - 256
+constexpr int64_t kMaxRows = INT32_MAX;         // n_valid is counted in 32 bits
 constexpr int64_t kCus = 256;                   // compute units of an MI355X
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -63,8 +64,7 @@ int make_plan(int64_t n, int64_t d, int64_t v, int32_t dtype, int32_t with_bwd, 
               int64_t budget_req, int whole_rows) {
   if (p == nullptr || n <= 0 || d <= 0 || v <= 0) return FLCE_ERR_INVALID_ARG;
   if (dtype != FLCE_BF16 && dtype != FLCE_F32) return FLCE_ERR_INVALID_ARG;
-  if (!mul_ok(n, d) || !mul_ok(v, d) || v > (int64_t(1) << 40) || n > (int64_t(1) << 40))
-    return FLCE_ERR_INVALID_ARG;
+  if (!mul_ok(n, d) || !mul_ok(v, d) || v > (int64_t(1) << 40) || n > kMaxRows) return FLCE_ERR_INVALID_ARG;
   // Row strides (d, and v rounded up to 256) stay below 2^24 elements, so the
   // 32-bit offsets of the matrix engine's buffer loads cannot overflow.
   if (d > kMaxDim || v > kMaxDim - 256) return FLCE_ERR_INVALID_ARG;
@@ -484,8 +484,7 @@ int call_bwd(const void* h, const void* w, const int64_t* labels, const float* l
 int make_lowmem_plan(int64_t n, int64_t d, int64_t v, int32_t dtype, LowmemPlan* lp) {
   if (lp == nullptr || n <= 0 || d <= 0 || v <= 0) return FLCE_ERR_INVALID_ARG;
   if (dtype != FLCE_BF16 && dtype != FLCE_F32) return FLCE_ERR_INVALID_ARG;
-  if (!mul_ok(n, d) || !mul_ok(v, d) || v > (int64_t(1) << 40) || n > (int64_t(1) << 40))
-    return FLCE_ERR_INVALID_ARG;
+  if (!mul_ok(n, d) || !mul_ok(v, d) || v > (int64_t(1) << 40) || n > kMaxRows) return FLCE_ERR_INVALID_ARG;
   LowmemPlan q;
   memset(&q, 0, sizeof(q));
   q.budget = env_i64("FLCE_LOWMEM_BUFFER_BYTES", static_cast<int64_t>(kLowmemBudget));
@@ -594,7 +593,7 @@ int call_ce_logits(const void* logits, const int64_t* labels, int64_t n, int64_t
                    int64_t ignore_index, flce_reduction reduction, const float* lse_in, const float* grad_scale,
                    float* loss_out, float* lse_out, void* grad_out, hipStream_t stream) {
   if (logits == nullptr || labels == nullptr) return FLCE_ERR_INVALID_ARG;
-  if (n <= 0 || v <= 0 || n > (int64_t(1) << 40) || v > (int64_t(1) << 40) || !mul_ok(n, v))
+  if (n <= 0 || v <= 0 || n > kMaxRows || v > (int64_t(1) << 40) || !mul_ok(n, v))
     return FLCE_ERR_INVALID_ARG;
   if (dtype != FLCE_BF16 && dtype != FLCE_F32) return FLCE_ERR_INVALID_ARG;
   if (reduction != FLCE_MEAN && reduction != FLCE_SUM) return FLCE_ERR_INVALID_ARG;

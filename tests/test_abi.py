@@ -315,3 +315,11 @@ def test_dh_split_partials_stay_below_the_chunk_buffer():
         if p["dh_splits"] > 1:
             assert p["dh_splits"] * p["chunk_rows"] * d * 4 <= max(p["prob_buffer_bytes"], p["chunk_rows"] * d * 4)
         assert p["workspace_bytes"] < n * v * 4 or n < 256   # tiny shapes: 16-row chunk rounding and alignment
+
+
+def test_row_count_limit():
+    """n_valid is counted in 32 bits, so more than 2^31 - 1 token rows is an argument error."""
+    assert flce.flce_workspace_bytes(2**31 - 1, 16, 64, flce.FLCE_BF16, 0) > 0
+    assert flce.flce_workspace_bytes(2**31, 16, 64, flce.FLCE_BF16, 0) == 0
+    assert flce.flce_workspace_bytes(2**31, 16, 64, flce.FLCE_BF16, 1) == 0
+    assert flce.flce_workspace_bytes_lowmem(2**31, 16, 64, flce.FLCE_BF16) == 0
