@@ -280,8 +280,9 @@ int flce_bwd_fp8(const void* h_q, const float* h_scale, const void* w_q, const f
  * with Online LogSumExp" (step 3), and the per-GPU half of a vocabulary-
  * parallel loss: one GPU per shard, the partials exchanged in between.
  * On one GPU a caller loops over the shards: flce_fwd_shard for each, then
- * flce_merge_shards, then flce_bwd_shard for each with the merged LSE, then
- * flce_sum_parts over the dH partials.
+ * flce_merge_shards, then flce_bwd_shard for the first shard and
+ * flce_bwd_shard_accumulate for the others with the merged LSE (one fp32 dH
+ * sum), then flce_sum_parts over that one part to round it to dtype.
  *
  * Labels are the full-vocabulary ids (ignore_index or [0, V)); a shard sees
  * the labels outside it as "no target in this shard".  A shard call's
@@ -325,6 +326,17 @@ int flce_merge_shards(const float* lse_parts, const float* zy_parts, int64_t num
 int flce_bwd_shard(const void* h, const void* w_shard, const int64_t* labels, const float* lse, const float* grad_out,
                    int64_t n, int64_t d, int64_t v_shard, int64_t v_first, flce_dtype dtype, int64_t ignore_index,
                    flce_reduction reduction, float* dh_part_out, void* dw_shard_out, hipStream_t stream);
+
+/*
+ * flce_bwd_shard with the shard's dH term added to dh_acc (fp32 [n, d], 16-byte
+ * aligned) instead of written over it, so that the shards of one GPU share one
+ * fp32 sum; every other argument and error as for flce_bwd_shard.  Calls that
+ * add into the same dh_acc must be ordered (one stream), as the sum is not atomic.
+ */
+int flce_bwd_shard_accumulate(const void* h, const void* w_shard, const int64_t* labels, const float* lse,
+                              const float* grad_out, int64_t n, int64_t d, int64_t v_shard, int64_t v_first,
+                              flce_dtype dtype, int64_t ignore_index, flce_reduction reduction, float* dh_acc,
+                              void* dw_shard_out, hipStream_t stream);
 
 /*
  * out[i] = sum_q parts[q * count + i] for i < count, accumulated in fp32 in

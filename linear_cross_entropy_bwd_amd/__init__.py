@@ -36,6 +36,7 @@ EXPORTED = (
     "flce_fwd_shard",
     "flce_merge_shards",
     "flce_bwd_shard",
+    "flce_bwd_shard_accumulate",
     "flce_sum_parts",
     "flce_workspace_bytes",
     "flce_workspace_bytes_lowmem",
@@ -132,6 +133,8 @@ def lib() -> ctypes.CDLL:
     L.flce_merge_shards.restype = i32
     L.flce_bwd_shard.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i32, i64, i32, p, p, p]
     L.flce_bwd_shard.restype = i32
+    L.flce_bwd_shard_accumulate.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i32, i64, i32, p, p, p]
+    L.flce_bwd_shard_accumulate.restype = i32
     L.flce_sum_parts.argtypes = [p, i64, i64, i32, p, p]
     L.flce_sum_parts.restype = i32
     L.flce_workspace_bytes.argtypes = [i64, i64, i64, i32, i32]
@@ -241,6 +244,13 @@ def flce_bwd_shard(h, w_shard, labels, lse, grad_out, n, d, v_shard, v_first, dt
     return lib().flce_bwd_shard(_ptr(h), _ptr(w_shard), _ptr(labels), _ptr(lse), _ptr(grad_out), n, d, v_shard,
                                 v_first, dtype, ignore_index, reduction, _ptr(dh_part_out), _ptr(dw_shard_out),
                                 _stream(stream))
+
+
+def flce_bwd_shard_accumulate(h, w_shard, labels, lse, grad_out, n, d, v_shard, v_first, dtype, ignore_index,
+                              reduction, dh_acc, dw_shard_out, stream) -> int:
+    return lib().flce_bwd_shard_accumulate(_ptr(h), _ptr(w_shard), _ptr(labels), _ptr(lse), _ptr(grad_out), n, d,
+                                           v_shard, v_first, dtype, ignore_index, reduction, _ptr(dh_acc),
+                                           _ptr(dw_shard_out), _stream(stream))
 
 
 def flce_sum_parts(parts, num_parts, count, dtype, out, stream) -> int:
@@ -549,9 +559,10 @@ def linear_cross_entropy_vocab_split(h, w, labels, num_shards: int = 2, ignore_i
     """Fused linear cross-entropy with W's vocabulary rows split into shards, on one GPU.
 
     Per shard the partial forward (flce_fwd_shard), then the exact merge
-    (flce_merge_shards), then per shard the backward from the merged LSE
-    (flce_bwd_shard, fp32 dH terms) and the sum of the dH terms
-    (flce_sum_parts).  Returns (loss fp32 [1], lse fp32 [n], dh, dw) as
+    (flce_merge_shards), then per shard the backward from the merged LSE, its
+    dH term added into one fp32 [n, d] sum (flce_bwd_shard for the first,
+    flce_bwd_shard_accumulate for the others), rounded to the input dtype by
+    flce_sum_parts.  Returns (loss fp32 [1], lse fp32 [n], dh, dw) as
     flce_fwd_bwd does; the logits of each shard are recomputed in its backward.
     ``shards`` may give explicit [a, b) bounds instead of ``num_shards``.
     """
@@ -579,15 +590,15 @@ def linear_cross_entropy_vocab_split(h, w, labels, num_shards: int = 2, ignore_i
     st = flce_merge_shards(lse_parts, zy_parts, q_n, labels, n, ignore_index, red, loss, lse, stream)
     if st != FLCE_OK:
         raise FlceError(st, "flce_merge_shards")
-    dh_parts = torch.empty(q_n, n, d, dtype=torch.float32, device=dev)
+    dh_sum = torch.empty(n, d, dtype=torch.float32, device=dev)
     dw = torch.empty_like(w)
     for q, (a, b) in enumerate(bounds):
-        st = flce_bwd_shard(h, w[a:b], labels, lse, grad_out, n, d, b - a, a, dt, ignore_index, red, dh_parts[q],
-                            dw[a:b], stream)
+        call = flce_bwd_shard if q == 0 else flce_bwd_shard_accumulate
+        st = call(h, w[a:b], labels, lse, grad_out, n, d, b - a, a, dt, ignore_index, red, dh_sum, dw[a:b], stream)
         if st != FLCE_OK:
-            raise FlceError(st, "flce_bwd_shard")
+            raise FlceError(st, call.__name__)
     dh = torch.empty_like(h)
-    st = flce_sum_parts(dh_parts, q_n, n * d, dt, dh, stream)
+    st = flce_sum_parts(dh_sum, 1, n * d, dt, dh, stream)
     if st != FLCE_OK:
         raise FlceError(st, "flce_sum_parts")
     return loss, lse, dh, dw

@@ -816,9 +816,11 @@ int call_merge_shards(const float* lse_parts, const float* zy_parts, int64_t num
   return status_of(f);
 }
 
+// accumulate: dh_part_out += the shard's dH term instead of = (one fp32 sum for every shard).
 int call_bwd_shard(const void* h, const void* w_shard, const int64_t* labels, const float* lse, const float* grad_out,
                    int64_t n, int64_t d, int64_t v_shard, int64_t v_first, flce_dtype dtype, int64_t ignore_index,
-                   flce_reduction reduction, float* dh_part_out, void* dw_shard_out, hipStream_t stream) {
+                   flce_reduction reduction, float* dh_part_out, void* dw_shard_out, hipStream_t stream,
+                   int accumulate) {
   if (lse == nullptr || dh_part_out == nullptr || dw_shard_out == nullptr) return FLCE_ERR_INVALID_ARG;
   int st = check_common(h, w_shard, labels, n, d, v_shard, dtype, reduction, lse, nullptr);
   if (st != FLCE_OK) return st;
@@ -833,7 +835,7 @@ int call_bwd_shard(const void* h, const void* w_shard, const int64_t* labels, co
     hipError_t e = launch_shift_labels(labels, n, v_first, shifted, stream);
     if (e != hipSuccess) return e;
     return run_bwd(p, wk, h, w_shard, shifted, lse, grad_out, ignore_index - v_first, reduction, dh_part_out,
-                   dw_shard_out, stream, 1);
+                   dw_shard_out, stream, 1, accumulate);
   });
 }
 
@@ -944,7 +946,15 @@ int flce_bwd_shard(const void* h, const void* w_shard, const int64_t* labels, co
                    int64_t n, int64_t d, int64_t v_shard, int64_t v_first, flce_dtype dtype, int64_t ignore_index,
                    flce_reduction reduction, float* dh_part_out, void* dw_shard_out, hipStream_t stream) {
   return flce::call_bwd_shard(h, w_shard, labels, lse, grad_out, n, d, v_shard, v_first, dtype, ignore_index,
-                              reduction, dh_part_out, dw_shard_out, stream);
+                              reduction, dh_part_out, dw_shard_out, stream, 0);
+}
+
+int flce_bwd_shard_accumulate(const void* h, const void* w_shard, const int64_t* labels, const float* lse,
+                              const float* grad_out, int64_t n, int64_t d, int64_t v_shard, int64_t v_first,
+                              flce_dtype dtype, int64_t ignore_index, flce_reduction reduction, float* dh_acc,
+                              void* dw_shard_out, hipStream_t stream) {
+  return flce::call_bwd_shard(h, w_shard, labels, lse, grad_out, n, d, v_shard, v_first, dtype, ignore_index,
+                              reduction, dh_acc, dw_shard_out, stream, 1);
 }
 
 int flce_sum_parts(const float* parts, int64_t num_parts, int64_t count, flce_dtype dtype, void* out,

@@ -100,12 +100,19 @@ def test_split_and_shard_outputs_stay_in_bounds(n, d, v, dtype, chunk):
     bws, dw_s = guarded((vs, d), tdt)
     assert flce.flce_bwd_shard(hd, wd[a:], yd, lse, None, n, d, vs, a, code, -100, flce.FLCE_MEAN, dh_p, dw_s,
                                s) == flce.FLCE_OK
+    # and the lower part of W added into the same dH sum
+    bws2, dw_s2 = guarded((a, d), tdt)
+    assert flce.flce_bwd_shard_accumulate(hd, wd[:a], yd, lse, None, n, d, a, 0, code, -100, flce.FLCE_MEAN, dh_p,
+                                          dw_s2, s) == flce.FLCE_OK
     torch.cuda.synchronize()
     for b, shp, what in ((blp, (n,), "shard lse"), (bzp, (n,), "shard zy"), (bdp, (n, d), "shard dH part"),
-                         (bws, (vs, d), "shard dW")):
+                         (bws, (vs, d), "shard dW"), (bws2, (a, d), "second shard dW")):
         assert intact(b, shp), f"shard path wrote outside {what}"
     ref = flce_forward_backward(h, w, y)
     np.testing.assert_allclose(to_f64(dw_s), to_f64(dw)[a:], rtol=0, atol=2e-2 * float(np.max(np.abs(ref[3]))))
+    np.testing.assert_allclose(to_f64(dw_s2), to_f64(dw)[:a], rtol=0, atol=2e-2 * float(np.max(np.abs(ref[3]))))
+    # the two shards' terms summed are the whole dH
+    np.testing.assert_allclose(to_f64(dh_p), ref[2], rtol=0, atol=2e-2 * float(np.max(np.abs(ref[2]))))
 
 
 @pytest.mark.parametrize("n,v,dtype", [(513, 2100, "bf16"), (37, 1001, "f32"), (3, 7, "bf16")])
@@ -163,6 +170,8 @@ def test_allocation_failure_returns_oom_and_writes_nothing(monkeypatch):
         "flce_merge_shards": lambda: flce.flce_merge_shards(parts, parts, 2, yd, n, -100, M, o["loss"], o["lse"], s),
         "flce_bwd_shard": lambda: flce.flce_bwd_shard(hd, wd[:1000], yd, lse0, None, n, d, 1000, 0, B, -100, M,
                                                       o["dhp"], o["dw"][:1000], s),
+        "flce_bwd_shard_accumulate": lambda: flce.flce_bwd_shard_accumulate(hd, wd[:1000], yd, lse0, None, n, d, 1000,
+                                                                            0, B, -100, M, o["dhp"], o["dw"][:1000], s),
     }
     torch.cuda.synchronize()
     monkeypatch.setenv("FLCE_TEST_ALLOC_LIMIT_BYTES", "1")

@@ -136,3 +136,35 @@ def test_vocab_split_llama3_8b_head_eight_shards():
     e_dw = rel_max(to_f64(dw[torch.tensor(cols, device=DEV)]), rdw)
     say(f"  sampled dH rel {e_dh:.2e}, dW rel {e_dw:.2e}")
     assert e_dh <= tol["grad"] and e_dw <= tol["grad"]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_accumulated_dh_equals_the_summed_parts(dtype):
+    """flce_bwd_shard_accumulate adds each shard's dH term into one fp32 sum: the
+    result equals the separate terms summed in shard order by flce_sum_parts (to
+    fp32 rounding, as split reductions may associate differently), and each
+    shard's dW rows are the same either way."""
+    n, d, v = 300, 256, 2500
+    wl, (h, w, y) = _case(n, d, v, dtype, seed=71)
+    hd, wd, yd = h.to(DEV), w.to(DEV), y.to(DEV)
+    shards = [(0, 700), (700, 1800), (1800, 2500)]
+    code = flce.FLCE_BF16 if dtype == "bf16" else flce.FLCE_F32
+    _, lse, _, _ = flce.linear_cross_entropy(hd, wd, yd)
+    s = torch.cuda.current_stream()
+    parts = torch.full((len(shards), n, d), float("nan"), dtype=torch.float32, device=DEV)
+    acc = torch.full((n, d), float("nan"), dtype=torch.float32, device=DEV)
+    dw_a, dw_b = torch.empty_like(wd), torch.empty_like(wd)
+    for q, (a, b) in enumerate(shards):
+        assert flce.flce_bwd_shard(hd, wd[a:b], yd, lse, None, n, d, b - a, a, code, -100, flce.FLCE_MEAN, parts[q],
+                                   dw_a[a:b], s) == flce.FLCE_OK
+        call = flce.flce_bwd_shard if q == 0 else flce.flce_bwd_shard_accumulate
+        assert call(hd, wd[a:b], yd, lse, None, n, d, b - a, a, code, -100, flce.FLCE_MEAN, acc, dw_b[a:b],
+                    s) == flce.FLCE_OK
+    summed = torch.empty(n, d, dtype=torch.float32, device=DEV)
+    assert flce.flce_sum_parts(parts, len(shards), n * d, flce.FLCE_F32, summed, s) == flce.FLCE_OK
+    torch.cuda.synchronize()
+    assert torch.isfinite(acc).all()
+    err = float(((acc - summed).abs().max() / summed.abs().max()).item())
+    say(f"[vocab split] accumulated dH {dtype}: max diff {err:.2e} of the largest entry")
+    assert err <= 1e-6
+    assert torch.equal(dw_a, dw_b)
