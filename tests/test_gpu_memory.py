@@ -35,3 +35,29 @@ def test_fused_call_peak_memory(n, d, v):
     # the largest buffer, the chunk probability buffer(s), holds fewer rows than the batch
     assert p["prob_buffer_bytes"] <= (p["chunk_rows"] * (2 if p["dw_pairs"] else 1)) * p["vocab_pitch"] * 2
     assert p["chunk_rows"] * (2 if p["dw_pairs"] else 1) < n
+
+
+def test_pool_keeps_the_workspace_until_trimmed():
+    """The pool keeps a finished call's workspace reserved for the next call;
+    flce_pool_trim gives it back after a synchronisation, and calls after the
+    trim allocate again and return the same results."""
+    n, d, v = 2048, 1024, 32000
+    g = torch.Generator(device=DEV).manual_seed(5)
+    h = torch.randn(n, d, device=DEV, generator=g).to(torch.bfloat16)
+    w = (0.02 * torch.randn(v, d, device=DEV, generator=g)).to(torch.bfloat16)
+    y = torch.randint(0, v, (n,), device=DEV, generator=g)
+    ws = flce.flce_plan_info(n, d, v, flce.FLCE_BF16, 1)["workspace_bytes"]
+    first = flce.linear_cross_entropy(h, w, y)
+    torch.cuda.synchronize()
+    held = flce.flce_memory_reserved()
+    say(f"[memory] pool after a call: {held / 1e6:.1f} MB reserved (workspace {ws / 1e6:.1f} MB)")
+    assert held >= ws
+    flce.flce_pool_trim(0)
+    trimmed = flce.flce_memory_reserved()
+    say(f"[memory] after flce_pool_trim(0): {trimmed / 1e6:.1f} MB")
+    assert trimmed < ws
+    again = flce.linear_cross_entropy(h, w, y)
+    torch.cuda.synchronize()
+    assert flce.flce_memory_reserved() >= ws
+    for a, b in zip(first, again):
+        assert torch.equal(a, b)
