@@ -363,7 +363,7 @@ typedef struct {
   int64_t group_cols;      /* vocabulary columns per partial (max, sum-exp) pair */
   int64_t dh_splits;       /* split of the vocabulary reduction in dH = G.W */
   int32_t engine;          /* 0: bf16 matrix-core engine, 1: fp32 FMA engine */
-  int32_t dw_accumulator;  /* 1 if dW keeps a bf16 low half of its running sum in the workspace */
+  int32_t dw_accumulator;  /* 1 if dW keeps the lower 16 bits of its fp32 running sum in the workspace */
   size_t workspace_bytes;
   size_t prob_buffer_bytes;   /* the chunks' [chunk_rows, vocab_pitch] buffer(s) */
   int32_t dw_pairs;        /* 1 if two chunk buffers sit side by side and each dW launch covers two chunks */

@@ -847,15 +847,15 @@ __device__ __forceinline__ uint4* dw_piece(char* block, int64_t row_bytes, int u
   return reinterpret_cast<uint4*>(block + 8 * (2 * u + h) * row_bytes + lane_off);
 }
 
+// The running sum is kept exactly, as fp32: hi holds the upper 16 bits of
+// each value, lo the lower 16 (byte shuffles, one v_perm_b32 per pair).
 __device__ __forceinline__ void split_store(const floatx16& x, uint4* hi0, uint4* hi1, uint4* lo0, uint4* lo1) {
   uint32_t h[8], l[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    const float a0 = x[2 * k], a1 = x[2 * k + 1];
-    h[k] = pack_bf16x2(a0, a1);
-    const float r0 = a0 - bf16_to_f32(static_cast<bf16_t>(h[k] & 0xffffu));
-    const float r1 = a1 - bf16_to_f32(static_cast<bf16_t>(h[k] >> 16));
-    l[k] = pack_bf16x2(r0, r1);
+    const uint32_t a0 = __float_as_uint(x[2 * k]), a1 = __float_as_uint(x[2 * k + 1]);
+    h[k] = (a0 >> 16) | (a1 & 0xffff0000u);
+    l[k] = (a0 & 0xffffu) | (a1 << 16);
   }
   *hi0 = make_uint4(h[0], h[1], h[2], h[3]);
   *hi1 = make_uint4(h[4], h[5], h[6], h[7]);
@@ -869,8 +869,8 @@ __device__ __forceinline__ void add_pair(floatx16& x, const uint4& hi0, const ui
   const uint32_t l[8] = {lo0.x, lo0.y, lo0.z, lo0.w, lo1.x, lo1.y, lo1.z, lo1.w};
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    x[2 * k] += bf16_to_f32(static_cast<bf16_t>(h[k] & 0xffffu)) + bf16_to_f32(static_cast<bf16_t>(l[k] & 0xffffu));
-    x[2 * k + 1] += bf16_to_f32(static_cast<bf16_t>(h[k] >> 16)) + bf16_to_f32(static_cast<bf16_t>(l[k] >> 16));
+    x[2 * k] += __uint_as_float((h[k] << 16) | (l[k] & 0xffffu));
+    x[2 * k + 1] += __uint_as_float((h[k] & 0xffff0000u) | (l[k] >> 16));
   }
 }
 
@@ -880,7 +880,7 @@ struct DwArgs {
   Operand gt, h;
   int64_t v, d;
   int64_t tiles_m, tiles_n, group_m;
-  bf16_t* lo;        // [v][d] low bf16 half of the running sum (out holds the high half)
+  bf16_t* lo;        // [v][d] lower 16 bits of the fp32 running sum (out holds the upper 16)
   bf16_t* out;       // dw_out
 };
 
@@ -1011,9 +1011,9 @@ __global__ __launch_bounds__(kThreads) void mfma_dw_kernel(DwArgs a) {
 
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int wm = wave >> 1, wn = wave & 1;
-  // The running dW sum across chunks is the pair (hi, lo) of bf16 values
-  // whose sum carries about 16 significant bits: hi lives in dw_out, lo in the
-  // workspace, both inside this tile's own 256x256 region.
+  // The running dW sum across chunks is fp32, split in its upper 16 bits (hi,
+  // in dw_out) and lower 16 bits (lo, in the workspace), both inside this
+  // tile's own 256x256 region.
   const bool interior = m0 + TM <= a.v && n0 + TN <= a.d;
   if (interior) {
     dw_epilogue_tiled<MODE>(a, acc, m0, n0, wave, lane);
@@ -1033,7 +1033,7 @@ __global__ __launch_bounds__(kThreads) void mfma_dw_kernel(DwArgs a) {
         prev[R] = 0.0f;
         if (read_acc && col_ok && row < a.v) {
           const int64_t o = row * a.d + col;
-          prev[R] = bf16_to_f32(a.out[o]) + bf16_to_f32(a.lo[o]);
+          prev[R] = __uint_as_float((static_cast<uint32_t>(a.out[o]) << 16) | a.lo[o]);
         }
       });
       static_for<16>([&](auto R) {
@@ -1041,9 +1041,12 @@ __global__ __launch_bounds__(kThreads) void mfma_dw_kernel(DwArgs a) {
         if (col_ok && row < a.v) {
           const int64_t o = row * a.d + col;
           const float x = acc.c[I][J][R.value] + prev[R];
-          const bf16_t hi = f32_to_bf16(x);
-          a.out[o] = hi;
-          if (keep_split) a.lo[o] = f32_to_bf16(x - bf16_to_f32(hi));
+          if (keep_split) {  // the running sum: x's upper and lower 16 bits
+            a.out[o] = static_cast<bf16_t>(__float_as_uint(x) >> 16);
+            a.lo[o] = static_cast<bf16_t>(__float_as_uint(x) & 0xffffu);
+          } else {
+            a.out[o] = f32_to_bf16(x);
+          }
         }
       });
     });

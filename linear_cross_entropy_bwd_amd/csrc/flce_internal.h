@@ -82,7 +82,7 @@ struct Work {
   float* pm;         // [G][C] partial row max per vocabulary group; becomes the softmax factor
   float* ps;         // [G][C] partial sum of exp(z - max) per group
   void* prob;        // [C][vp] exp(z - group max), turned into G in place (dtype of the engine)
-  uint16_t* dwlo;    // [v][d] bf16 low half of the running dW sum; dw_out holds the high half
+  uint16_t* dwlo;    // [v][d] lower 16 bits of the fp32 running dW sum; dw_out holds the upper 16
   float* dhpart;     // [S][C][d] fp32 split-vocabulary partials of dH (when dh_splits > 1)
 };
 
