@@ -1,14 +1,15 @@
-"""How the error of dW grows with the number of token chunks.
+"""How the error of dW behaves as the number of token chunks grows.
 
-Across chunks the fused call keeps dW as a bf16 pair (hi, lo): about 16
-significant bits instead of fp32's 24.  This measures dW's error against the
-full fp64 oracle for 2, 8, 32 and 64 chunks (FLCE_CHUNK_ROWS 4096, 1024, 256,
-128 on 8192 x 1024 x 32000; plans of four or more chunks pair them, so 64
-chunks are 32 dW launches over the running sum), next to the low-memory path,
-whose dW rows are single fp32 reductions over all tokens.  Every count must
-stay within the 2e-2 bound.  Measured: the error does not grow with the
-count (the Frobenius error is the same at 2 and 64 chunks; 64 chunks move
-0.3% of the entries by one bf16 step); it is set by G's bf16 rounding."""
+Across chunks the fused call keeps dW as an exact fp32 sum, its upper 16 bits
+in dw_out and its lower 16 bits in the workspace; only the last chunk rounds
+it to bf16.  This measures dW's error against the full fp64 oracle for 2, 8,
+32 and 64 chunks (FLCE_CHUNK_ROWS 4096, 1024, 256, 128 on 8192 x 1024 x 32000;
+plans of four or more chunks pair them, so 64 chunks are 32 dW launches over
+the running sum), next to the low-memory path, whose dW rows are single fp32
+reductions over all tokens.  Every count must stay within the 2e-2 bound.
+Measured: the error does not grow with the count (the Frobenius error is the
+same at 2 and 64 chunks; 64 chunks move 0.02% of the entries by one bf16
+step, the fp32 rounding of the partial sums); it is set by G's bf16 rounding."""
 import numpy as np
 import pytest
 import torch
