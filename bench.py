@@ -1,8 +1,9 @@
 """Benchmark: fused linear cross-entropy forward + backward on one MI355X.
 
-One step = one flce_fwd_bwd call (label scan, logits GEMM with the online
-LSE / target epilogue, merge, in-place gradient, dH and dW GEMMs, loss
-reduction) over the Llama-3-8B LM-head workload: N=8192 tokens, D=4096,
+One step = one flce_fwd_bwd call (label scan; per chunk the target-logit
+reference, the logits GEMM with the online LSE / target epilogue, the merge,
+the per-row factor patch, dH and dW GEMMs; loss reduction) over the
+Llama-3-8B LM-head workload: N=8192 tokens, D=4096,
 V=128256, bf16, 5% ignored labels, mean reduction.  Inputs are synthetic,
 seeded and resident in HBM before timing starts.  The headline `value` and
 `ms_per_step` come from steps timed without any per-kernel instrumentation;
@@ -13,8 +14,8 @@ By default the line also carries every workload (`per_config`: tokens/s,
 matrix-peak fraction, extra device memory against the N V 4 bytes of logits
 avoided, and parity against the fp64 oracle), the parity of the headline
 workload, the low-memory path and a memory/speed sweep, the other entry
-points (split forward/backward, forward only, vocabulary split, FP8,
-cross-entropy on given logits), torch's hipBLASLt products on the same
+points (split forward/backward, the in-place gradient form of the fused call,
+forward only, vocabulary split, FP8, cross-entropy on given logits), torch's hipBLASLt products on the same
 contraction shapes for context, and the oracle's CPU baseline.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
@@ -611,6 +612,29 @@ def main() -> int:
             "tflops_8ndv": 8.0 * wl.n * wl.d * wl.v / (ms_split * 1e-3) / 1e12,
             "mfma_pct_8ndv": 100.0 * 8.0 * wl.n * wl.d * wl.v / (ms_split * 1e-3) / (peak * 1e12),
             "path": "flce_fwd then flce_bwd (logits recomputed from the saved LSE)",
+        }
+
+        # flce_fwd_bwd with the softmax factor written into the stored probabilities in
+        # place (FLCE_INPLACE_GRAD=1) instead of applied per row, for comparison
+        os.environ["FLCE_INPLACE_GRAD"] = "1"
+        try:
+            def inplace_step():
+                flce.linear_cross_entropy(hd, wd, yd, reduction=wl.reduction, out=out)
+            inplace_step()
+            torch.cuda.synchronize()
+            flce.flce_memory_high_water(reset=True)
+            _, tot = time_steps(torch, inplace_step, stream, args.steps, max(1, args.warmup))
+            peak_ip = flce.flce_memory_high_water()
+        finally:
+            os.environ.pop("FLCE_INPLACE_GRAD", None)
+        ms_ip = tot / args.steps
+        log(f"[bench] fused, in-place gradient pass: {ms_ip:.3f} ms/step, peak {peak_ip / 1e6:.1f} MB")
+        result["inplace_grad"] = {
+            "ms_per_step": ms_ip,
+            "tokens_per_s": wl.n / (ms_ip * 1e-3),
+            "mfma_pct_6ndv": 100.0 * 6.0 * wl.n * wl.d * wl.v / (ms_ip * 1e-3) / (peak * 1e12),
+            "extra_device_bytes": peak_ip,
+            "path": "flce_fwd_bwd, FLCE_INPLACE_GRAD=1 (P rewritten into G in place; no per-row factor)",
         }
 
         # the forward alone (loss and LSE), 2 N D V flop

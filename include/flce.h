@@ -53,9 +53,9 @@
  * crosses this interface and nothing aborts.
  *
  * Labels: each label must be ignore_index or lie in [0, v).  Any other value
- * is a caller error that is not diagnosed on the device: the kernels never
- * index memory with a label, such a row counts as valid with a target logit
- * of 0 and no one-hot term.
+ * is a caller error that is not diagnosed on the device: the kernels index
+ * memory with a label only after checking that it lies in [0, v), and such a
+ * row counts as valid with a target logit of 0 and no one-hot term.
  *
  * Environment overrides (read at every call and by flce_plan_info and
  * flce_workspace_bytes; meant for tests and tuning, positive integers only,
@@ -66,7 +66,9 @@
  * FLCE_DW_PAIR_CHUNKS (fewest chunks that pair, default 4), FLCE_DH_SPLITS
  * (split of dH's vocabulary reduction), FLCE_GROUP_LOGITS,
  * FLCE_GROUP_DH, FLCE_GROUP_DW (tile-order group sizes of the three
- * contractions on the bf16 engine).  Results stay within the
+ * contractions on the bf16 engine), FLCE_INPLACE_GRAD (1: flce_fwd_bwd on the
+ * bf16 engine rewrites the stored probabilities into G in place instead of
+ * applying the softmax factor per row; see flce_fwd_bwd).  Results stay within the
  * stated tolerances under any of them; bitwise results can change.
  * FLCE_TEST_ALLOC_LIMIT_BYTES is a test hook: a workspace request above that
  * many bytes fails as an allocation failure would (FLCE_ERR_OOM, nothing
@@ -106,7 +108,11 @@ enum {
  * (chunked streaming, online LSE, target extraction); backward: section
  * "2. In-Kernel Gradient Computation During the Backward Pass" (softmax minus
  * one-hot, dH = G.W, dW = G^T.H), computed in the same pass from the chunk's
- * logits rather than by recomputing them.
+ * logits rather than by recomputing them.  On the bf16 engine (vocabulary
+ * rounded up to 256 at least 2 d) the chunk's probabilities are stored against
+ * one reference per row and the row's softmax factor is applied to dH's
+ * output rows and to a bf16 copy of the chunk's H that dW reads
+ * (G = diag(F) P', so G.W = diag(F) (P'.W) and G^T.H = P'^T (diag(F) H)).
  *
  *   h, w           inputs, see Layout above.
  *   labels         int64 [n]; ignore_index marks rows that do not count.
@@ -286,8 +292,9 @@ int flce_bwd_fp8(const void* h_q, const float* h_scale, const void* w_q, const f
  *
  * Labels are the full-vocabulary ids (ignore_index or [0, V)); a shard sees
  * the labels outside it as "no target in this shard".  A shard call's
- * workspace is flce_workspace_bytes(n, d, v_shard, dtype, with_bwd) plus
- * 8 n bytes (the shard's shifted labels).
+ * workspace is flce_workspace_bytes(n, d, v_shard, dtype, 0) (forward) or
+ * flce_workspace_bytes(n, d, v_shard, dtype, 2) (backward) plus 8 n bytes
+ * (the shard's shifted labels).
  */
 
 /*
@@ -348,8 +355,8 @@ int flce_sum_parts(const float* parts, int64_t num_parts, int64_t count, flce_dt
                    hipStream_t stream);
 
 /*
- * Bytes of device workspace one call allocates (with_bwd = 1 for
- * flce_fwd_bwd and flce_bwd, 0 for flce_fwd); 0 for invalid sizes.  Honours the
+ * Bytes of device workspace one call allocates (with_bwd = 0 for flce_fwd,
+ * 2 for flce_bwd, 1 or any other value for flce_fwd_bwd); 0 for invalid sizes.  Honours the
  * FLCE_CHUNK_ROWS and FLCE_WORKSPACE_CAP_BYTES environment overrides exactly
  * as the calls do.
  */
@@ -367,6 +374,9 @@ typedef struct {
   size_t workspace_bytes;
   size_t prob_buffer_bytes;   /* the chunks' [chunk_rows, vocab_pitch] buffer(s) */
   int32_t dw_pairs;        /* 1 if two chunk buffers sit side by side and each dW launch covers two chunks */
+  int32_t folded_factor;   /* 1 if the one-pass backward applies the softmax factor per row, to dH's rows
+                              and to a bf16 copy of the chunk's H that dW reads (matrix engine, vocabulary
+                              pitch at least 2 d) */
 } flce_plan_t;
 
 /* Fill *out with the plan for these sizes; returns 0 or FLCE_ERR_INVALID_ARG. */

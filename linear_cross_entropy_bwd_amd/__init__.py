@@ -70,6 +70,7 @@ class PlanInfo(ctypes.Structure):
         ("workspace_bytes", ctypes.c_size_t),
         ("prob_buffer_bytes", ctypes.c_size_t),
         ("dw_pairs", ctypes.c_int32),
+        ("folded_factor", ctypes.c_int32),
     ]
 
     def as_dict(self):

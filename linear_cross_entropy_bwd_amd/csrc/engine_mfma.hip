@@ -564,6 +564,9 @@ struct LogitsArgs {
   // fp8 operands: z = h_scale[token] * w_scale[vocabulary row] * (q_h . q_w)
   const float* h_scale;
   const float* w_scale;
+  // folded one-pass backward: per-row reference u_t of the stored P, row flags
+  const float* uref;
+  int32_t* flag;
 };
 
 // Recompute-mode epilogue of one wave's 128 vocabulary rows x 128 tokens:
@@ -645,7 +648,9 @@ __device__ __forceinline__ void logits_grad_epilogue(const LogitsArgs& a, Acc& a
 
 // STORE_P: the epilogue also writes P = exp(z - group max) into the chunk buffer
 // (a compile-time choice, so that the statistics loop carries no branch).
-template <bool RECOMP, bool FP8 = false, bool STORE_P = false>
+// FOLD: P = exp(z - r) instead, r = max(u_t, group max - kFoldMargin) with the
+// row's reference u_t; a row with r above u_t is flagged.
+template <bool RECOMP, bool FP8 = false, bool STORE_P = false, bool FOLD = false>
 __global__ __launch_bounds__(kThreads) void mfma_logits_kernel(LogitsArgs a) {
   const int64_t nb = a.tiles_m * a.tiles_n;
   const int64_t t = xcd_remap(blockIdx.x, nb);
@@ -713,9 +718,11 @@ __global__ __launch_bounds__(kThreads) void mfma_logits_kernel(LogitsArgs a) {
     // after a column's P stores would wait for them (vmcnt is in order).
     // (unconditional, from a clamped row, so that no branch makes them wait one by one)
     int64_t labs[4];
+    float us[4];
     static_for<4>([&](auto J) {
       const int64_t tok = n0 + wn * 128 + J * 32 + (lane & 31);
       labs[J] = a.labels[tok < a.rows ? tok : a.rows - 1];
+      if constexpr (FOLD) us[J] = a.uref[tok < a.rows ? tok : a.rows - 1];
     });
     static_for<4>([&](auto J) {
       const int64_t tok = n0 + wn * 128 + J * 32 + (lane & 31);
@@ -733,6 +740,12 @@ __global__ __launch_bounds__(kThreads) void mfma_logits_kernel(LogitsArgs a) {
       });
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       const float mxl = mx * kLog2e;
+      float cref = 1.0f;  // the stored P is e * cref
+      if constexpr (FOLD) {
+        const float r = fmaxf(us[J], mx - kFoldMargin);
+        cref = __builtin_amdgcn_exp2f((mx - r) * kLog2e);
+        if (live && half == 0 && vbase < a.v && r != us[J]) a.flag[tok] = 1;
+      }
       float s = 0.0f;
       static_for<4>([&](auto I) {
         static_for<4>([&](auto Q) {
@@ -744,8 +757,8 @@ __global__ __launch_bounds__(kThreads) void mfma_logits_kernel(LogitsArgs a) {
           });
           if constexpr (STORE_P) {
             uint2 pk;
-            pk.x = pack_bf16x2(e[0], e[1]);
-            pk.y = pack_bf16x2(e[2], e[3]);
+            pk.x = pack_bf16x2(e[0] * cref, e[1] * cref);
+            pk.y = pack_bf16x2(e[2] * cref, e[3] * cref);
             *reinterpret_cast<uint2*>(srow + ((I * 4 + Q) ^ sx) * 16) = pk;
           }
         });
@@ -798,8 +811,10 @@ struct DhArgs {
   float* out_f32;    // direct fp32 output (splits == 1, fp32) or split partials [splits][C][d]
   int64_t part_stride;
   int32_t accumulate;  // splits == 1, fp32 output: add to what out_f32 holds
+  const float* rowf;   // FOLD: per-row factor of the output rows
 };
 
+template <bool FOLD>
 __global__ __launch_bounds__(kThreads) void mfma_dh_kernel(DhArgs a) {
   const int64_t nb = a.tiles_m * a.tiles_n * a.splits;
   const int64_t t = xcd_remap(blockIdx.x, nb);
@@ -816,12 +831,25 @@ __global__ __launch_bounds__(kThreads) void mfma_dh_kernel(DhArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   static_for<4>([&](auto I) {
+    // rows acc_row(I, 4Q + U) = 32 I + 8 Q + 4 (lane / 32) + U: one float4 per Q
+    // (the factor array is padded to whole tiles)
+    float rf[16];
+    if constexpr (FOLD) {
+      static_for<4>([&](auto Q) {
+        const float4 f4 = *reinterpret_cast<const float4*>(a.rowf + m0 + wm * 128 + I * 32 + 8 * Q + 4 * (lane >> 5));
+        rf[4 * Q] = f4.x;
+        rf[4 * Q + 1] = f4.y;
+        rf[4 * Q + 2] = f4.z;
+        rf[4 * Q + 3] = f4.w;
+      });
+    }
     static_for<4>([&](auto J) {
       const int64_t col = n0 + wn * 128 + J * 32 + (lane & 31);
       static_for<16>([&](auto R) {
         const int64_t row = m0 + wm * 128 + acc_row(I, R, lane);
         if (col < a.d && row < a.rows) {
-          const float x = acc.c[I][J][R.value];
+          float x = acc.c[I][J][R.value];
+          if constexpr (FOLD) x *= rf[R.value];
           if (a.out_bf16 != nullptr)
             a.out_bf16[row * a.d + col] = f32_to_bf16(x);
           else if (a.accumulate)
@@ -1080,6 +1108,8 @@ hipError_t mfma_logits(const Plan& p, const Work& w, const ChunkArgs& c, int mod
   a.ignore_index = c.ignore_index;
   a.h_scale = c.h_scale;
   a.w_scale = c.w_scale;
+  a.uref = w.uref;
+  a.flag = w.flag;
   const dim3 grid(static_cast<unsigned>(a.tiles_m * a.tiles_n));
   if (c.fp8) {
     if (mode == LOGITS_PROB) return hipErrorInvalidValue;  // the fp8 path has no one-pass backward
@@ -1090,7 +1120,10 @@ hipError_t mfma_logits(const Plan& p, const Work& w, const ChunkArgs& c, int mod
   } else if (mode == LOGITS_GRAD_FROM_LSE) {
     mfma_logits_kernel<true><<<grid, kThreads, 0, s>>>(a);
   } else if (mode == LOGITS_PROB) {
-    mfma_logits_kernel<false, false, true><<<grid, kThreads, 0, s>>>(a);
+    if (c.fold)
+      mfma_logits_kernel<false, false, true, true><<<grid, kThreads, 0, s>>>(a);
+    else
+      mfma_logits_kernel<false, false, true><<<grid, kThreads, 0, s>>>(a);
   } else {
     mfma_logits_kernel<false, false, false><<<grid, kThreads, 0, s>>>(a);
   }
@@ -1118,14 +1151,20 @@ hipError_t mfma_dh(const Plan& p, const Work& w, const ChunkArgs& c, hipStream_t
     a.out_bf16 = static_cast<bf16_t*>(c.dh);
   else
     a.out_f32 = static_cast<float*>(c.dh);
-  mfma_dh_kernel<<<static_cast<unsigned>(a.tiles_m * a.tiles_n * a.splits), kThreads, 0, s>>>(a);
+  a.rowf = c.fold ? w.rowf : nullptr;
+  const unsigned blocks = static_cast<unsigned>(a.tiles_m * a.tiles_n * a.splits);
+  if (c.fold)
+    mfma_dh_kernel<true><<<blocks, kThreads, 0, s>>>(a);
+  else
+    mfma_dh_kernel<false><<<blocks, kThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 
 hipError_t mfma_dw(const Plan& p, const Work& w, const ChunkArgs& c, hipStream_t s) {
   DwArgs a;
   a.gt = Operand{static_cast<const bf16_t*>(w.prob), p.vp, p.vp, c.rows};
-  a.h = Operand{static_cast<const bf16_t*>(c.h), p.d, p.d, c.rows};
+  // folded backward: the token operand is the chunk's bf16(F * H)
+  a.h = Operand{static_cast<const bf16_t*>(c.fold ? w.hs : c.h), p.d, p.d, c.rows};
   a.v = p.v;
   a.d = p.d;
   a.tiles_m = p.vp / TM;

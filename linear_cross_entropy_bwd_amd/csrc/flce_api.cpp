@@ -137,6 +137,12 @@ int make_plan(int64_t n, int64_t d, int64_t v, int32_t dtype, int32_t with_bwd, 
   // one dW launch reduces over 2 C tokens: half the launches and half the
   // passes over the running sum, for one more chunk buffer.
   q.dw_pair = (allow_pair && q.dw_acc && q.nchunks >= env_i64("FLCE_DW_PAIR_CHUNKS", 4)) ? 1 : 0;
+  // The one-pass backward of the matrix engine folds the softmax factor into a
+  // per-row factor applied to dH's rows and to dW's token operand (a bf16 copy
+  // of the chunk's H), where the vocabulary is wide enough for that copy to be
+  // small next to the chunk buffer.
+  const bool one_pass = with_bwd != 0 && with_bwd != 2;
+  q.fold = (one_pass && q.engine == ENGINE_MFMA && q.vp >= 2 * d && env_i64("FLCE_INPLACE_GRAD", 0) == 0) ? 1 : 0;
   // Tile orders (see tile_coords): consecutive tiles share operand tiles in L2.
   q.group_m[0] = env_i64("FLCE_GROUP_LOGITS", 8);
   q.group_m[1] = env_i64("FLCE_GROUP_DH", 8);
@@ -160,6 +166,10 @@ int make_plan(int64_t n, int64_t d, int64_t v, int32_t dtype, int32_t with_bwd, 
   q.off_prob = take(q.prob_bytes);
   q.off_dwacc = take(q.dw_acc ? sizeof(uint16_t) * static_cast<size_t>(v * d) : 0);
   q.off_dhpart = take(with_bwd && q.dh_splits > 1 ? sizeof(float) * q.dh_splits * q.chunk * d : 0);
+  q.off_uref = take(q.fold ? sizeof(float) * q.chunk : 0);
+  q.off_flag = take(q.fold ? sizeof(int32_t) * q.chunk : 0);
+  q.off_rowf = take(q.fold ? sizeof(float) * static_cast<size_t>((q.chunk + 255) / 256 * 256) : 0);
+  q.off_hs = take(q.fold ? sizeof(uint16_t) * static_cast<size_t>(q.chunk * d) * (q.dw_pair ? 2 : 1) : 0);
   q.total = off;
   *p = q;
   return FLCE_OK;
@@ -229,7 +239,8 @@ struct Prof {
 Prof g_prof;
 
 const char* const kKindNames[K_NUM_KINDS] = {"label_scan", "logits_lse", "lse_merge",   "grad_inplace", "dh_gemm",
-                                             "dh_reduce",  "dw_gemm",    "loss_reduce", "ce_rows",      "dequant_e4m3"};
+                                             "dh_reduce",  "dw_gemm",    "loss_reduce", "ce_rows",      "dequant_e4m3",
+                                             "target_ref", "fold_patch"};
 
 template <class F>
 hipError_t timed(int kind, hipStream_t s, F&& launch) {
@@ -274,6 +285,10 @@ Work carve(const Plan& p, char* base) {
   w.prob = base + p.off_prob;
   w.dwlo = reinterpret_cast<uint16_t*>(base + p.off_dwacc);
   w.dhpart = reinterpret_cast<float*>(base + p.off_dhpart);
+  w.uref = reinterpret_cast<float*>(base + p.off_uref);
+  w.flag = reinterpret_cast<int32_t*>(base + p.off_flag);
+  w.rowf = reinterpret_cast<float*>(base + p.off_rowf);
+  w.hs = base + p.off_hs;
   return w;
 }
 
@@ -285,6 +300,7 @@ Work chunk_work(const Plan& p, const Work& wk, int64_t c) {
   if (p.dw_pair && (c & 1)) {
     const size_t elem = p.engine == ENGINE_MFMA ? 2 : 4;
     wc.prob = static_cast<char*>(wk.prob) + static_cast<size_t>(p.chunk * p.vp) * elem;
+    wc.hs = static_cast<char*>(wk.hs) + static_cast<size_t>(p.chunk * p.d) * sizeof(uint16_t);
   }
   return wc;
 }
@@ -344,16 +360,24 @@ hipError_t run(const Plan& p, const Work& wk, const void* h, const void* w, cons
     a.fp8 = h_scale != nullptr ? 1 : 0;
     a.h_scale = h_scale != nullptr ? h_scale + a.row0 : nullptr;
     a.w_scale = w_scale;
+    a.fold = p.fold;
 
+    if (a.fold) {
+      e = timed(K_TARGET_REF, s, [&] { return launch_target_ref(p, wc, a, s); });
+      if (e != hipSuccess) return e;
+    }
     const int mode = p.with_bwd ? LOGITS_PROB : LOGITS_STATS;
     e = timed(K_LOGITS, s, [&] {
       return p.engine == ENGINE_MFMA ? mfma_logits(p, wc, a, mode, s) : fma_logits(p, wc, a, mode, s);
     });
     if (e != hipSuccess) return e;
-    e = timed(K_LSE_MERGE, s, [&] { return launch_lse_merge(p, wc, a, p.with_bwd, s); });
+    e = timed(K_LSE_MERGE, s, [&] { return launch_lse_merge(p, wc, a, p.with_bwd ? (a.fold ? 2 : 1) : 0, s); });
     if (e != hipSuccess) return e;
     if (!p.with_bwd) continue;
-    e = timed(K_GRAD, s, [&] { return launch_grad(p, wc, a, s); });
+    if (a.fold)
+      e = timed(K_FOLD_PATCH, s, [&] { return launch_fold_patch(p, wc, a, s); });
+    else
+      e = timed(K_GRAD, s, [&] { return launch_grad(p, wc, a, s); });
     if (e != hipSuccess) return e;
     e = timed(K_DH, s, [&] { return p.engine == ENGINE_MFMA ? mfma_dh(p, wc, a, s) : fma_dh(p, wc, a, s); });
     if (e != hipSuccess) return e;
@@ -399,6 +423,7 @@ hipError_t run_bwd(const Plan& p, const Work& wk, const void* h, const void* w, 
     a.dh_f32 = dh_f32;
     a.dh_accumulate = dh_accumulate;
     a.fp8 = 0;
+    a.fold = 0;
     a.h_scale = nullptr;
     a.w_scale = nullptr;
     e = timed(K_LOGITS, s, [&] {
@@ -461,7 +486,7 @@ int call_bwd(const void* h, const void* w, const int64_t* labels, const float* l
   if (!aligned(dh_out, 16) || !aligned(dw_out, 16) || (grad_out != nullptr && !aligned(grad_out, 4)))
     return FLCE_ERR_ALIGNMENT;
   Plan p;
-  st = make_plan(n, d, v, dtype, 1, &p);
+  st = make_plan(n, d, v, dtype, 2, &p);
   if (st != FLCE_OK) return st;
   return with_workspace(p, stream, [&](const Work& wk) {
     return run_bwd(p, wk, h, w, labels, lse, grad_out, ignore_index, reduction, dh_out, dw_out, stream);
@@ -502,10 +527,10 @@ int make_lowmem_plan(int64_t n, int64_t d, int64_t v, int32_t dtype, LowmemPlan*
   q.nslices = (v + vb - 1) / vb;
   int st = make_plan(n, d, v, dtype, 0, &q.fwd, 1, q.budget);
   if (st != FLCE_OK) return st;
-  st = make_plan(n, d, vb, dtype, 1, &q.slice, 0, q.budget, whole_rows);
+  st = make_plan(n, d, vb, dtype, 2, &q.slice, 0, q.budget, whole_rows);
   if (st != FLCE_OK) return st;
   const int64_t v_last = v - (q.nslices - 1) * vb;
-  st = make_plan(n, d, v_last, dtype, 1, &q.last, 0, q.budget, whole_rows);
+  st = make_plan(n, d, v_last, dtype, 2, &q.last, 0, q.budget, whole_rows);
   if (st != FLCE_OK) return st;
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -683,9 +708,9 @@ int call_bwd_fp8(const void* h_q, const float* h_scale, const void* w_q, const f
     return FLCE_ERR_ALIGNMENT;
   Plan p, p8;
   // both plans as for a backward (chunked, unpaired), so that their chunks match
-  int st = make_plan(n, d, v, FLCE_BF16, 1, &p, /*allow_pair=*/0);
+  int st = make_plan(n, d, v, FLCE_BF16, 2, &p, /*allow_pair=*/0);
   if (st != FLCE_OK) return st;
-  st = make_plan(n, d / 2, v, FLCE_BF16, 1, &p8, /*allow_pair=*/0);
+  st = make_plan(n, d / 2, v, FLCE_BF16, 2, &p8, /*allow_pair=*/0);
   if (st != FLCE_OK) return st;
   if (p8.chunk != p.chunk || p8.vp != p.vp || !mul_ok(v, d)) return FLCE_ERR_INVALID_ARG;
   const size_t off_w16 = p.total;
@@ -713,6 +738,7 @@ int call_bwd_fp8(const void* h_q, const float* h_scale, const void* w_q, const f
       a.dh_f32 = 0;
       a.dh_accumulate = 0;
       a.dw_mode = p.nchunks == 1 ? DW_SINGLE : (c == 0 ? DW_FIRST : (c == p.nchunks - 1 ? DW_LAST : DW_MID));
+      a.fold = 0;
       // recompute: fp8 operands, G into the chunk buffer
       a.fp8 = 1;
       a.h = static_cast<const char*>(h_q) + a.row0 * d;
@@ -828,7 +854,7 @@ int call_bwd_shard(const void* h, const void* w_shard, const int64_t* labels, co
     return FLCE_ERR_ALIGNMENT;
   Plan p;
   size_t off_labels = 0;
-  st = shard_plan(n, d, v_shard, v_first, dtype, ignore_index, 1, &p, &off_labels);
+  st = shard_plan(n, d, v_shard, v_first, dtype, ignore_index, 2, &p, &off_labels);
   if (st != FLCE_OK) return st;
   return with_workspace(p, stream, [&](const Work& wk) {
     int64_t* shifted = reinterpret_cast<int64_t*>(wk.base + off_labels);
@@ -983,6 +1009,7 @@ int flce_plan_info(int64_t n, int64_t d, int64_t v, flce_dtype dtype, int with_b
   out->workspace_bytes = p.total;
   out->prob_buffer_bytes = p.prob_bytes;
   out->dw_pairs = p.dw_pair;
+  out->folded_factor = p.fold;
   return FLCE_OK;
 }
 

@@ -38,13 +38,17 @@ struct Plan {
   int64_t dh_splits;   // split of the K = vocabulary reduction of dH
   int32_t dw_acc;      // dW's running sum needs a workspace low half (bf16 path, several chunks)
   int32_t dw_pair;     // two chunk buffers; each dW launch reduces over a pair of consecutive chunks
+  int32_t fold;        // one-pass backward with the softmax factor folded into a per-row factor (see run())
   int64_t group_m[3];  // tile-row group of the logits, dH and dW tile orders
   // byte offsets inside the single workspace allocation
   size_t off_nvalid, off_zy, off_gy, off_lse, off_loss, off_pm, off_ps, off_prob, off_dwacc, off_dhpart;
+  size_t off_uref, off_flag, off_rowf, off_hs;
   size_t total;
   size_t prob_bytes;
 };
 
+// with_bwd: 0 forward only, 2 backward by recomputing the logits from a saved
+// LSE (run_bwd), any other value forward and one-pass backward (run).
 // allow_pair = 0 keeps one chunk buffer (for loops that run dW chunk by chunk).
 // budget > 0 replaces the default byte budget of one chunk's buffer (or, for a
 // forward-only plan, of its group partials).  whole_rows = 1 lets a chunk hold
@@ -84,7 +88,17 @@ struct Work {
   void* prob;        // [C][vp] exp(z - group max), turned into G in place (dtype of the engine)
   uint16_t* dwlo;    // [v][d] lower 16 bits of the fp32 running dW sum; dw_out holds the upper 16
   float* dhpart;     // [S][C][d] fp32 split-vocabulary partials of dH (when dh_splits > 1)
+  // folded one-pass backward (plan.fold)
+  float* uref;       // [C] row reference r_t of the stored P: the target logit (+-1e30, see target_ref_kernel)
+  int32_t* flag;     // [C] 1 where some group max exceeds r_t by more than kFoldMargin
+  float* rowf;       // [C rounded up to 256] per-row factor F_t = scale * exp(ref_t - lse_t)
+  void* hs;          // [C][d] bf16(F * H) (two such with paired buffers): dW's token operand
 };
+
+// Folded backward: P is stored as exp(z - max(r_t, group max - kFoldMargin)),
+// at most exp(kFoldMargin), so the factor F_t >= scale * exp(-kFoldMargin - log v)
+// stays a normal number.
+constexpr float kFoldMargin = 30.0f;
 
 // Kernel kinds for the timing instrumentation.
 enum Kind : int {
@@ -98,7 +112,9 @@ enum Kind : int {
   K_LOSS = 7,
   K_CE_ROWS = 8,
   K_DEQUANT = 9,
-  K_NUM_KINDS = 10
+  K_TARGET_REF = 10,
+  K_FOLD_PATCH = 11,
+  K_NUM_KINDS = 12
 };
 
 // What the logits contraction's epilogue produces.
@@ -130,6 +146,7 @@ struct ChunkArgs {
   int32_t fp8;              // 1: h and w hold e4m3 bytes (d counts byte pairs), scaled per row
   const float* h_scale;     // fp8: chunk's first token scale
   const float* w_scale;     // fp8: vocabulary row scales
+  int32_t fold;             // 1: folded one-pass backward (plan.fold, run() only)
 };
 
 // --- launchers (each returns the launch status) ---------------------------------
@@ -139,6 +156,8 @@ hipError_t launch_label_scan(const Plan& p, const Work& w, const int64_t* labels
                              hipStream_t s);
 hipError_t launch_lse_merge(const Plan& p, const Work& w, const ChunkArgs& a, int with_grad, hipStream_t s);
 hipError_t launch_grad(const Plan& p, const Work& w, const ChunkArgs& a, hipStream_t s);
+hipError_t launch_target_ref(const Plan& p, const Work& w, const ChunkArgs& a, hipStream_t s);
+hipError_t launch_fold_patch(const Plan& p, const Work& w, const ChunkArgs& a, hipStream_t s);
 hipError_t launch_loss_reduce(const Plan& p, const Work& w, int32_t reduction, float* loss_out, hipStream_t s);
 hipError_t launch_dh_reduce(const Plan& p, const Work& w, const ChunkArgs& a, hipStream_t s);
 hipError_t launch_label_count(const int64_t* labels, int64_t n, int64_t ignore_index, int32_t* nvalid, hipStream_t s);

@@ -52,7 +52,8 @@ __global__ __launch_bounds__(kMergeRows* kMergeSlices) void lse_merge_kernel(
     float* __restrict__ pm, const float* __restrict__ ps, int64_t C, int64_t G, int64_t rows,
     const int64_t* __restrict__ labels, int64_t ignore_index, int64_t v, const int32_t* __restrict__ nvalid,
     int32_t reduction, float* __restrict__ zy, float* __restrict__ gy, float* __restrict__ lse_rows,
-    float* __restrict__ loss_rows, float* __restrict__ zy_rows, int with_grad) {
+    float* __restrict__ loss_rows, float* __restrict__ zy_rows, int with_grad, const float* __restrict__ uref,
+    const int32_t* __restrict__ flag, float* __restrict__ rowf) {
   __shared__ float red[kMergeSlices][kMergeRows];
   __shared__ float row_lse[kMergeRows];
   const int r = threadIdx.x % kMergeRows;
@@ -92,16 +93,32 @@ __global__ __launch_bounds__(kMergeRows* kMergeSlices) void lse_merge_kernel(
       lse_rows[t] = l;
       loss_rows[t] = valid ? l - z : 0.0f;
       if (zy_rows != nullptr) zy_rows[t] = valid ? z : 0.0f;
-      if (with_grad) {
-        const float sc = valid ? row_scale(*nvalid, reduction) : 0.0f;
-        const bool hit = valid && y >= 0 && y < v;
+      const float sc = valid ? row_scale(*nvalid, reduction) : 0.0f;
+      const bool hit = valid && y >= 0 && y < v;
+      if (with_grad == 1) {
         gy[t] = hit ? (fast_exp(z - l) - 1.0f) * sc : 0.0f;
+      } else if (with_grad == 2) {
+        // Folded: G = F_t * P' with one reference per row, the target logit
+        // u_t, or the row max m where the row is flagged (its groups are then
+        // brought to m by the patch); the target column of P' takes
+        // (exp(z - l) - 1) / exp(ref - l).
+        const float ref = flag[t] ? m : uref[t];
+        rowf[t] = sc > 0.0f ? sc * fast_exp(ref - l) : 0.0f;
+        gy[t] = hit ? fast_exp(z - ref) - fast_exp(l - ref) : 0.0f;
       }
     }
   }
   if (!with_grad) return;
   __syncthreads();
   if (!live) return;
+  if (with_grad == 2) {
+    // a flagged row's group g holds exp(z - r_g), r_g = max(u_t, m_g - margin):
+    // its factor to the common reference m is exp(r_g - m)
+    if (!flag[t]) return;
+    const float u = uref[t];
+    for (int64_t g = sl; g < G; g += kMergeSlices) pm[g * C + t] = fast_exp(fmaxf(u, pm[g * C + t] - kFoldMargin) - m);
+    return;
+  }
   const float l = row_lse[r];
   const int64_t y = labels[t];
   const float sc = y != ignore_index ? row_scale(*nvalid, reduction) : 0.0f;
@@ -166,6 +183,82 @@ __global__ __launch_bounds__(256) void grad_kernel(TP* __restrict__ prob, int64_
     if (c0 >= vp) return;
     const float f = c0 < v ? factor[(c0 / group) * C + t] : 0.0f;
     grad_vec8<TP>(row + c0, f, c0, v, y, gt);
+  }
+}
+
+// Folded backward, before the logits: u_t = h_t . w_{y_t} in fp32, the row's
+// reference for the stored P (one wave per row); +1e30 for an ignored row
+// (its P and factor are then 0) and -1e30 for a label outside [0, v) (every
+// group then exceeds it, which flags the row).  Also clears the row flags.
+__global__ __launch_bounds__(256) void target_ref_kernel(const bf16_t* __restrict__ h, const bf16_t* __restrict__ w,
+                                                         int64_t d, int64_t v, const int64_t* __restrict__ labels,
+                                                         int64_t ignore_index, int64_t rows, float* __restrict__ uref,
+                                                         int32_t* __restrict__ flag) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (t >= rows) return;  // whole waves
+  const int64_t y = labels[t];
+  float u;
+  if (y == ignore_index) {
+    u = 1e30f;
+  } else if (y < 0 || y >= v) {
+    u = -1e30f;
+  } else {
+    const uint4* hr = reinterpret_cast<const uint4*>(h + t * d);
+    const uint4* wr = reinterpret_cast<const uint4*>(w + y * d);
+    float acc = 0.0f;
+    for (int64_t k = lane; k < d / 8; k += 64) {
+      const uint4 a = hr[k], b = wr[k];
+      const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc = fmaf(__uint_as_float(av[q] << 16), __uint_as_float(bv[q] << 16), acc);
+        acc = fmaf(__uint_as_float(av[q] & 0xffff0000u), __uint_as_float(bv[q] & 0xffff0000u), acc);
+      }
+    }
+    for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+    u = acc;
+  }
+  if (lane == 0) {
+    uref[t] = u;
+    flag[t] = 0;
+  }
+}
+
+// Folded backward, after the merge (one block per chunk row): the token
+// operand of dW, H'_t = bf16(F_t h_t); the target column of P' takes its
+// value; a flagged row's groups are rescaled to the common reference.
+__global__ __launch_bounds__(256) void fold_patch_kernel(const bf16_t* __restrict__ h, bf16_t* __restrict__ hs,
+                                                         int64_t d, bf16_t* __restrict__ prob, int64_t vp, int64_t v,
+                                                         int64_t group, const float* __restrict__ factor, int64_t C,
+                                                         const float* __restrict__ rowf,
+                                                         const int32_t* __restrict__ flag,
+                                                         const float* __restrict__ gy,
+                                                         const int64_t* __restrict__ labels, int64_t ignore_index) {
+  const int64_t t = blockIdx.x;
+  const float f = rowf[t];
+  const uint4* src = reinterpret_cast<const uint4*>(h + t * d);
+  uint4* dst = reinterpret_cast<uint4*>(hs + t * d);
+  for (int64_t k = threadIdx.x; k < d / 8; k += 256) {
+    const uint4 x = src[k];
+    const uint32_t xv[4] = {x.x, x.y, x.z, x.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      o[q] = pack_bf16x2(__uint_as_float(xv[q] << 16) * f, __uint_as_float(xv[q] & 0xffff0000u) * f);
+    dst[k] = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+  const int64_t y = labels[t];
+  const bool hit = y != ignore_index && y >= 0 && y < v;
+  bf16_t* row = prob + t * vp;
+  if (flag[t]) {
+    const float gt = gy[t];
+    for (int64_t c0 = static_cast<int64_t>(threadIdx.x) * 8; c0 < vp; c0 += 256 * 8) {
+      const float fg = c0 < v ? factor[(c0 / group) * C + t] : 0.0f;
+      grad_vec8<bf16_t>(row + c0, fg, c0, v, hit ? y : -1, gt);
+    }
+  } else if (hit && threadIdx.x == 0) {
+    row[y] = f32_to_bf16(gy[t]);
   }
 }
 
@@ -277,7 +370,21 @@ hipError_t launch_lse_merge(const Plan& p, const Work& w, const ChunkArgs& a, in
   const int64_t blocks = (a.rows + kMergeRows - 1) / kMergeRows;
   lse_merge_kernel<<<static_cast<unsigned>(blocks), kMergeRows * kMergeSlices, 0, s>>>(
       w.pm, w.ps, p.chunk, p.ngroups, a.rows, a.labels, a.ignore_index, p.v, w.nvalid, a.reduction, w.zy, w.gy,
-      a.lse_rows, w.loss_rows + a.row0, a.zy_rows, with_grad);
+      a.lse_rows, w.loss_rows + a.row0, a.zy_rows, with_grad, w.uref, w.flag, w.rowf);
+  return hipGetLastError();
+}
+
+hipError_t launch_target_ref(const Plan& p, const Work& w, const ChunkArgs& a, hipStream_t s) {
+  const unsigned blocks = static_cast<unsigned>((a.rows + 3) / 4);
+  target_ref_kernel<<<blocks, 256, 0, s>>>(static_cast<const bf16_t*>(a.h), static_cast<const bf16_t*>(a.w), p.d, p.v,
+                                           a.labels, a.ignore_index, a.rows, w.uref, w.flag);
+  return hipGetLastError();
+}
+
+hipError_t launch_fold_patch(const Plan& p, const Work& w, const ChunkArgs& a, hipStream_t s) {
+  fold_patch_kernel<<<static_cast<unsigned>(a.rows), 256, 0, s>>>(
+      static_cast<const bf16_t*>(a.h), static_cast<bf16_t*>(w.hs), p.d, static_cast<bf16_t*>(w.prob), p.vp, p.v,
+      p.group, w.pm, p.chunk, w.rowf, w.flag, w.gy, a.labels, a.ignore_index);
   return hipGetLastError();
 }
 

@@ -57,6 +57,17 @@ def test_plan_invariants(dtype, shape):
     fwd = flce.flce_plan_info(n, d, v, dtype, 0)
     assert fwd["prob_buffer_bytes"] == 0 and fwd["dw_pairs"] == 0
     assert fwd["workspace_bytes"] <= p["workspace_bytes"]
+    # the per-row factor of the one-pass backward: bf16 with a pitch of at least 2 d;
+    # its bf16 copy of H (one per chunk buffer) is what sets the one-pass workspace
+    # above the recompute backward's
+    fold = int(dtype == flce.FLCE_BF16 and p["vocab_pitch"] >= 2 * d)
+    assert p["folded_factor"] == fold
+    rec = flce.flce_plan_info(n, d, v, dtype, 2)
+    assert rec["folded_factor"] == 0 and fwd["folded_factor"] == 0
+    assert (rec["chunk_rows"], rec["dw_pairs"], rec["prob_buffer_bytes"]) == (c, p["dw_pairs"], p["prob_buffer_bytes"])
+    hs = c * d * 2 * (2 if p["dw_pairs"] else 1)
+    assert fold * hs <= p["workspace_bytes"] - rec["workspace_bytes"] <= fold * (hs + 4 * 256 + 16 * c + 3 * 256)
+    assert rec["workspace_bytes"] == flce.flce_workspace_bytes(n, d, v, dtype, 2)
 
 
 def test_plan_env_overrides(monkeypatch):
@@ -67,6 +78,10 @@ def test_plan_env_overrides(monkeypatch):
     p = flce.flce_plan_info(8192, 4096, 128256, flce.FLCE_BF16, 1)
     assert p["chunk_rows"] * p["vocab_pitch"] * 2 <= 64 * 1024 * 1024     # the cap bounds one chunk's buffer
     assert p["dw_pairs"] == 1 and p["prob_buffer_bytes"] == 2 * p["chunk_rows"] * p["vocab_pitch"] * 2
+    monkeypatch.delenv("FLCE_WORKSPACE_CAP_BYTES")
+    assert flce.flce_plan_info(8192, 4096, 128256, flce.FLCE_BF16, 1)["folded_factor"] == 1
+    monkeypatch.setenv("FLCE_INPLACE_GRAD", "1")
+    assert flce.flce_plan_info(8192, 4096, 128256, flce.FLCE_BF16, 1)["folded_factor"] == 0
 
 
 def test_invalid_sizes():

@@ -60,6 +60,32 @@ def test_large_logits_bf16():
     _parity(wl, inp, "large logits")
 
 
+@pytest.mark.parametrize("chunk", [None, "64"])
+def test_folded_factor_flagged_rows(monkeypatch, chunk):
+    """The matrix engine's one-pass backward stores each row's P against the
+    row's target logit and applies the softmax factor per row (to dH's rows and
+    to dW's copy of H).  A row whose target logit lies more than 30 below some
+    128-column group's max is flagged and brought to the row max after the
+    merge.  W ~ N(0, 0.5^2) at D = 512 gives both kinds of row; chunks of 64
+    rows add paired dW launches and a ragged last chunk."""
+    n, d, v = 300, 512, 4100
+    wl, (h, w, y) = _case(n, d, v, "bf16", sigma_w=0.5, ignore_frac=0.1, seed=31)
+    if chunk is not None:
+        monkeypatch.setenv("FLCE_CHUNK_ROWS", chunk)
+    p = flce.flce_plan_info(n, d, v, flce.FLCE_BF16, 1)
+    assert p["folded_factor"] == 1
+    # the case holds flagged and unflagged rows (fp64 logits of the bf16 inputs)
+    z = h.double().numpy() @ w.double().numpy().T
+    zp = np.full((n, (v + 127) // 128 * 128), -np.inf)
+    zp[:, :v] = z
+    gmax = zp.reshape(n, -1, 128).max(axis=2)
+    valid = (y != -100).numpy()
+    zy = z[np.arange(n), np.where(valid, y.numpy(), 0)]
+    flagged = np.any(gmax - 30.0 > zy[:, None], axis=1) & valid
+    assert 0 < int(flagged.sum()) < int(valid.sum())
+    _parity(wl, (h, w, y), f"flagged rows, chunk {chunk}")
+
+
 def test_all_rows_ignored():
     for red in ("mean", "sum"):
         wl, (h, w, y) = _case(64, 128, 500, "f32", sigma_w=0.2, seed=15, reduction=red)
@@ -140,15 +166,21 @@ def test_chunk_size_invariance(monkeypatch, chunk):
 CHUNK_MODES = {"128": (3, 0), "80": (4, 1), "64": (5, 1), "512": (1, 0)}
 
 
+@pytest.mark.parametrize("grad", ["folded", "inplace"])
 @pytest.mark.parametrize("chunk", list(CHUNK_MODES))
-def test_chunk_modes_bf16(monkeypatch, chunk):
+def test_chunk_modes_bf16(monkeypatch, chunk, grad):
     """The matrix engine's dW accumulation modes on interior 256x256 tiles, chunk by
-    chunk and over chunk pairs (one launch reducing over two chunks' rows)."""
+    chunk and over chunk pairs (one launch reducing over two chunks' rows), with
+    the softmax factor applied per row (dW reads the scaled copy of H) or written
+    into the stored probabilities in place."""
     wl, inp = _case(300, 256, 1500, "bf16", sigma_w=0.1, seed=25)
     monkeypatch.setenv("FLCE_CHUNK_ROWS", chunk)
+    if grad == "inplace":
+        monkeypatch.setenv("FLCE_INPLACE_GRAD", "1")
     p = flce.flce_plan_info(300, 256, 1500, flce.FLCE_BF16, 1)
     assert (p["num_chunks"], p["dw_pairs"]) == CHUNK_MODES[chunk]
-    _parity(wl, inp, f"bf16 chunk {chunk}")
+    assert p["folded_factor"] == int(grad == "folded")
+    _parity(wl, inp, f"bf16 chunk {chunk}, {grad}")
 
 
 def test_ignored_rows_exact_zero_and_isolation():
