@@ -97,6 +97,48 @@ def test_all_rows_ignored():
         assert np.max(np.abs(lse - ref[1]) / np.abs(ref[1])) <= 1e-5
 
 
+def test_all_rows_ignored_bf16():
+    """bf16 with the per-row gradient factor: every row ignored gives loss 0, zero
+    gradients and the true LSE of every row."""
+    for red in ("mean", "sum"):
+        wl, (h, w, y) = _case(300, 128, 1500, "bf16", sigma_w=0.2, seed=19, reduction=red)
+        y[:] = -100
+        assert flce.flce_plan_info(300, 128, 1500, flce.FLCE_BF16, 1)["folded_factor"] == 1
+        loss, lse, dh, dw = run_lib(h, w, y, red)
+        ref = flce_forward_backward(h, w, y, reduction=red)
+        assert loss == 0.0
+        assert np.all(dh == 0.0) and np.all(dw == 0.0)
+        assert np.max(np.abs(lse - ref[1]) / np.abs(ref[1])) <= TOL[torch.bfloat16]["loss"]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_labels_outside_the_vocabulary(dtype):
+    """Labels outside [0, v) that are not ignore_index are a caller error the header
+    defines: the row counts as valid, with target logit 0 and no one-hot term.  With
+    the sum reduction that is the oracle's result with those rows ignored, plus
+    lse_i in the loss and softmax_i in G for each of them (computed here in fp64).
+    On the bf16 engine such rows have no target reference and take the flagged path."""
+    n, d, v = 200, 128, 1000
+    wl, (h, w, y) = _case(n, d, v, dtype, sigma_w=0.2, ignore_frac=0.1, seed=37, reduction="sum")
+    rng = np.random.default_rng(37)
+    oor = rng.choice(np.flatnonzero((y != -100).numpy()), size=24, replace=False)
+    y_bad = y.clone()
+    y_bad[torch.from_numpy(oor[:12])] = v + 7
+    y_bad[torch.from_numpy(oor[12:])] = -5
+    y_ign = y.clone()
+    y_ign[torch.from_numpy(oor)] = -100
+    rloss, rlse, rdh, rdw = flce_forward_backward(h, w, y_ign, reduction="sum")
+    hd, wd = to_f64(h), to_f64(w)
+    p = np.exp(hd[oor] @ wd.T - rlse[oor, None])            # softmax rows of the out-of-range rows
+    rloss = rloss + float(rlse[oor].sum())
+    rdh = rdh.copy()
+    rdh[oor] = p @ wd
+    rdw = rdw + p.T @ hd[oor]
+    say(f"[parity] labels outside [0, v): {len(oor)} rows, {dtype}")
+    gpu = run_lib(h, w, y_bad, "sum")
+    check(gpu, (rloss, rlse, rdh, rdw), wl.torch_dtype, "labels outside the vocabulary")
+
+
 def test_w_zero_closed_form():
     wl, (h, w, y) = _case(80, 64, 300, "f32", seed=16)
     w.zero_()
