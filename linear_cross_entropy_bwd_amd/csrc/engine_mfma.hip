@@ -5,6 +5,10 @@
 //   dH      dH[t, k]  = sum_j G[t, j] W[j, k]    A = G   (k-major), B = W   (n-major)
 //   dW      dW[j, k]  = sum_t G[t, j] H[t, k]    A = G^T (m-major), B = H   (n-major)
 //
+// In the one-pass backward G = diag(F) P' (one factor per token row): dH takes
+// P' as A and scales its output rows by F, dW takes P'^T as A and diag(F) H,
+// a bf16 copy written beforehand, as B.
+//
 // One 256x256 output tile per 256-thread block (4 waves, 2x2, 128x128 per
 // wave = 4x4 MFMA tiles of 32x32).  K advances 64 at a time.  Operand tiles
 // go from global memory straight into LDS with 16-byte loads (no register
@@ -23,7 +27,8 @@
 // The logits are computed transposed (vocabulary on the MFMA rows, tokens on
 // the lanes) so that each lane holds 64 vocabulary entries of the same token:
 // the per-token max and sum-exp over a 128-wide vocabulary group need one
-// cross-lane step.  The epilogue stores exp(z - group max) in bf16 into the
+// cross-lane step.  The epilogue stores exp(z - group max), or in the
+// one-pass backward exp(z - r) against a per-row reference r, in bf16 into the
 // chunk's buffer; the full logits never leave registers.
 //
 // Consecutive workgroups are dispatched round-robin over the 8 XCDs; block

@@ -85,18 +85,21 @@ struct Work {
   float* loss_rows;  // [n]   per-row NLL (unscaled; 0 for ignored rows)
   float* pm;         // [G][C] partial row max per vocabulary group; becomes the softmax factor
   float* ps;         // [G][C] partial sum of exp(z - max) per group
-  void* prob;        // [C][vp] exp(z - group max), turned into G in place (dtype of the engine)
+  void* prob;        // [C][vp] exp(z - group max), turned into G in place (dtype of the engine);
+                     // folded: exp(z - r_g), with the target column patched in place
   uint16_t* dwlo;    // [v][d] lower 16 bits of the fp32 running dW sum; dw_out holds the upper 16
   float* dhpart;     // [S][C][d] fp32 split-vocabulary partials of dH (when dh_splits > 1)
   // folded one-pass backward (plan.fold)
-  float* uref;       // [C] row reference r_t of the stored P: the target logit (+-1e30, see target_ref_kernel)
-  int32_t* flag;     // [C] 1 where some group max exceeds r_t by more than kFoldMargin
-  float* rowf;       // [C rounded up to 256] per-row factor F_t = scale * exp(ref_t - lse_t)
+  float* uref;       // [C] u_t, the row's target logit (+-1e30, see target_ref_kernel)
+  int32_t* flag;     // [C] 1 where some group max exceeds u_t by more than kFoldMargin
+  float* rowf;       // [C rounded up to 256] per-row factor F_t = scale * exp(ref_t - lse_t),
+                     // ref_t = u_t, or the row max for a flagged row
   void* hs;          // [C][d] bf16(F * H) (two such with paired buffers): dW's token operand
 };
 
-// Folded backward: P is stored as exp(z - max(r_t, group max - kFoldMargin)),
-// at most exp(kFoldMargin), so the factor F_t >= scale * exp(-kFoldMargin - log v)
+// Folded backward: group g of row t is stored as exp(z - r_g) with
+// r_g = max(u_t, group max - kFoldMargin), at most exp(kFoldMargin); for an
+// unflagged row u_t >= row max - kFoldMargin, so F_t >= scale * exp(-kFoldMargin - log v)
 // stays a normal number.
 constexpr float kFoldMargin = 30.0f;
 

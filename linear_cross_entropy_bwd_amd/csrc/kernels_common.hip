@@ -1,7 +1,8 @@
 // Bandwidth-light kernels around the three contractions:
 //   label scan (valid-row count), partial-LSE merge and per-row loss,
-//   in-place softmax-minus-one-hot gradient, split-vocabulary dH reduction,
-//   and the fixed-order loss reduction.
+//   in-place softmax-minus-one-hot gradient, the target-logit pre-pass and the
+//   patch of the per-row factor form of that gradient, split-vocabulary dH
+//   reduction, and the fixed-order loss reduction.
 #include "device_util.h"
 #include "flce_internal.h"
 
