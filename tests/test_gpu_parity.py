@@ -173,6 +173,23 @@ def test_logit_shift_100_f32():
     assert np.all(dh[:, d + 1:] == 0.0) and np.all(dw[:, d + 1:] == 0.0)
 
 
+@pytest.mark.parametrize("c", [100.0, -100.0])
+def test_logit_shift_bf16_folded(c):
+    """The shift of every logit by +-100 (a ones column in H, a column of c in W,
+    both exact in bf16) on the bf16 path with the per-row factor: the target-logit
+    references, the group maxes and the LSE all move by c, and loss, dH[:, :D] and
+    dW[:, :D] match the unshifted oracle; the LSE moves by c."""
+    n, d, v = 300, 64, 2000
+    wl, (h, w, y) = _case(n, d, v, "bf16", sigma_w=0.3, seed=27)
+    h1 = torch.cat([h, torch.ones(n, 1, dtype=h.dtype), torch.zeros(n, 7, dtype=h.dtype)], dim=1)
+    w1 = torch.cat([w, torch.full((v, 1), c, dtype=w.dtype), torch.zeros(v, 7, dtype=w.dtype)], dim=1)
+    assert flce.flce_plan_info(n, d + 8, v, flce.FLCE_BF16, 1)["folded_factor"] == 1
+    say(f"[parity] logit shift {c:+.0f}, bf16 folded")
+    loss, lse, dh, dw = run_lib(h1, w1, y)
+    base = flce_forward_backward(h, w, y)
+    check((loss, lse - c, dh[:, :d], dw[:, :d]), base, torch.bfloat16, f"shift {c:+.0f} vs unshifted")
+
+
 def test_labels_at_vocab_edges():
     wl, (h, w, y) = _case(50, 64, 777, "bf16", sigma_w=0.2, ignore_frac=0.0, seed=18)
     y[0::3] = 0
