@@ -179,3 +179,30 @@ def test_stress_all_ignored_chunk(monkeypatch):
     say(f"[stress, ignored chunk] loss rel {e_loss:.2e}, max lse rel {e_lse:.2e}")
     assert e_loss <= TOL[torch.bfloat16]["loss"] and e_lse <= TOL[torch.bfloat16]["loss"]
     _check_gradients_sampled(wl, h, w64, y, rlse, dh, dw, 4096, "ignored chunk")
+
+
+@pytest.mark.parametrize("name", ["llama3_8b_head", "stability_stress"])
+def test_full_size_gradient_forms_agree(monkeypatch, name):
+    """The per-row factor form (default) against the in-place form of the gradient
+    (FLCE_INPLACE_GRAD=1) at full size: the forward is shared, so loss and every
+    LSE are bitwise equal; dH and dW agree to within the bf16 gradient tolerance on
+    every element.  The stability-stress workload flags nearly every row."""
+    wl = CONFIGS[name]
+    say(f"[fullsize] gradient forms, {name}")
+    h, w, y = make_inputs(wl)
+    dev = torch.device("cuda:0")
+    hd, wd, yd = h.to(dev), w.to(dev), y.to(dev)
+    assert flce.flce_plan_info(wl.n, wl.d, wl.v, flce.FLCE_BF16, 1)["folded_factor"] == 1
+    loss_f, lse_f, dh_f, dw_f = flce.linear_cross_entropy(hd, wd, yd, reduction=wl.reduction)
+    monkeypatch.setenv("FLCE_INPLACE_GRAD", "1")
+    assert flce.flce_plan_info(wl.n, wl.d, wl.v, flce.FLCE_BF16, 1)["folded_factor"] == 0
+    loss_i, lse_i, dh_i, dw_i = flce.linear_cross_entropy(hd, wd, yd, reduction=wl.reduction)
+    torch.cuda.synchronize()
+    assert torch.equal(loss_f, loss_i) and torch.equal(lse_f, lse_i)
+    tol = TOL[torch.bfloat16]["grad"]
+    for a, b, what in ((dh_f, dh_i, "dH"), (dw_f, dw_i, "dW")):
+        err = float((a.float() - b.float()).abs().max()) / float(b.float().abs().max())
+        say(f"  {what}: max|folded - in place| / max|in place| = {err:.2e}")
+        assert err <= tol, what
+    del hd, wd, yd, dh_f, dw_f, dh_i, dw_i
+    torch.cuda.empty_cache()
