@@ -355,6 +355,20 @@ int flce_sum_parts(const float* parts, int64_t num_parts, int64_t count, flce_dt
                    hipStream_t stream);
 
 /*
+ * x[i] *= *scale for i < count, in place: the fp32 product rounded to dtype
+ * (round-to-nearest-even for bf16).  The scale is read on the device, so a
+ * caller can hand over an upstream gradient without a host synchronisation;
+ * a scale of exactly 1 leaves x untouched.  This applies the upstream
+ * gradient of the loss (the gradients are those of upstream * loss) to the
+ * dH and dW that flce_fwd_bwd computed in the same pass as the loss, as an
+ * autograd function whose forward runs flce_fwd_bwd does in its backward.
+ *   x      device, [count] in dtype, 16-byte aligned; count in (0, 2^40].
+ *   scale  device, one fp32.
+ * FLCE_ERR_INVALID_ARG / FLCE_ERR_ALIGNMENT before anything is enqueued.
+ */
+int flce_scale(void* x, int64_t count, flce_dtype dtype, const float* scale, hipStream_t stream);
+
+/*
  * Bytes of device workspace one call allocates (with_bwd = 0 for flce_fwd,
  * 2 for flce_bwd, 1 or any other value for flce_fwd_bwd); 0 for invalid sizes.  Honours the
  * FLCE_CHUNK_ROWS and FLCE_WORKSPACE_CAP_BYTES environment overrides exactly

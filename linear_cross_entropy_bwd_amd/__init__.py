@@ -38,6 +38,7 @@ EXPORTED = (
     "flce_bwd_shard",
     "flce_bwd_shard_accumulate",
     "flce_sum_parts",
+    "flce_scale",
     "flce_workspace_bytes",
     "flce_workspace_bytes_lowmem",
     "flce_plan_info",
@@ -138,6 +139,8 @@ def lib() -> ctypes.CDLL:
     L.flce_bwd_shard_accumulate.restype = i32
     L.flce_sum_parts.argtypes = [p, i64, i64, i32, p, p]
     L.flce_sum_parts.restype = i32
+    L.flce_scale.argtypes = [p, i64, i32, p, p]
+    L.flce_scale.restype = i32
     L.flce_workspace_bytes.argtypes = [i64, i64, i64, i32, i32]
     L.flce_workspace_bytes.restype = ctypes.c_size_t
     L.flce_plan_info.argtypes = [i64, i64, i64, i32, i32, ctypes.POINTER(PlanInfo)]
@@ -256,6 +259,10 @@ def flce_bwd_shard_accumulate(h, w_shard, labels, lse, grad_out, n, d, v_shard, 
 
 def flce_sum_parts(parts, num_parts, count, dtype, out, stream) -> int:
     return lib().flce_sum_parts(_ptr(parts), num_parts, count, dtype, _ptr(out), _stream(stream))
+
+
+def flce_scale(x, count, dtype, scale, stream) -> int:
+    return lib().flce_scale(_ptr(x), count, dtype, _ptr(scale), _stream(stream))
 
 
 def flce_workspace_bytes(n, d, v, dtype, with_bwd) -> int:
@@ -417,6 +424,20 @@ def linear_cross_entropy(h, w, labels, ignore_index: int = -100, reduction: str 
     if st != FLCE_OK:
         raise FlceError(st, "flce_fwd_bwd")
     return loss, lse, dh, dw
+
+
+def scale_(x, scale):
+    """x *= scale in place (flce_scale): ``x`` a contiguous bf16 or fp32 device tensor,
+    ``scale`` a one-element fp32 tensor on the same device; a scale of exactly 1
+    leaves x untouched.  Returns x."""
+    import torch
+    if not x.is_contiguous() or x.numel() == 0:
+        raise ValueError("x must be a non-empty contiguous tensor")
+    _check_scalar(scale, x.device, "scale")
+    st = flce_scale(x, x.numel(), _dtype_code(x), scale, torch.cuda.current_stream(x.device))
+    if st != FLCE_OK:
+        raise FlceError(st, "flce_scale")
+    return x
 
 
 def linear_cross_entropy_lowmem(h, w, labels, ignore_index: int = -100, reduction: str = "mean", out=None):

@@ -874,6 +874,13 @@ int call_sum_parts(const float* parts, int64_t num_parts, int64_t count, flce_dt
   return status_of(timed(K_DH_REDUCE, stream, [&] { return launch_sum_parts(parts, num_parts, count, dtype, out, stream); }));
 }
 
+int call_scale(void* x, int64_t count, flce_dtype dtype, const float* scale, hipStream_t stream) {
+  if (x == nullptr || scale == nullptr || count <= 0 || count > (int64_t(1) << 40)) return FLCE_ERR_INVALID_ARG;
+  if (dtype != FLCE_BF16 && dtype != FLCE_F32) return FLCE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(scale, 4)) return FLCE_ERR_ALIGNMENT;
+  return status_of(launch_scale(x, count, dtype, scale, stream));
+}
+
 }  // namespace
 
 int fwd_in_workspace(const void* h, const void* w, const int64_t* labels, int64_t n, int64_t d, int64_t v,
@@ -986,6 +993,10 @@ int flce_bwd_shard_accumulate(const void* h, const void* w_shard, const int64_t*
 int flce_sum_parts(const float* parts, int64_t num_parts, int64_t count, flce_dtype dtype, void* out,
                    hipStream_t stream) {
   return flce::call_sum_parts(parts, num_parts, count, dtype, out, stream);
+}
+
+int flce_scale(void* x, int64_t count, flce_dtype dtype, const float* scale, hipStream_t stream) {
+  return flce::call_scale(x, count, dtype, scale, stream);
 }
 
 size_t flce_workspace_bytes(int64_t n, int64_t d, int64_t v, flce_dtype dtype, int with_bwd) {

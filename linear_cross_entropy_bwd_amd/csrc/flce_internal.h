@@ -173,6 +173,7 @@ hipError_t launch_shift_labels(const int64_t* labels, int64_t n, int64_t first, 
 hipError_t launch_shard_merge(const float* lse_parts, const float* zy_parts, int64_t shards, int64_t n,
                               const int64_t* labels, int64_t ignore_index, float* lse_out, float* loss_rows,
                               hipStream_t s);
+hipError_t launch_scale(void* x, int64_t count, int32_t dtype, const float* scale, hipStream_t s);
 hipError_t launch_sum_parts(const float* parts, int64_t num_parts, int64_t count, int32_t dtype, void* out,
                             hipStream_t s);
 

@@ -263,6 +263,25 @@ __global__ __launch_bounds__(256) void fold_patch_kernel(const bf16_t* __restric
   }
 }
 
+// x *= *scale in place (fp32 products rounded to the element type), 16-byte
+// vectors; a scale of exactly 1 returns at once.
+template <typename T>
+__global__ __launch_bounds__(256) void scale_kernel(T* __restrict__ x, int64_t count, const float* __restrict__ scale) {
+  const float s = *scale;
+  if (s == 1.0f) return;
+  constexpr int kVec = 16 / sizeof(T);
+  const int64_t i0 = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * kVec;
+  if (i0 + kVec <= count) {
+    uint4 q = *reinterpret_cast<const uint4*>(x + i0);
+    T* e = reinterpret_cast<T*>(&q);
+#pragma unroll
+    for (int k = 0; k < kVec; ++k) Elem<T>::st(e, k, Elem<T>::ld(e, k) * s);
+    *reinterpret_cast<uint4*>(x + i0) = q;
+  } else {
+    for (int64_t i = i0; i < count; ++i) Elem<T>::st(x, i, Elem<T>::ld(x, i) * s);
+  }
+}
+
 // dH rows = sum of the split partials (added to what `out` holds when
 // accumulating), rounded to the output type.
 template <typename TO>
@@ -452,6 +471,16 @@ hipError_t launch_sum_parts(const float* parts, int64_t num_parts, int64_t count
     dh_reduce_kernel<bf16_t><<<blocks, 256, 0, s>>>(parts, num_parts, count, count, 0, static_cast<bf16_t*>(out));
   else
     dh_reduce_kernel<float><<<blocks, 256, 0, s>>>(parts, num_parts, count, count, 0, static_cast<float*>(out));
+  return hipGetLastError();
+}
+
+hipError_t launch_scale(void* x, int64_t count, int32_t dtype, const float* scale, hipStream_t s) {
+  const int64_t vec = dtype == FLCE_BF16 ? 8 : 4;
+  const unsigned blocks = static_cast<unsigned>((count + 256 * vec - 1) / (256 * vec));
+  if (dtype == FLCE_BF16)
+    scale_kernel<bf16_t><<<blocks, 256, 0, s>>>(static_cast<bf16_t*>(x), count, scale);
+  else
+    scale_kernel<float><<<blocks, 256, 0, s>>>(static_cast<float*>(x), count, scale);
   return hipGetLastError();
 }
 

@@ -103,6 +103,58 @@ def test_autograd_module(dtype):
     _check_grads(to_f64(hd.grad), to_f64(wd.grad), 2.5 * rdh, 2.5 * rdw, wl.torch_dtype, "autograd")
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_autograd_one_pass(dtype):
+    """LinearCrossEntropyLoss(one_pass=True): dH and dW formed in the forward by
+    flce_fwd_bwd, scaled by the upstream gradient (2.5) in the backward; the loss
+    is bitwise the recompute mode's, the gradients match the oracle's times 2.5,
+    only the inputs that require a gradient get one, and a second backward
+    through the same graph is refused."""
+    wl, (h, w, y) = _case(150, 128, 2500, dtype, ignore_frac=0.2, seed=35)
+    loss_ref, _, rdh, rdw = flce_forward_backward(h, w, y)
+    hd = h.to(DEV).requires_grad_(True)
+    wd = w.to(DEV).requires_grad_(True)
+    yd = y.to(DEV)
+    loss = LinearCrossEntropyLoss(one_pass=True)(hd, wd, yd)
+    loss_rc = LinearCrossEntropyLoss()(hd.detach(), wd.detach(), yd)
+    assert loss.dim() == 0 and torch.equal(loss.detach(), loss_rc)
+    (2.5 * loss).backward()
+    torch.cuda.synchronize()
+    tol = TOL[wl.torch_dtype]
+    assert abs(float(loss.item()) - loss_ref) <= tol["loss"] * abs(loss_ref)
+    _check_grads(to_f64(hd.grad), to_f64(wd.grad), 2.5 * rdh, 2.5 * rdw, wl.torch_dtype, "autograd one pass")
+
+    # upstream gradient 1: the fused call's own dH and dW, untouched
+    w2 = w.to(DEV).requires_grad_(True)
+    LinearCrossEntropyLoss(one_pass=True)(h.to(DEV), w2, yd).backward()
+    _, _, dh1, dw1 = flce.linear_cross_entropy(h.to(DEV), w.to(DEV), yd)
+    torch.cuda.synchronize()
+    assert torch.equal(w2.grad, dw1)
+
+    # one backward per graph
+    h3 = h.to(DEV).requires_grad_(True)
+    loss3 = LinearCrossEntropyLoss(one_pass=True)(h3, w.to(DEV), yd)
+    loss3.backward(retain_graph=True)
+    with pytest.raises(RuntimeError, match="one backward"):
+        loss3.backward()
+
+
+@pytest.mark.parametrize("dtype,count", [("bf16", 4096), ("bf16", 1001), ("f32", 4096), ("f32", 1003)])
+def test_scale_in_place(dtype, count):
+    """flce_scale: x *= s with the fp32 product rounded to the element type
+    (round-to-nearest-even, torch's own conversion), ragged tails included; a
+    scale of exactly 1 leaves x bitwise untouched."""
+    td = torch.bfloat16 if dtype == "bf16" else torch.float32
+    g = torch.Generator().manual_seed(count)
+    x = torch.randn(count, generator=g).to(td).to(DEV)
+    for s in (1.0, 0.5, 3.0, -1e-3):
+        y = x.clone()
+        flce.scale_(y, torch.tensor([s], dtype=torch.float32, device=DEV))
+        torch.cuda.synchronize()
+        want = (x.float() * s).to(td)
+        assert torch.equal(y, want if s != 1.0 else x), f"scale {s}"
+
+
 def test_bwd_single_row_and_tiny_vocab():
     wl, (h, w, y) = _case(1, 16, 5, "bf16", ignore_frac=0.0, seed=36)
     _, lse64 = flce_forward(h, w, y)
