@@ -375,6 +375,20 @@ def _check_inputs(h, w, labels):
         raise ValueError("h, w and labels must be on one device")
 
 
+def _debug_labels(labels, v: int, ignore_index: int):
+    """With FLCE_CHECK_LABELS=1 in the environment: raise ValueError on a label that is
+    neither ignore_index nor in [0, v).  Off by default: it synchronises with the host,
+    and the kernels give such a row the documented meaning (target logit 0, no one-hot
+    term) without reading out of bounds."""
+    if os.environ.get("FLCE_CHECK_LABELS", "") in ("", "0"):
+        return
+    bad = (labels != ignore_index) & ((labels < 0) | (labels >= v))
+    if bool(bad.any()):
+        i = int(bad.nonzero()[0, 0])
+        raise ValueError(f"label {int(labels[i])} at row {i} is outside [0, {v}) and is not "
+                         f"ignore_index ({ignore_index})")
+
+
 def _check_vec(t, n: int, device, name: str):
     """A contiguous fp32 [n] tensor on `device` (a saved LSE or an LSE output)."""
     import torch
@@ -408,6 +422,7 @@ def linear_cross_entropy(h, w, labels, ignore_index: int = -100, reduction: str 
     _check_inputs(h, w, labels)
     n, d = h.shape
     v = w.shape[0]
+    _debug_labels(labels, v, ignore_index)
     if out is None:
         loss = torch.empty(1, dtype=torch.float32, device=h.device)
         lse = torch.empty(n, dtype=torch.float32, device=h.device)
@@ -448,6 +463,7 @@ def linear_cross_entropy_lowmem(h, w, labels, ignore_index: int = -100, reductio
     _check_inputs(h, w, labels)
     n, d = h.shape
     v = w.shape[0]
+    _debug_labels(labels, v, ignore_index)
     if out is None:
         loss = torch.empty(1, dtype=torch.float32, device=h.device)
         lse = torch.empty(n, dtype=torch.float32, device=h.device)
@@ -472,6 +488,7 @@ def linear_cross_entropy_forward(h, w, labels, ignore_index: int = -100, reducti
     _check_inputs(h, w, labels)
     n, d = h.shape
     v = w.shape[0]
+    _debug_labels(labels, v, ignore_index)
     loss = torch.empty(1, dtype=torch.float32, device=h.device)
     lse = torch.empty(n, dtype=torch.float32, device=h.device)
     st = flce_fwd(h, w, labels, n, d, v, _dtype_code(h), ignore_index, _red_code(reduction), loss, lse,
@@ -493,6 +510,7 @@ def linear_cross_entropy_backward(h, w, labels, lse, grad_out=None, ignore_index
     _check_inputs(h, w, labels)
     n, d = h.shape
     v = w.shape[0]
+    _debug_labels(labels, v, ignore_index)
     _check_vec(lse, n, h.device, "lse")
     _check_scalar(grad_out, h.device, "grad_out")
     dh, dw = (torch.empty_like(h), torch.empty_like(w)) if out is None else out
@@ -529,6 +547,7 @@ def cross_entropy(logits, labels, ignore_index: int = -100, reduction: str = "me
     import torch
     _check_logits(logits, labels)
     n, v = logits.shape
+    _debug_labels(labels, v, ignore_index)
     loss = torch.empty(1, dtype=torch.float32, device=logits.device)
     lse = torch.empty(n, dtype=torch.float32, device=logits.device)
     if grad is None:
@@ -552,6 +571,7 @@ def cross_entropy_backward(logits, labels, lse, grad_scale=None, ignore_index: i
     import torch
     _check_logits(logits, labels)
     n, v = logits.shape
+    _debug_labels(labels, v, ignore_index)
     _check_vec(lse, n, logits.device, "lse")
     _check_scalar(grad_scale, logits.device, "grad_scale")
     g = torch.empty_like(logits) if out is None else out
@@ -592,6 +612,7 @@ def linear_cross_entropy_vocab_split(h, w, labels, num_shards: int = 2, ignore_i
     _check_inputs(h, w, labels)
     n, d = h.shape
     v = w.shape[0]
+    _debug_labels(labels, v, ignore_index)
     bounds = list(shards) if shards is not None else vocab_shard_bounds(v, num_shards)
     if bounds[0][0] != 0 or bounds[-1][1] != v or any(a >= b for a, b in bounds) or any(
             bounds[q][1] != bounds[q + 1][0] for q in range(len(bounds) - 1)):
@@ -653,6 +674,7 @@ def linear_cross_entropy_forward_fp8(h_q, h_scale, w_q, w_scale, labels, ignore_
     device tensors) with fp32 per-row scales [n] and [v]."""
     import torch
     n, d, v = _check_fp8_inputs(h_q, h_scale, w_q, w_scale, labels)
+    _debug_labels(labels, v, ignore_index)
     loss = torch.empty(1, dtype=torch.float32, device=h_q.device)
     lse = torch.empty(n, dtype=torch.float32, device=h_q.device)
     st = flce_fwd_fp8(h_q, h_scale, w_q, w_scale, labels, n, d, v, ignore_index, _red_code(reduction), loss, lse,
@@ -668,6 +690,7 @@ def linear_cross_entropy_backward_fp8(h_q, h_scale, w_q, w_scale, labels, lse, g
     from the LSE flce_fwd_fp8 returned (flce_bwd_fp8)."""
     import torch
     n, d, v = _check_fp8_inputs(h_q, h_scale, w_q, w_scale, labels)
+    _debug_labels(labels, v, ignore_index)
     _check_vec(lse, n, h_q.device, "lse")
     _check_scalar(grad_out, h_q.device, "grad_out")
     dh = torch.empty(n, d, dtype=torch.bfloat16, device=h_q.device)

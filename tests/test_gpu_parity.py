@@ -139,6 +139,27 @@ def test_labels_outside_the_vocabulary(dtype):
     check(gpu, (rloss, rlse, rdh, rdw), wl.torch_dtype, "labels outside the vocabulary")
 
 
+def test_debug_label_check(monkeypatch):
+    """FLCE_CHECK_LABELS=1 makes the binding refuse a label outside [0, v) that is
+    not ignore_index (ValueError naming the row) before any library call; unset,
+    the call runs with the documented meaning of such a row."""
+    wl, (h, w, y) = _case(40, 64, 300, "bf16", sigma_w=0.1, seed=38)
+    hd, wd, yd = h.to("cuda:0"), w.to("cuda:0"), y.clone()
+    yd[7] = 300
+    yd = yd.to("cuda:0")
+    flce.linear_cross_entropy(hd, wd, yd)
+    monkeypatch.setenv("FLCE_CHECK_LABELS", "1")
+    with pytest.raises(ValueError, match="row 7"):
+        flce.linear_cross_entropy(hd, wd, yd)
+    with pytest.raises(ValueError, match="row 7"):
+        flce.linear_cross_entropy_forward(hd, wd, yd)
+    with pytest.raises(ValueError, match="row 7"):
+        flce.cross_entropy(torch.zeros(40, 300, dtype=torch.bfloat16, device="cuda:0"), yd)
+    ok = y.to("cuda:0")
+    flce.linear_cross_entropy(hd, wd, ok)                 # valid and ignored labels pass
+    torch.cuda.synchronize()
+
+
 def test_w_zero_closed_form():
     wl, (h, w, y) = _case(80, 64, 300, "f32", seed=16)
     w.zero_()
